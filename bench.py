@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""One-GPU benchmark of shared-prefix decode attention on MI355X.
+
+A step is one pass of the whole path -- decode kernel (partials) + merge
+kernel (bf16 output) -- over one synthetic batch whose inputs are resident
+in HBM.  Before every step (warm-up and timed) a 1 GiB fill evicts L2 and
+the 256 MB Infinity Cache, so KV is read from HBM, not from cache.  Step time
+is the HIP-event time of the two kernels on the stream they run on; the
+planner and the uploads run once, before timing.
+
+Prints one JSON line.  Default workload: the 64-request shared-system-prompt
+tree (4096-token root, suffixes U[256,1024], 32 q / 8 KV heads, D=128).
+"""
+import argparse
+import hashlib
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode attn unique-KV HBM GB/s (% of peak) + request-heads/s per step, 1 GPU"
+PEAK_HBM_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "decode_attention_prefix_amd", "csrc", "cap_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_cfg{cfg}_traffic.txt")
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(cfg: int):
+    """HBM bytes per decode launch from a committed rocprofv3 --pmc summary,
+    if it was taken on the current kernel source; else None."""
+    path = TRAFFIC_FILE.format(cfg=cfg)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=15)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--control", action="store_true", help="time the unshared control batch of the config")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--flush-mb", type=int, default=1024)
+    ap.add_argument("--share", type=int, default=-1, help="-1 auto, 0 fold all, 1 share all")
+    ap.add_argument("--split-pages", type=int, default=0)
+    ap.add_argument("--max-rows", type=int, default=0)
+    ap.add_argument("--rounds", type=float, default=0.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--read-probe-mb", type=int, default=2048)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build has no "
+              "multi-GPU path; the per-GPU share of a sharded run is the one-GPU workload.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from decode_attention_prefix_amd import cap
+    from decode_attention_prefix_amd import workloads as wl
+    from decode_attention_prefix_amd.decoder import TreeDecoder
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t_gen = time.perf_counter()
+    w = wl.make_config(args.config, seed=args.seed, tail_fill="zero", keep_tokens=args.control)
+    if args.control:
+        w = wl.control_workload(w, tail_fill="zero")
+    st_tree = wl.tree_stats(w.tree)
+    t_gen = time.perf_counter() - t_gen
+    opts = {"share_mode": args.share, "split_pages": args.split_pages}
+    if args.max_rows:
+        opts["max_rows"] = args.max_rows
+    if args.rounds:
+        opts["rounds"] = args.rounds
+    dec = TreeDecoder(w.tree, w.q, w.k_pool, w.v_pool, device=dev, **opts)
+    plan = dec.stats
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    # achievable HBM read rate (plain streaming read of a buffer >> caches)
+    probe_bytes = args.read_probe_mb << 20
+    probe = torch.empty(probe_bytes, dtype=torch.uint8, device=dev)
+    sink = torch.empty(8192, dtype=torch.int32, device=dev)
+    flush = torch.empty(max(args.flush_mb, 1) << 20, dtype=torch.uint8, device=dev)
+    cap.cap_bench_fill(probe.data_ptr(), probe_bytes, 0x3F803F80, sp)
+    read_ms = []
+    for _ in range(5):
+        cap.cap_bench_fill(flush.data_ptr(), flush.numel(), 0, sp)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        cap.cap_bench_read(probe.data_ptr(), probe_bytes, sink.data_ptr(), sp)
+        b.record(stream)
+        b.synchronize()
+        read_ms.append(a.elapsed_time(b))
+    read_gbs = probe_bytes / (min(read_ms) * 1e-3) / 1e9
+    del probe
+
+    def one_step(evs=None):
+        if args.flush_mb > 0:
+            cap.cap_bench_fill(flush.data_ptr(), flush.numel(), 0, sp)
+        if evs is not None:
+            evs[0].record(stream)
+        dec.decode()
+        if evs is not None:
+            evs[1].record(stream)
+        dec.merge()
+        if evs is not None:
+            evs[2].record(stream)
+
+    for _ in range(args.warmup):
+        one_step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        one_step(events[k])
+    torch.cuda.synchronize(dev)
+    wall_s = time.perf_counter() - t0
+    dec_ms = [e[0].elapsed_time(e[1]) for e in events]
+    mrg_ms = [e[1].elapsed_time(e[2]) for e in events]
+    step_ms = [a + b for a, b in zip(dec_ms, mrg_ms)]
+    mean_ms = statistics.fmean(step_ms)
+    med_ms = statistics.median(step_ms)
+    srt = sorted(step_ms)
+    p90_ms = srt[min(len(srt) - 1, int(round(0.9 * (len(srt) - 1))))]
+
+    uniq = st_tree["unique_kv_bytes"]
+    value = uniq / (mean_ms * 1e-3) / 1e9
+    dec_mean = statistics.fmean(dec_ms)
+    alg_bytes_decode = uniq + st_tree["q_bytes"]
+    achieved = alg_bytes_decode / (dec_mean * 1e-3) / 1e9
+    traffic = load_traffic(args.config) if not args.control else None
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(mean_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": ("control batch of " if args.control else "") + f"config {args.config}: "
+                        + wl.CONFIG_NAMES[args.config],
+            "requests": w.tree.num_requests, "q_heads": w.tree.num_q_heads,
+            "kv_heads": w.tree.num_kv_heads, "head_dim": w.tree.head_dim, "page_size": 16,
+            "seed": args.seed, "nodes": w.tree.num_nodes,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "kernel": "decode_kernel<128>" if w.tree.head_dim == 128 else "decode_kernel<64>",
+            "algorithmic_bytes_per_launch": alg_bytes_decode,
+            "decode_us_mean": round(dec_mean * 1e3, 3),
+        },
+        "pct_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
+        "pct_measured_read_roofline": round(100 * value / read_gbs, 2),
+        "req_heads_per_s": round(st_tree["request_heads"] / (mean_ms * 1e-3), 1),
+        "mfma_util": round(st_tree["useful_flop"] / (mean_ms * 1e-3) / 2.5e15, 5),
+        "t_decode_us": {"mean": round(dec_mean * 1e3, 3), "median": round(statistics.median(dec_ms) * 1e3, 3)},
+        "t_merge_us": {"mean": round(statistics.fmean(mrg_ms) * 1e3, 3),
+                       "median": round(statistics.median(mrg_ms) * 1e3, 3)},
+        "t_step_us": {"mean": round(mean_ms * 1e3, 3), "median": round(med_ms * 1e3, 3),
+                      "min": round(srt[0] * 1e3, 3), "p90": round(p90_ms * 1e3, 3)},
+        "value_median_step": round(uniq / (med_ms * 1e-3) / 1e9, 2),
+        "wall_ms_per_step_incl_flush": round(wall_s * 1e3 / args.steps, 4),
+        "read_roofline_gbs": round(read_gbs, 1),
+        "bytes": {"unique_kv": uniq, "unshared_kv": st_tree["unshared_kv_bytes"],
+                  "kv_streamed_by_items": plan["kv_bytes_streamed"],
+                  "partial": plan["partial_bytes"], "q": st_tree["q_bytes"], "out": st_tree["out_bytes"]},
+        "plan": {k: plan[k] for k in ("num_items", "num_tasks", "num_groups", "partial_rows",
+                                      "max_partials_per_request", "max_pages_per_item")},
+        "plan_host_us": round(plan["plan_host_us"], 1),
+        "flush_mb": args.flush_mb,
+        "gen_s": round(t_gen, 2),
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+        ncores = len(os.sched_getaffinity(0))
+        # bounded sample: the whole tree if it fits ~30 s of CPU work, else a
+        # prefix of the requests (the metric's unit scales by unique bytes read)
+        t1 = time.perf_counter()
+        oracle.decode(w.tree, w.q, w.k_pool, w.v_pool, nthreads=ncores)
+        t_or = time.perf_counter() - t1
+        result["cpu_baseline"] = {
+            "value": round(uniq / t_or / 1e9, 4),
+            "unit": "GB/s",
+            "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"whole workload ({w.tree.num_requests} requests), one run, {t_or:.2f} s",
+            "cpu": cpu_model(),
+        }
+    dec.close()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,252 @@
+"""Thin ctypes binding of libcap (include/cap.h, include/cap_bench.h).
+
+Argument marshalling only: every step of the attention path runs in the
+library's HIP kernels.  Functions keep the C names; device buffers are
+passed as integer device addresses and streams as integer hipStream_t
+handles (``torch.cuda.current_stream().cuda_stream``).  A missing library is
+an error -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcap.so")
+
+CAP_OK = 0
+STATUS_NAMES = {0: "CAP_OK", 1: "CAP_ERR_INVALID_ARG", 2: "CAP_ERR_BAD_TREE",
+                3: "CAP_ERR_WORKSPACE", 4: "CAP_ERR_UNSUPPORTED", 5: "CAP_ERR_HIP",
+                6: "CAP_ERR_STATE"}
+
+EXPORTED = [
+    "cap_abi_version", "cap_last_error", "cap_plan_opts_default", "cap_tree_device_bytes",
+    "cap_tree_upload", "cap_tree_free", "cap_plan_step", "cap_plan_get_stats",
+    "cap_plan_get_view", "cap_plan_upload", "cap_decode_attention", "cap_merge_partials",
+    "cap_plan_free", "cap_bench_fill", "cap_bench_read", "cap_bench_copy",
+]
+
+
+class CapError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("sm_scale", ctypes.c_float)]
+
+
+class TreeDesc(ctypes.Structure):
+    _fields_ = [("num_nodes", ctypes.c_int32), ("parent", ctypes.c_void_p),
+                ("num_tokens", ctypes.c_void_p), ("page_offsets", ctypes.c_void_p),
+                ("page_ids", ctypes.c_void_p), ("num_requests", ctypes.c_int32),
+                ("path_offsets", ctypes.c_void_p), ("path_nodes", ctypes.c_void_p),
+                ("num_pool_pages", ctypes.c_int64)]
+
+
+class PlanOpts(ctypes.Structure):
+    _fields_ = [("share_mode", ctypes.c_int32), ("split_pages", ctypes.c_int32),
+                ("max_rows", ctypes.c_int32), ("num_cus", ctypes.c_int32),
+                ("waves_per_cu", ctypes.c_int32), ("rounds", ctypes.c_float),
+                ("share_margin", ctypes.c_float), ("reserved", ctypes.c_int32 * 4)]
+
+
+class PlanStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "num_items", "num_tasks", "num_groups", "partial_rows", "workspace_bytes",
+        "plan_device_bytes", "tree_device_bytes", "kv_bytes_streamed", "kv_bytes_unique",
+        "kv_bytes_unshared", "partial_bytes")] + [
+        ("max_partials_per_request", ctypes.c_int32), ("max_pages_per_item", ctypes.c_int32),
+        ("plan_host_us", ctypes.c_double)]
+
+
+class WorkItemC(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("stream_off", "npages", "head", "row_off", "nreq", "slot_base")]
+
+
+class PlanView(ctypes.Structure):
+    _fields_ = [("num_items", ctypes.c_int32), ("items", ctypes.POINTER(WorkItemC)),
+                ("stream_len", ctypes.c_int32), ("stream", ctypes.POINTER(ctypes.c_int32)),
+                ("rows_len", ctypes.c_int32), ("rows", ctypes.POINTER(ctypes.c_int32)),
+                ("num_requests", ctypes.c_int32), ("merge_off", ctypes.POINTER(ctypes.c_int32)),
+                ("merge_rows", ctypes.POINTER(ctypes.c_int32))]
+
+
+_lib = None
+
+
+def lib():
+    """Load libcap.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m decode_attention_prefix_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, st = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        L.cap_abi_version.restype = ctypes.c_int32
+        L.cap_last_error.restype = ctypes.c_char_p
+        L.cap_plan_opts_default.argtypes = [ctypes.POINTER(PlanOpts)]
+        L.cap_plan_opts_default.restype = None
+        L.cap_tree_device_bytes.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(TreeDesc),
+                                            ctypes.POINTER(sz)]
+        L.cap_tree_upload.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(TreeDesc), vp, sz,
+                                      vp, ctypes.POINTER(vp)]
+        L.cap_tree_free.argtypes = [vp]
+        L.cap_tree_free.restype = None
+        L.cap_plan_step.argtypes = [vp, ctypes.POINTER(PlanOpts), ctypes.POINTER(vp)]
+        L.cap_plan_get_stats.argtypes = [vp, ctypes.POINTER(PlanStats)]
+        L.cap_plan_get_view.argtypes = [vp, ctypes.POINTER(PlanView)]
+        L.cap_plan_upload.argtypes = [vp, vp, sz, vp]
+        L.cap_decode_attention.argtypes = [vp, vp, vp, vp, vp, sz, vp]
+        L.cap_merge_partials.argtypes = [vp, vp, sz, vp, vp]
+        L.cap_plan_free.argtypes = [vp]
+        L.cap_plan_free.restype = None
+        L.cap_bench_fill.argtypes = [vp, sz, ctypes.c_uint32, vp]
+        L.cap_bench_read.argtypes = [vp, sz, vp, vp]
+        L.cap_bench_copy.argtypes = [vp, vp, sz, vp]
+        for name in ("cap_tree_device_bytes", "cap_tree_upload", "cap_plan_step",
+                     "cap_plan_get_stats", "cap_plan_get_view", "cap_plan_upload",
+                     "cap_decode_attention", "cap_merge_partials", "cap_bench_fill",
+                     "cap_bench_read", "cap_bench_copy"):
+            getattr(L, name).restype = st
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != CAP_OK:
+        raise CapError(status, lib().cap_last_error().decode(errors="replace"))
+
+
+def cap_abi_version() -> int:
+    return int(lib().cap_abi_version())
+
+
+def cap_last_error() -> str:
+    return lib().cap_last_error().decode(errors="replace")
+
+
+class _TreeArrays:
+    """Keeps contiguous host arrays alive while a TreeDesc points at them."""
+
+    def __init__(self, tree):
+        self.parent = np.ascontiguousarray(tree.parent, dtype=np.int32)
+        self.num_tokens = np.ascontiguousarray(tree.num_tokens, dtype=np.int32)
+        self.page_offsets = np.ascontiguousarray(tree.page_offsets, dtype=np.int64)
+        self.page_ids = np.ascontiguousarray(tree.page_ids, dtype=np.int32)
+        self.path_offsets = np.ascontiguousarray(tree.path_offsets, dtype=np.int32)
+        self.path_nodes = np.ascontiguousarray(tree.path_nodes, dtype=np.int32)
+        self.attn = AttnDesc(int(tree.num_q_heads), int(tree.num_kv_heads), int(tree.head_dim),
+                             int(getattr(tree, "page_size", 16)), float(tree.sm_scale))
+        p = lambda a: a.ctypes.data if a.size else None
+        self.desc = TreeDesc(int(self.parent.shape[0]), p(self.parent), p(self.num_tokens),
+                             p(self.page_offsets), p(self.page_ids),
+                             int(self.path_offsets.shape[0] - 1), p(self.path_offsets),
+                             p(self.path_nodes), int(tree.num_pool_pages))
+
+
+def cap_tree_device_bytes(tree) -> int:
+    arr = _TreeArrays(tree)
+    out = ctypes.c_size_t(0)
+    _check(lib().cap_tree_device_bytes(ctypes.byref(arr.attn), ctypes.byref(arr.desc),
+                                       ctypes.byref(out)))
+    return int(out.value)
+
+
+def cap_tree_upload(tree, dev_buf: int = 0, dev_bytes: int = 0, stream: int = 0) -> int:
+    """Validate and upload; returns the opaque handle (an int).  dev_buf=0: host only."""
+    arr = _TreeArrays(tree)
+    h = ctypes.c_void_p(None)
+    _check(lib().cap_tree_upload(ctypes.byref(arr.attn), ctypes.byref(arr.desc),
+                                 ctypes.c_void_p(dev_buf or None), dev_bytes,
+                                 ctypes.c_void_p(stream or None), ctypes.byref(h)))
+    return int(h.value)
+
+
+def cap_tree_free(handle: int) -> None:
+    if handle:
+        lib().cap_tree_free(ctypes.c_void_p(handle))
+
+
+def make_opts(**kw) -> PlanOpts:
+    o = PlanOpts()
+    lib().cap_plan_opts_default(ctypes.byref(o))
+    for k, v in kw.items():
+        if not hasattr(o, k):
+            raise TypeError(f"unknown planner option {k}")
+        setattr(o, k, v)
+    return o
+
+
+def cap_plan_step(tree_handle: int, **opts) -> int:
+    o = make_opts(**opts)
+    h = ctypes.c_void_p(None)
+    _check(lib().cap_plan_step(ctypes.c_void_p(tree_handle), ctypes.byref(o), ctypes.byref(h)))
+    return int(h.value)
+
+
+def cap_plan_get_stats(plan: int) -> dict:
+    s = PlanStats()
+    _check(lib().cap_plan_get_stats(ctypes.c_void_p(plan), ctypes.byref(s)))
+    return {name: getattr(s, name) for name, _ in PlanStats._fields_}
+
+
+def cap_plan_get_view(plan: int) -> dict:
+    """Copies of the plan's host arrays (items as an int32 [n][6] array)."""
+    v = PlanView()
+    _check(lib().cap_plan_get_view(ctypes.c_void_p(plan), ctypes.byref(v)))
+
+    def arr(ptr, n, width=1):
+        if n == 0:
+            return np.zeros((0, width) if width > 1 else (0,), np.int32)
+        a = np.ctypeslib.as_array(ctypes.cast(ptr, ctypes.POINTER(ctypes.c_int32)), (n * width,))
+        return a.copy().reshape((n, width) if width > 1 else (n,))
+
+    return {"items": arr(v.items, v.num_items, 6), "stream": arr(v.stream, v.stream_len),
+            "rows": arr(v.rows, v.rows_len),
+            "merge_off": arr(v.merge_off, v.num_requests + 1),
+            "merge_rows": arr(v.merge_rows, int(arr(v.merge_off, v.num_requests + 1)[-1]))}
+
+
+def cap_plan_upload(plan: int, dev_buf: int, nbytes: int, stream: int = 0) -> None:
+    _check(lib().cap_plan_upload(ctypes.c_void_p(plan), ctypes.c_void_p(dev_buf), nbytes,
+                                 ctypes.c_void_p(stream or None)))
+
+
+def cap_decode_attention(plan: int, q: int, k_pool: int, v_pool: int, workspace: int,
+                         ws_bytes: int, stream: int = 0) -> None:
+    _check(lib().cap_decode_attention(ctypes.c_void_p(plan), ctypes.c_void_p(q),
+                                      ctypes.c_void_p(k_pool), ctypes.c_void_p(v_pool),
+                                      ctypes.c_void_p(workspace), ws_bytes,
+                                      ctypes.c_void_p(stream or None)))
+
+
+def cap_merge_partials(plan: int, workspace: int, ws_bytes: int, out: int, stream: int = 0) -> None:
+    _check(lib().cap_merge_partials(ctypes.c_void_p(plan), ctypes.c_void_p(workspace), ws_bytes,
+                                    ctypes.c_void_p(out), ctypes.c_void_p(stream or None)))
+
+
+def cap_plan_free(plan: int) -> None:
+    if plan:
+        lib().cap_plan_free(ctypes.c_void_p(plan))
+
+
+def cap_bench_fill(buf: int, nbytes: int, value: int = 0, stream: int = 0) -> None:
+    _check(lib().cap_bench_fill(ctypes.c_void_p(buf), nbytes, value, ctypes.c_void_p(stream or None)))
+
+
+def cap_bench_read(buf: int, nbytes: int, sink: int, stream: int = 0) -> None:
+    _check(lib().cap_bench_read(ctypes.c_void_p(buf), nbytes, ctypes.c_void_p(sink),
+                                ctypes.c_void_p(stream or None)))
+
+
+def cap_bench_copy(dst: int, src: int, nbytes: int, stream: int = 0) -> None:
+    _check(lib().cap_bench_copy(ctypes.c_void_p(dst), ctypes.c_void_p(src), nbytes,
+                                ctypes.c_void_p(stream or None)))

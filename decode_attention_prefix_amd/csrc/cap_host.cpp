@@ -1,0 +1,621 @@
+// cap_host.cpp -- host side of libcap: tree validation and upload, the
+// per-step planner, and the C ABI entry points declared in include/cap.h.
+//
+// The planner is this library's counterpart of the per-decoding-step cost
+// model on the Capillary Kernels project page (abstract, second paragraph),
+// which picks query grouping so that saved HBM traffic pays for the cost of
+// cooperating.  On CDNA4 the cooperation cost is the (m, l, o) partial
+// traffic through global memory, so each tree node is either
+//   * shared: its pages (plus any folded ancestors') are streamed once per
+//     KV head for all requests below it, split into page runs that each
+//     write one partial per query row, or
+//   * folded: its pages ride along as a prefix of each child's run, read
+//     again by every child group but adding no partials of its own.
+// A node is shared when the bytes it saves, (groups below - 1) x its bytes,
+// exceed `share_margin` x the partial bytes sharing adds (cf. the CREDIT
+// summary, section III.B "Traffic Model": the saving is the removed reread
+// bytes, while fixed traffic stays).  Runs are sized so that the work items
+// fill the GPU's resident wave slots about `rounds` times (cf. CREDIT
+// section III.D "Occupancy": the wave count enters the execution time).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <limits>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/cap_bench.h"
+#include "cap_internal.h"
+
+using cap::WorkItem;
+
+namespace {
+
+thread_local std::string g_err;
+
+cap_status fail(cap_status st, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+}  // namespace
+
+struct cap_tree {
+    cap_attn_desc attn{};
+    int32_t N = 0, R = 0, G = 0;
+    std::vector<int32_t> parent, ntok;
+    std::vector<int64_t> page_off;
+    std::vector<int32_t> page_ids;
+    std::vector<int32_t> path_off, path_nodes;
+    int64_t num_pool_pages = 0;
+    // derived
+    std::vector<std::vector<int32_t>> children;
+    std::vector<int32_t> req_off, req_list;   // requests whose path contains node (sorted)
+    std::vector<int32_t> end_off, end_list;   // requests whose path ends at node
+    std::vector<int64_t> ctx_len;
+    int64_t unique_tokens = 0, sum_ctx = 0;
+    const int32_t *dev_pages = nullptr;       // device copy of page_ids (may be null)
+};
+
+struct cap_plan {
+    const cap_tree *tree = nullptr;
+    cap_plan_stats stats{};
+    std::vector<WorkItem> items;
+    std::vector<int32_t> stream;      // (tree page index << 5) | (ntok - 1)
+    std::vector<int32_t> rows;        // request ids
+    std::vector<int32_t> merge_off, merge_rows;
+    // device image
+    size_t off_items = 0, off_stream = 0, off_rows = 0, off_moff = 0, off_mrows = 0, dev_bytes = 0;
+    std::vector<unsigned char> host_image;
+    void *dev = nullptr;
+};
+
+namespace {
+
+cap_status check_attn(const cap_attn_desc *a)
+{
+    if (!a) return fail(CAP_ERR_INVALID_ARG, "attn desc is NULL");
+    if (a->num_q_heads <= 0 || a->num_kv_heads <= 0)
+        return fail(CAP_ERR_UNSUPPORTED, "head counts must be positive (Hq=%d, Hkv=%d)",
+                    a->num_q_heads, a->num_kv_heads);
+    if (a->num_q_heads % a->num_kv_heads != 0)
+        return fail(CAP_ERR_UNSUPPORTED, "Hq=%d is not a multiple of Hkv=%d", a->num_q_heads,
+                    a->num_kv_heads);
+    const int G = a->num_q_heads / a->num_kv_heads;
+    if (G > cap::kRowsPerItem || cap::kRowsPerItem % G != 0)
+        return fail(CAP_ERR_UNSUPPORTED, "GQA group size %d not in {1,2,4,8,16,32}", G);
+    if (a->head_dim != 64 && a->head_dim != 128)
+        return fail(CAP_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", a->head_dim);
+    if (a->page_size != cap::kPage)
+        return fail(CAP_ERR_UNSUPPORTED, "page_size %d != 16", a->page_size);
+    if (!(a->sm_scale > 0.f) || !std::isfinite(a->sm_scale))
+        return fail(CAP_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+    return CAP_OK;
+}
+
+// Validate and copy the description into a new tree object (host only).
+cap_status build_tree(const cap_attn_desc *attn, const cap_tree_desc *d, cap_tree **out)
+{
+    cap_status st = check_attn(attn);
+    if (st != CAP_OK) return st;
+    if (!d) return fail(CAP_ERR_INVALID_ARG, "tree desc is NULL");
+    const int N = d->num_nodes, R = d->num_requests;
+    if (N <= 0) return fail(CAP_ERR_BAD_TREE, "num_nodes must be > 0");
+    if (R <= 0) return fail(CAP_ERR_BAD_TREE, "num_requests must be > 0");
+    if (!d->parent || !d->num_tokens || !d->page_offsets || !d->path_offsets || !d->path_nodes)
+        return fail(CAP_ERR_INVALID_ARG, "a tree array pointer is NULL");
+    if (d->num_pool_pages <= 0 || d->num_pool_pages > std::numeric_limits<int32_t>::max())
+        return fail(CAP_ERR_BAD_TREE, "num_pool_pages %lld out of range",
+                    (long long)d->num_pool_pages);
+    if (d->page_offsets[0] != 0) return fail(CAP_ERR_BAD_TREE, "page_offsets[0] != 0");
+    for (int i = 0; i < N; ++i) {
+        const int p = d->parent[i];
+        if (p < -1 || p >= i)
+            return fail(CAP_ERR_BAD_TREE, "node %d: parent %d must be -1 or a smaller node id", i, p);
+        if (d->num_tokens[i] < 0) return fail(CAP_ERR_BAD_TREE, "node %d: negative token count", i);
+        const int64_t want = (d->num_tokens[i] + cap::kPage - 1) / cap::kPage;
+        const int64_t have = d->page_offsets[i + 1] - d->page_offsets[i];
+        if (have != want)
+            return fail(CAP_ERR_BAD_TREE, "node %d: %lld pages for %d tokens (need %lld)", i,
+                        (long long)have, d->num_tokens[i], (long long)want);
+    }
+    const int64_t total_pages = d->page_offsets[N];
+    if (total_pages >= (int64_t(1) << 26))
+        return fail(CAP_ERR_UNSUPPORTED, "tree has %lld pages (limit 2^26)", (long long)total_pages);
+    if (total_pages > 0 && !d->page_ids) return fail(CAP_ERR_INVALID_ARG, "page_ids is NULL");
+    {
+        std::vector<int32_t> ids(d->page_ids, d->page_ids + total_pages);
+        for (int64_t i = 0; i < total_pages; ++i)
+            if (ids[i] < 0 || ids[i] >= d->num_pool_pages)
+                return fail(CAP_ERR_BAD_TREE, "page_ids[%lld] = %d outside the pool of %lld pages",
+                            (long long)i, ids[i], (long long)d->num_pool_pages);
+        std::sort(ids.begin(), ids.end());
+        for (int64_t i = 1; i < total_pages; ++i)
+            if (ids[i] == ids[i - 1])
+                return fail(CAP_ERR_BAD_TREE, "physical page %d is owned twice", ids[i]);
+    }
+    if (d->path_offsets[0] != 0) return fail(CAP_ERR_BAD_TREE, "path_offsets[0] != 0");
+    std::vector<int64_t> ctx(R, 0);
+    for (int r = 0; r < R; ++r) {
+        const int b = d->path_offsets[r], e = d->path_offsets[r + 1];
+        if (e <= b) return fail(CAP_ERR_BAD_TREE, "request %d has an empty path", r);
+        for (int j = b; j < e; ++j) {
+            const int nd = d->path_nodes[j];
+            if (nd < 0 || nd >= N) return fail(CAP_ERR_BAD_TREE, "request %d: node %d out of range", r, nd);
+            if (j == b && d->parent[nd] != -1)
+                return fail(CAP_ERR_BAD_TREE, "request %d: path starts at node %d, not a root", r, nd);
+            if (j > b && d->parent[nd] != d->path_nodes[j - 1])
+                return fail(CAP_ERR_BAD_TREE, "request %d: node %d does not follow its parent", r, nd);
+            ctx[r] += d->num_tokens[nd];
+        }
+        if (ctx[r] == 0) return fail(CAP_ERR_BAD_TREE, "request %d has no context tokens", r);
+    }
+
+    cap_tree *t = new (std::nothrow) cap_tree();
+    if (!t) return fail(CAP_ERR_INVALID_ARG, "out of host memory");
+    t->attn = *attn;
+    t->N = N;
+    t->R = R;
+    t->G = attn->num_q_heads / attn->num_kv_heads;
+    t->parent.assign(d->parent, d->parent + N);
+    t->ntok.assign(d->num_tokens, d->num_tokens + N);
+    t->page_off.assign(d->page_offsets, d->page_offsets + N + 1);
+    t->page_ids.assign(d->page_ids, d->page_ids + total_pages);
+    t->path_off.assign(d->path_offsets, d->path_offsets + R + 1);
+    t->path_nodes.assign(d->path_nodes + 0, d->path_nodes + d->path_offsets[R]);
+    t->num_pool_pages = d->num_pool_pages;
+    t->ctx_len = ctx;
+    t->children.assign(N, {});
+    for (int i = 0; i < N; ++i)
+        if (t->parent[i] >= 0) t->children[t->parent[i]].push_back(i);
+    std::vector<std::vector<int32_t>> under(N), ends(N);
+    for (int r = 0; r < R; ++r) {
+        for (int j = t->path_off[r]; j < t->path_off[r + 1]; ++j) under[t->path_nodes[j]].push_back(r);
+        ends[t->path_nodes[t->path_off[r + 1] - 1]].push_back(r);
+    }
+    t->req_off.assign(N + 1, 0);
+    t->end_off.assign(N + 1, 0);
+    for (int i = 0; i < N; ++i) {
+        t->req_off[i + 1] = t->req_off[i] + (int32_t)under[i].size();
+        t->end_off[i + 1] = t->end_off[i] + (int32_t)ends[i].size();
+        t->req_list.insert(t->req_list.end(), under[i].begin(), under[i].end());
+        t->end_list.insert(t->end_list.end(), ends[i].begin(), ends[i].end());
+        t->unique_tokens += t->ntok[i];
+    }
+    for (int r = 0; r < R; ++r) t->sum_ctx += ctx[r];
+    *out = t;
+    return CAP_OK;
+}
+
+// ------------------------------------------------------------------ planner
+
+struct Group {
+    std::vector<int32_t> reqs;     // sorted request ids
+    std::vector<int32_t> entries;  // page-stream entries
+};
+
+struct Planner {
+    const cap_tree &t;
+    cap_plan_opts o;
+    int D, Hkv, G;
+    int64_t head_tok_bytes;        // K+V bytes per token per KV head
+    int64_t partial_row_bytes;     // partial bytes per query row (o, m, l)
+    int target_pages = 0;
+    std::vector<Group> groups;
+
+    Planner(const cap_tree &tree, const cap_plan_opts &opts) : t(tree), o(opts)
+    {
+        D = t.attn.head_dim;
+        Hkv = t.attn.num_kv_heads;
+        G = t.G;
+        head_tok_bytes = 4LL * D;
+        partial_row_bytes = 4LL * D + 8;
+    }
+
+    void node_entries(int n, std::vector<int32_t> &out) const
+    {
+        const int64_t np = t.page_off[n + 1] - t.page_off[n];
+        for (int64_t p = 0; p < np; ++p) {
+            const int64_t left = t.ntok[n] - p * cap::kPage;
+            const int nt = (int)std::min<int64_t>(cap::kPage, left);
+            out.push_back((int32_t)(((t.page_off[n] + p) << 5) | (nt - 1)));
+        }
+    }
+
+    int rows_per_item() const { return o.max_rows; }
+    int reqs_per_item() const { return std::max(1, rows_per_item() / G); }
+
+    int64_t estimate_chunks(int64_t pages) const
+    {
+        const int tp = target_pages > 0 ? target_pages : 16;
+        return std::max<int64_t>(1, (pages + tp - 1) / tp);
+    }
+
+    bool decide_share(int n, int64_t prefix_tokens) const
+    {
+        if (o.share_mode == 1) return t.ntok[n] > 0 || prefix_tokens > 0;
+        if (o.share_mode == 0) return false;
+        const int64_t below = (int64_t)t.children[n].size() + (t.end_off[n + 1] > t.end_off[n] ? 1 : 0);
+        if (below <= 1) return false;                 // a chain: folding costs nothing
+        const int64_t tok = t.ntok[n] + prefix_tokens;
+        if (tok == 0) return false;
+        const int64_t nreq = t.req_off[n + 1] - t.req_off[n];
+        const int64_t saved = (below - 1) * tok * head_tok_bytes;
+        const int64_t pages = (tok + cap::kPage - 1) / cap::kPage;
+        const int64_t added = 2 * nreq * G * partial_row_bytes * estimate_chunks(pages);
+        return (double)saved > (double)o.share_margin * (double)added;
+    }
+
+    void emit(const int32_t *reqs, int nreq, const std::vector<int32_t> &entries)
+    {
+        if (entries.empty() || nreq == 0) return;
+        Group g;
+        g.reqs.assign(reqs, reqs + nreq);
+        g.entries = entries;
+        groups.push_back(std::move(g));
+    }
+
+    void walk(int n, std::vector<int32_t> prefix, int64_t prefix_tokens)
+    {
+        std::vector<int32_t> entries = std::move(prefix);
+        node_entries(n, entries);
+        const int64_t tok = prefix_tokens + t.ntok[n];
+        if (decide_share(n, prefix_tokens)) {
+            emit(&t.req_list[t.req_off[n]], t.req_off[n + 1] - t.req_off[n], entries);
+            for (int c : t.children[n]) walk(c, {}, 0);
+        } else {
+            emit(t.end_list.data() + t.end_off[n], t.end_off[n + 1] - t.end_off[n], entries);
+            for (int c : t.children[n]) walk(c, entries, tok);
+        }
+    }
+
+    void build_groups()
+    {
+        // first pass with a provisional chunk size, then refine the target
+        // using the resulting work volume and plan again
+        for (int pass = 0; pass < 2; ++pass) {
+            groups.clear();
+            for (int n = 0; n < t.N; ++n)
+                if (t.parent[n] == -1) walk(n, {}, 0);
+            int64_t W = 0;   // item-pages if nothing were split
+            for (const Group &g : groups) {
+                const int64_t rg = ((int64_t)g.reqs.size() + reqs_per_item() - 1) / reqs_per_item();
+                W += (int64_t)g.entries.size() * rg * Hkv;
+            }
+            if (o.split_pages > 0) {
+                target_pages = o.split_pages;
+                break;
+            }
+            const double slots = (double)o.num_cus * o.waves_per_cu * o.rounds;
+            target_pages = (int)std::max<int64_t>(4, (int64_t)std::ceil((double)W / slots));
+        }
+    }
+};
+
+void fill_defaults(cap_plan_opts &o)
+{
+    if (o.share_mode == 2) o.share_mode = -1;
+    if (o.max_rows == 0) o.max_rows = 32;
+    if (o.num_cus == 0) o.num_cus = 256;
+    if (o.waves_per_cu == 0) o.waves_per_cu = 4;
+    if (o.rounds == 0.f) o.rounds = 2.0f;
+    if (o.share_margin == 0.f) o.share_margin = 1.0f;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t cap_abi_version(void) { return CAP_ABI_VERSION; }
+
+const char *cap_last_error(void) { return g_err.c_str(); }
+
+void cap_plan_opts_default(cap_plan_opts *opts)
+{
+    if (!opts) return;
+    std::memset(opts, 0, sizeof *opts);
+    opts->share_mode = -1;
+    fill_defaults(*opts);
+}
+
+cap_status cap_tree_device_bytes(const cap_attn_desc *attn, const cap_tree_desc *tree, size_t *bytes)
+{
+    if (!tree || !bytes) return fail(CAP_ERR_INVALID_ARG, "NULL argument");
+    cap_status st = check_attn(attn);
+    if (st != CAP_OK) return st;
+    if (tree->num_nodes <= 0 || !tree->page_offsets) return fail(CAP_ERR_BAD_TREE, "empty tree");
+    const int64_t pages = tree->page_offsets[tree->num_nodes];
+    if (pages < 0) return fail(CAP_ERR_BAD_TREE, "negative page count");
+    *bytes = align_up((size_t)std::max<int64_t>(pages, 1) * 4);
+    return CAP_OK;
+}
+
+cap_status cap_tree_upload(const cap_attn_desc *attn, const cap_tree_desc *desc, void *dev_buf,
+                           size_t dev_bytes, cap_stream_t stream, cap_tree **out)
+{
+    if (!out) return fail(CAP_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    cap_tree *t = nullptr;
+    cap_status st = build_tree(attn, desc, &t);
+    if (st != CAP_OK) return st;
+    if (dev_buf) {
+        const size_t need = t->page_ids.size() * 4;
+        if (dev_bytes < need || (reinterpret_cast<uintptr_t>(dev_buf) & 15)) {
+            delete t;
+            return fail(CAP_ERR_WORKSPACE, "tree device buffer: %zu bytes given, %zu needed (16-byte aligned)",
+                        dev_bytes, need);
+        }
+        if (need) {
+            hipError_t e = hipMemcpyAsync(dev_buf, t->page_ids.data(), need, hipMemcpyHostToDevice,
+                                          reinterpret_cast<hipStream_t>(stream));
+            if (e != hipSuccess) {
+                delete t;
+                return fail(CAP_ERR_HIP, "tree upload copy failed: %s", hipGetErrorString(e));
+            }
+        }
+        t->dev_pages = static_cast<const int32_t *>(dev_buf);
+    }
+    *out = t;
+    return CAP_OK;
+}
+
+void cap_tree_free(cap_tree *tree) { delete tree; }
+
+cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap_plan **out)
+{
+    if (!tree || !out) return fail(CAP_ERR_INVALID_ARG, "NULL argument");
+    *out = nullptr;
+    const auto t0 = std::chrono::steady_clock::now();
+    cap_plan_opts o;
+    if (opts_in) o = *opts_in; else cap_plan_opts_default(&o);
+    fill_defaults(o);
+    if (o.share_mode < -1 || o.share_mode > 1)
+        return fail(CAP_ERR_INVALID_ARG, "share_mode %d not in {-1, 0, 1, 2}", o.share_mode);
+    if (o.max_rows != 16 && o.max_rows != 32)
+        return fail(CAP_ERR_INVALID_ARG, "max_rows %d not in {16, 32}", o.max_rows);
+    if (o.max_rows < tree->G)
+        return fail(CAP_ERR_INVALID_ARG, "max_rows %d below the GQA group %d", o.max_rows, tree->G);
+    if (o.split_pages < 0 || o.num_cus < 0 || o.waves_per_cu < 0 || !(o.rounds > 0.f) ||
+        !(o.share_margin > 0.f))
+        return fail(CAP_ERR_INVALID_ARG, "negative planner option");
+
+    cap_plan *p = new (std::nothrow) cap_plan();
+    if (!p) return fail(CAP_ERR_INVALID_ARG, "out of host memory");
+    p->tree = tree;
+    const int Hkv = tree->attn.num_kv_heads, Hq = tree->attn.num_q_heads, D = tree->attn.head_dim;
+    Planner pl(*tree, o);
+    pl.build_groups();
+
+    // tasks: (page run, request subgroup); balanced splits of both
+    struct Task { int32_t so, np, ro, nr, sb; int64_t cost; };
+    std::vector<Task> tasks;
+    std::vector<std::vector<int32_t>> req_rows(tree->R);
+    int32_t slot_rows = 0;
+    for (const Group &g : pl.groups) {
+        const int64_t npg = (int64_t)g.entries.size();
+        const int64_t k = std::max<int64_t>(1, (npg + pl.target_pages - 1) / pl.target_pages);
+        const int nreq = (int)g.reqs.size();
+        const int rg = (nreq + pl.reqs_per_item() - 1) / pl.reqs_per_item();
+        const int32_t so0 = (int32_t)p->stream.size();
+        p->stream.insert(p->stream.end(), g.entries.begin(), g.entries.end());
+        const int32_t ro0 = (int32_t)p->rows.size();
+        p->rows.insert(p->rows.end(), g.reqs.begin(), g.reqs.end());
+        for (int64_t ci = 0; ci < k; ++ci) {
+            const int64_t pb = npg * ci / k, pe = npg * (ci + 1) / k;
+            for (int ri = 0; ri < rg; ++ri) {
+                const int rb = (int)((int64_t)nreq * ri / rg), re = (int)((int64_t)nreq * (ri + 1) / rg);
+                Task tk{(int32_t)(so0 + pb), (int32_t)(pe - pb), ro0 + rb, re - rb, slot_rows,
+                        (pe - pb) * 16};
+                for (int q = rb; q < re; ++q) req_rows[g.reqs[q]].push_back(slot_rows + (q - rb));
+                slot_rows += re - rb;
+                tasks.push_back(tk);
+            }
+        }
+    }
+    // longest runs first; the row subgroups of one run stay adjacent
+    std::stable_sort(tasks.begin(), tasks.end(),
+                     [](const Task &a, const Task &b) { return a.np > b.np; });
+    // items: for each page run, for each KV head, its request subgroups back to
+    // back, so the waves that read the same pages share a workgroup (and its L1)
+    p->items.reserve(tasks.size() * Hkv);
+    for (size_t i = 0; i < tasks.size();) {
+        size_t j = i + 1;
+        while (j < tasks.size() && tasks[j].so == tasks[i].so && tasks[j].np == tasks[i].np) ++j;
+        for (int h = 0; h < Hkv; ++h)
+            for (size_t k = i; k < j; ++k)
+                p->items.push_back(WorkItem{tasks[k].so, tasks[k].np, h, tasks[k].ro, tasks[k].nr, tasks[k].sb});
+        i = j;
+    }
+    p->merge_off.assign(tree->R + 1, 0);
+    int32_t maxp = 0;
+    for (int r = 0; r < tree->R; ++r) {
+        p->merge_off[r + 1] = p->merge_off[r] + (int32_t)req_rows[r].size();
+        p->merge_rows.insert(p->merge_rows.end(), req_rows[r].begin(), req_rows[r].end());
+        maxp = std::max<int32_t>(maxp, (int32_t)req_rows[r].size());
+    }
+
+    // device image: items | stream | rows | merge_off | merge_rows
+    p->off_items = 0;
+    p->off_stream = align_up(p->items.size() * sizeof(WorkItem));
+    p->off_rows = p->off_stream + align_up(p->stream.size() * 4);
+    p->off_moff = p->off_rows + align_up(p->rows.size() * 4);
+    p->off_mrows = p->off_moff + align_up(p->merge_off.size() * 4);
+    p->dev_bytes = std::max<size_t>(p->off_mrows + align_up(p->merge_rows.size() * 4), kAlign);
+    p->host_image.assign(p->dev_bytes, 0);
+    std::memcpy(p->host_image.data() + p->off_items, p->items.data(), p->items.size() * sizeof(WorkItem));
+    std::memcpy(p->host_image.data() + p->off_stream, p->stream.data(), p->stream.size() * 4);
+    std::memcpy(p->host_image.data() + p->off_rows, p->rows.data(), p->rows.size() * 4);
+    std::memcpy(p->host_image.data() + p->off_moff, p->merge_off.data(), p->merge_off.size() * 4);
+    std::memcpy(p->host_image.data() + p->off_mrows, p->merge_rows.data(), p->merge_rows.size() * 4);
+
+    cap_plan_stats &s = p->stats;
+    s.num_items = (int64_t)p->items.size();
+    s.num_tasks = (int64_t)tasks.size();
+    s.num_groups = (int64_t)pl.groups.size();
+    s.partial_rows = slot_rows;
+    const size_t slots = (size_t)slot_rows * Hq;
+    s.workspace_bytes = (int64_t)(align_up(slots * D * 4) + 2 * align_up(slots * 4));
+    s.plan_device_bytes = (int64_t)p->dev_bytes;
+    s.tree_device_bytes = (int64_t)align_up(std::max<size_t>(tree->page_ids.size(), 1) * 4);
+    const int64_t page_bytes = 2LL * cap::kPage * D * 2;   // K+V of one page, one head
+    int64_t streamed = 0;
+    for (const Task &tk : tasks) streamed += (int64_t)tk.np * page_bytes * Hkv;
+    s.kv_bytes_streamed = streamed;
+    s.kv_bytes_unique = tree->unique_tokens * 4LL * D * Hkv;
+    s.kv_bytes_unshared = tree->sum_ctx * 4LL * D * Hkv;
+    s.partial_bytes = (int64_t)slots * (4LL * D + 8);
+    s.max_partials_per_request = maxp;
+    s.max_pages_per_item = pl.target_pages;
+    s.plan_host_us = std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count();
+    *out = p;
+    return CAP_OK;
+}
+
+cap_status cap_plan_get_stats(const cap_plan *plan, cap_plan_stats *stats)
+{
+    if (!plan || !stats) return fail(CAP_ERR_INVALID_ARG, "NULL argument");
+    *stats = plan->stats;
+    return CAP_OK;
+}
+
+cap_status cap_plan_get_view(const cap_plan *plan, cap_plan_view *v)
+{
+    if (!plan || !v) return fail(CAP_ERR_INVALID_ARG, "NULL argument");
+    v->num_items = (int32_t)plan->items.size();
+    v->items = reinterpret_cast<const cap_work_item *>(plan->items.data());
+    v->stream_len = (int32_t)plan->stream.size();
+    v->stream = plan->stream.data();
+    v->rows_len = (int32_t)plan->rows.size();
+    v->rows = plan->rows.data();
+    v->num_requests = plan->tree->R;
+    v->merge_off = plan->merge_off.data();
+    v->merge_rows = plan->merge_rows.data();
+    return CAP_OK;
+}
+
+cap_status cap_plan_upload(cap_plan *plan, void *dev_buf, size_t bytes, cap_stream_t stream)
+{
+    if (!plan || !dev_buf) return fail(CAP_ERR_INVALID_ARG, "NULL argument");
+    if (!plan->tree->dev_pages)
+        return fail(CAP_ERR_STATE, "the plan's tree has no device page table (uploaded with dev_buf = NULL)");
+    if (bytes < plan->dev_bytes || (reinterpret_cast<uintptr_t>(dev_buf) & (kAlign - 1)))
+        return fail(CAP_ERR_WORKSPACE, "plan buffer: %zu bytes given, %zu needed (256-byte aligned)",
+                    bytes, plan->dev_bytes);
+    hipError_t e = hipMemcpyAsync(dev_buf, plan->host_image.data(), plan->dev_bytes,
+                                  hipMemcpyHostToDevice, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(CAP_ERR_HIP, "plan upload copy failed: %s", hipGetErrorString(e));
+    plan->dev = dev_buf;
+    return CAP_OK;
+}
+
+static cap_status split_workspace(const cap_plan *p, const void *ws, size_t ws_bytes, float **o,
+                                  float **m, float **l)
+{
+    if ((size_t)p->stats.workspace_bytes > ws_bytes || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)))
+        return fail(CAP_ERR_WORKSPACE, "workspace: %zu bytes given, %lld needed (256-byte aligned)",
+                    ws_bytes, (long long)p->stats.workspace_bytes);
+    const size_t slots = (size_t)p->stats.partial_rows * p->tree->attn.num_q_heads;
+    char *b = (char *)ws;
+    *o = (float *)b;
+    *m = (float *)(b + align_up(slots * p->tree->attn.head_dim * 4));
+    *l = (float *)(b + align_up(slots * p->tree->attn.head_dim * 4) + align_up(slots * 4));
+    return CAP_OK;
+}
+
+cap_status cap_decode_attention(const cap_plan *plan, const void *q, const void *k_pool,
+                                const void *v_pool, void *workspace, size_t ws_bytes,
+                                cap_stream_t stream)
+{
+    if (!plan || !q || !k_pool || !v_pool || !workspace) return fail(CAP_ERR_INVALID_ARG, "NULL argument");
+    if (!plan->dev) return fail(CAP_ERR_STATE, "plan not uploaded (call cap_plan_upload first)");
+    if (((uintptr_t)q | (uintptr_t)k_pool | (uintptr_t)v_pool) & 15)
+        return fail(CAP_ERR_INVALID_ARG, "q, k_pool and v_pool must be 16-byte aligned");
+    cap::DecodeArgs a{};
+    cap_status st = split_workspace(plan, workspace, ws_bytes, &a.part_o, &a.part_m, &a.part_l);
+    if (st != CAP_OK) return st;
+    const char *d = static_cast<const char *>(plan->dev);
+    a.items = reinterpret_cast<const WorkItem *>(d + plan->off_items);
+    a.stream = reinterpret_cast<const int32_t *>(d + plan->off_stream);
+    a.rows = reinterpret_cast<const int32_t *>(d + plan->off_rows);
+    a.tree_pages = plan->tree->dev_pages;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k_pool = static_cast<const uint16_t *>(k_pool);
+    a.v_pool = static_cast<const uint16_t *>(v_pool);
+    a.n_items = (int32_t)plan->items.size();
+    a.Hq = plan->tree->attn.num_q_heads;
+    a.Hkv = plan->tree->attn.num_kv_heads;
+    a.G = plan->tree->G;
+    a.scale_log2 = (float)((double)plan->tree->attn.sm_scale * 1.4426950408889634);
+    const int e = cap::launch_decode(a, plan->tree->attn.head_dim, stream);
+    if (e != 0) return fail(CAP_ERR_HIP, "decode launch failed: %s", cap::hip_error_string(e));
+    return CAP_OK;
+}
+
+cap_status cap_merge_partials(const cap_plan *plan, const void *workspace, size_t ws_bytes, void *out,
+                              cap_stream_t stream)
+{
+    if (!plan || !workspace || !out) return fail(CAP_ERR_INVALID_ARG, "NULL argument");
+    if (!plan->dev) return fail(CAP_ERR_STATE, "plan not uploaded (call cap_plan_upload first)");
+    if ((uintptr_t)out & 15) return fail(CAP_ERR_INVALID_ARG, "out must be 16-byte aligned");
+    cap::MergeArgs a{};
+    float *o, *m, *l;
+    cap_status st = split_workspace(plan, workspace, ws_bytes, &o, &m, &l);
+    if (st != CAP_OK) return st;
+    const char *d = static_cast<const char *>(plan->dev);
+    a.merge_off = reinterpret_cast<const int32_t *>(d + plan->off_moff);
+    a.merge_rows = reinterpret_cast<const int32_t *>(d + plan->off_mrows);
+    a.part_o = o;
+    a.part_m = m;
+    a.part_l = l;
+    a.out = static_cast<uint16_t *>(out);
+    a.R = plan->tree->R;
+    a.Hq = plan->tree->attn.num_q_heads;
+    const int e = cap::launch_merge(a, plan->tree->attn.head_dim, stream);
+    if (e != 0) return fail(CAP_ERR_HIP, "merge launch failed: %s", cap::hip_error_string(e));
+    return CAP_OK;
+}
+
+void cap_plan_free(cap_plan *plan) { delete plan; }
+
+// ------------------------------------------------------------ bench helpers
+
+cap_status cap_bench_fill(void *buf, size_t bytes, uint32_t value, cap_stream_t stream)
+{
+    if (!buf || bytes == 0 || (bytes & 15) || ((uintptr_t)buf & 15))
+        return fail(CAP_ERR_INVALID_ARG, "fill: bad buffer or size");
+    const int e = cap::launch_fill(buf, bytes / 4, value, stream);
+    return e ? fail(CAP_ERR_HIP, "fill launch failed: %s", cap::hip_error_string(e)) : CAP_OK;
+}
+
+cap_status cap_bench_read(const void *buf, size_t bytes, void *sink, cap_stream_t stream)
+{
+    if (!buf || !sink || bytes == 0 || (bytes & 15) || ((uintptr_t)buf & 15))
+        return fail(CAP_ERR_INVALID_ARG, "read: bad buffer or size");
+    const int e = cap::launch_read(buf, bytes / 16, sink, stream);
+    return e ? fail(CAP_ERR_HIP, "read launch failed: %s", cap::hip_error_string(e)) : CAP_OK;
+}
+
+cap_status cap_bench_copy(void *dst, const void *src, size_t bytes, cap_stream_t stream)
+{
+    if (!dst || !src || bytes == 0 || (bytes & 15) || (((uintptr_t)dst | (uintptr_t)src) & 15))
+        return fail(CAP_ERR_INVALID_ARG, "copy: bad buffer or size");
+    const int e = cap::launch_copy(dst, src, bytes / 16, stream);
+    return e ? fail(CAP_ERR_HIP, "copy launch failed: %s", cap::hip_error_string(e)) : CAP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// cap_internal.h -- structures shared by the host side of libcap and its
+// HIP kernels.  Not part of the public ABI.
+#pragma once
+
+#include <stdint.h>
+
+#include "../../include/cap.h"
+
+namespace cap {
+
+// Layout constants of the paged KV cache.
+constexpr int kPage = 16;            // tokens per page
+constexpr int kWaveSize = 64;        // CDNA wavefront
+constexpr int kWavesPerBlock = 4;    // waves per workgroup in the decode kernel
+constexpr int kRowsPerItem = 32;     // query rows one wave can hold (two 16-row MFMA blocks)
+
+// One wave's work: a run of KV pages of one KV head applied to up to 32
+// query rows (nreq requests x G query heads).  Same layout as cap_work_item.
+struct WorkItem {
+    int32_t stream_off;
+    int32_t npages;
+    int32_t head;
+    int32_t row_off;
+    int32_t nreq;
+    int32_t slot_base;
+};
+static_assert(sizeof(WorkItem) == sizeof(cap_work_item), "work item layout");
+
+struct DecodeArgs {
+    const WorkItem *items;
+    const int32_t *stream;       // page-stream entries: (tree page index << 5) | (ntok - 1)
+    const int32_t *tree_pages;   // tree page index -> physical page
+    const int32_t *rows;         // request ids of each item's request list
+    const uint16_t *q;           // [R][Hq][D] bf16
+    const uint16_t *k_pool;      // [pages][Hkv][D/8][16][8] bf16
+    const uint16_t *v_pool;      // [pages][Hkv][D][16] bf16
+    float *part_o;               // [slots][D]
+    float *part_m;               // [slots]
+    float *part_l;               // [slots]
+    int32_t n_items;
+    int32_t Hq, Hkv, G;
+    float scale_log2;            // sm_scale * log2(e)
+};
+
+struct MergeArgs {
+    const int32_t *merge_off;    // [R+1]
+    const int32_t *merge_rows;   // partial rows per request
+    const float *part_o;
+    const float *part_m;
+    const float *part_l;
+    uint16_t *out;               // [R][Hq][D] bf16
+    int32_t R, Hq;
+};
+
+// Kernel launchers (cap_kernels.hip); return the hipError_t as int.
+int launch_decode(const DecodeArgs &a, int head_dim, void *stream);
+int launch_merge(const MergeArgs &a, int head_dim, void *stream);
+int launch_fill(void *buf, size_t words, uint32_t value, void *stream);
+int launch_read(const void *buf, size_t vec16, void *sink, void *stream);
+int launch_copy(void *dst, const void *src, size_t vec16, void *stream);
+const char *hip_error_string(int err);
+
+}  // namespace cap

@@ -1,0 +1,394 @@
+// cap_kernels.hip -- gfx950 (CDNA4) kernels of libcap.
+//
+// decode_kernel: one wavefront per work item.  A work item is a run of KV
+// pages of one KV head together with every query row (requests x GQA heads,
+// up to 32) that reads those pages, so the pages are streamed from HBM once
+// for the whole row group -- the point of the Capillary Kernels project page
+// (abstract, first paragraph): shared prefixes should not be fetched once per
+// request.  Both contractions run on the matrix cores with
+// v_mfma_f32_16x16x32_bf16:
+//
+//   S^T[16 tokens x 16 rows] = K_page[16 x D] . Q^T[D x 16]     (D/32 MFMAs per page)
+//   O^T[16 dims  x 16 rows] += V^T[16 dims x 32 tokens] . P^T   (D/16 MFMAs per 2 pages)
+//
+// The page layouts are chosen so that every MFMA operand is one contiguous
+// 16- or 8-byte global load per lane, straight into VGPRs, with no LDS round
+// trip and no transpose: K pages are [D/8][16][8] (a lane's 8 dims of one
+// token are 16 contiguous bytes, and the 16 tokens of one dim chunk form a
+// contiguous 256-byte line), V pages are [D][16] (a lane's 4 tokens of one
+// dim are 8 contiguous bytes).  The QK output layout (lane n + 16c holds
+// tokens 4c..4c+3 of row n) is exactly the B-operand layout the PV MFMA
+// wants for P, so the probabilities never leave the lane.
+//
+// Softmax is online in base 2 (scale folded with log2 e, exp via v_exp_f32).
+// The running maximum of a row is shared by the four lanes that hold the
+// row (two xor shuffles per 2-page step); the running sum stays per lane and
+// is reduced once at the end.  Each item writes (m, l, o) for its rows into
+// write-once partial slots; merge_kernel combines the partials of each
+// (request, head) with log-sum-exp rescaling (the partial-result combination
+// of the project page's second paragraph, done through global memory/L2
+// because CDNA4 has no cross-CU shared memory).
+#include <hip/hip_runtime.h>
+
+#include "cap_internal.h"
+
+namespace cap {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32x4 ld16(const uint16_t *p)
+{
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+
+__device__ __forceinline__ u32x2 ld8(const uint16_t *p)
+{
+    return *reinterpret_cast<const u32x2 *>(p);
+}
+
+__device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x)
+{
+    return __builtin_amdgcn_exp2f(x);
+}
+
+// KV fragments of one 2-page step, already in MFMA operand layout.
+template <int D>
+struct Step {
+    u32x4 k0[D / 32], k1[D / 32];   // QK A operands, page 0 / page 1
+    u32x2 v0[D / 16], v1[D / 16];   // PV A operand halves, page 0 / page 1
+    int nt0, nt1;                   // valid tokens in page 0 / page 1 (nt1 = 0: no page)
+};
+
+template <int D>
+__device__ __forceinline__ void load_step(Step<D> &f, const DecodeArgs &a, const WorkItem &it,
+                                          int s, int n, int c)
+{
+    const int64_t blk = (int64_t)kPage * D;             // elements per (page, head)
+    const int e0 = a.stream[it.stream_off + 2 * s];
+    const bool has1 = 2 * s + 1 < it.npages;
+    const int64_t p0 = a.tree_pages[e0 >> 5];
+    f.nt0 = (e0 & 31) + 1;
+    const uint16_t *kb = a.k_pool + (p0 * a.Hkv + it.head) * blk;
+    const uint16_t *vb = a.v_pool + (p0 * a.Hkv + it.head) * blk;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) f.k0[i] = ld16(kb + ((4 * i + c) * kPage + n) * 8);
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) f.v0[j] = ld8(vb + (16 * j + n) * kPage + 4 * c);
+    if (has1) {
+        const int e1 = a.stream[it.stream_off + 2 * s + 1];
+        const int64_t p1 = a.tree_pages[e1 >> 5];
+        f.nt1 = (e1 & 31) + 1;
+        const uint16_t *kb1 = a.k_pool + (p1 * a.Hkv + it.head) * blk;
+        const uint16_t *vb1 = a.v_pool + (p1 * a.Hkv + it.head) * blk;
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) f.k1[i] = ld16(kb1 + ((4 * i + c) * kPage + n) * 8);
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) f.v1[j] = ld8(vb1 + (16 * j + n) * kPage + 4 * c);
+    } else {
+        f.nt1 = 0;
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) f.k1[i] = u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) f.v1[j] = u32x2{0, 0};
+    }
+}
+
+// Zero the V elements of tokens >= nt in a page's fragments (they may hold
+// NaN; 0 * NaN would otherwise poison the MFMA sum).
+template <int D>
+__device__ __forceinline__ void mask_v(u32x2 (&v)[D / 16], int nt, int c)
+{
+    const int t = 4 * c;
+    const uint32_t w0 = (t + 0 < nt ? 0x0000FFFFu : 0u) | (t + 1 < nt ? 0xFFFF0000u : 0u);
+    const uint32_t w1 = (t + 2 < nt ? 0x0000FFFFu : 0u) | (t + 3 < nt ? 0xFFFF0000u : 0u);
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) {
+        v[j].x &= w0;
+        v[j].y &= w1;
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void compute_step(Step<D> &f, const u32x4 (&qf)[2][D / 32],
+                                             f32x4 (&o)[2][D / 16], float (&m_run)[2],
+                                             float (&l_run)[2], bool two, float scale, int c)
+{
+    const bool has1 = f.nt1 > 0;
+    if (f.nt0 < kPage) mask_v<D>(f.v0, f.nt0, c);
+    if (f.nt1 < kPage) mask_v<D>(f.v1, f.nt1, c);
+    u32x4 vf[D / 16];
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) vf[j] = u32x4{f.v0[j].x, f.v0[j].y, f.v1[j].x, f.v1[j].y};
+
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        if (b == 1 && !two) break;
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) s0 = mfma(f.k0[i], qf[b][i], s0);
+        if (has1) {
+#pragma unroll
+            for (int i = 0; i < D / 32; ++i) s1 = mfma(f.k1[i], qf[b][i], s1);
+        }
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[j] = s0[j] * scale;
+            x[4 + j] = s1[j] * scale;
+        }
+        if (f.nt0 < kPage) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j] = (4 * c + j < f.nt0) ? x[j] : -INFINITY;
+        }
+        if (f.nt1 < kPage) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[4 + j] = (4 * c + j < f.nt1) ? x[4 + j] : -INFINITY;
+        }
+        float mx = x[0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run[b], mx);
+        const float alpha = fast_exp2(m_run[b] - m_new);
+        m_run[b] = m_new;
+        float p[8];
+        float psum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            p[j] = fast_exp2(x[j] - m_new);
+            psum += p[j];
+        }
+        l_run[b] = l_run[b] * alpha + psum;
+        bf16x8 pb;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pb[j] = (__bf16)p[j];
+        const u32x4 pw = __builtin_bit_cast(u32x4, pb);
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) {
+            o[b][j] *= alpha;
+            o[b][j] = mfma(vf[j], pw, o[b][j]);
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kWaveSize * kWavesPerBlock) void decode_kernel(DecodeArgs a)
+{
+    const int lane = threadIdx.x & (kWaveSize - 1);
+    const int n = lane & 15, c = lane >> 4;
+    const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
+    if (wid >= a.n_items) return;
+    const WorkItem it = a.items[wid];
+    const int G = a.G;
+    const int nrows = it.nreq * G;
+    const bool two = nrows > 16;
+
+    // Q fragments (B operand of QK): lane (n, c) holds row 16b+n, dims 8(4i+c)..+7.
+    u32x4 qf[2][D / 32];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int row = 16 * b + n;
+        if (row < nrows) {
+            const int req = a.rows[it.row_off + row / G];
+            const int h = it.head * G + row % G;
+            const uint16_t *qb = a.q + ((int64_t)req * a.Hq + h) * D;
+#pragma unroll
+            for (int i = 0; i < D / 32; ++i) qf[b][i] = ld16(qb + 8 * (4 * i + c));
+        } else {
+#pragma unroll
+            for (int i = 0; i < D / 32; ++i) qf[b][i] = u32x4{0, 0, 0, 0};
+        }
+    }
+
+    f32x4 o[2][D / 16];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) o[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run[2] = {-INFINITY, -INFINITY};
+    float l_run[2] = {0.f, 0.f};
+
+    // Two register buffers: the loads of step s+1 are in flight while step s computes.
+    const int nsteps = (it.npages + 1) >> 1;
+    Step<D> fa, fb;
+    load_step<D>(fa, a, it, 0, n, c);
+    for (int s = 0; s < nsteps; s += 2) {
+        if (s + 1 < nsteps) load_step<D>(fb, a, it, s + 1, n, c);
+        compute_step<D>(fa, qf, o, m_run, l_run, two, a.scale_log2, c);
+        if (s + 1 >= nsteps) break;
+        if (s + 2 < nsteps) load_step<D>(fa, a, it, s + 2, n, c);
+        compute_step<D>(fb, qf, o, m_run, l_run, two, a.scale_log2, c);
+    }
+
+    // Partials: slot = (slot_base + row / G) * Hq + head * G + row % G.
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        if (b == 1 && !two) break;
+        float l = l_run[b];
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        const int row = 16 * b + n;
+        if (row < nrows) {
+            const int64_t slot = (int64_t)(it.slot_base + row / G) * a.Hq + it.head * G + row % G;
+            float *po = a.part_o + slot * D + 4 * c;
+#pragma unroll
+            for (int j = 0; j < D / 16; ++j) *reinterpret_cast<f32x4 *>(po + 16 * j) = o[b][j];
+            if (c == 0) {
+                a.part_m[slot] = m_run[b];
+                a.part_l[slot] = l;
+            }
+        }
+    }
+}
+
+// One wave per (request, query head): out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i.
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a)
+{
+    constexpr int V = D / 64;   // values per lane
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+    if (wid >= a.R * a.Hq) return;
+    const int r = wid / a.Hq, h = wid % a.Hq;
+    const int beg = a.merge_off[r], end = a.merge_off[r + 1];
+    float M = -INFINITY;
+    for (int k = beg; k < end; ++k) {
+        const int64_t slot = (int64_t)a.merge_rows[k] * a.Hq + h;
+        if (a.part_l[slot] > 0.f) M = fmaxf(M, a.part_m[slot]);
+    }
+    float L = 0.f;
+    float acc[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc[v] = 0.f;
+    for (int k = beg; k < end; ++k) {
+        const int64_t slot = (int64_t)a.merge_rows[k] * a.Hq + h;
+        const float l = a.part_l[slot];
+        const float w = l > 0.f ? fast_exp2(a.part_m[slot] - M) : 0.f;
+        L += w * l;
+        const float *po = a.part_o + slot * D + lane * V;
+        if (V == 2) {
+            const f32x2 x = *reinterpret_cast<const f32x2 *>(po);
+            acc[0] += w * x[0];
+            acc[V - 1] += w * x[1];
+        } else {
+            acc[0] += w * po[0];
+        }
+    }
+    const float inv = 1.0f / L;
+    uint16_t *ob = a.out + ((int64_t)r * a.Hq + h) * D + lane * V;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+        const __bf16 y = (__bf16)(acc[v] * inv);
+        ob[v] = __builtin_bit_cast(uint16_t, y);
+    }
+}
+
+__global__ __launch_bounds__(256) void fill_kernel(uint32_t *buf, size_t words, uint32_t value)
+{
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += stride)
+        buf[i] = value;
+}
+
+__global__ __launch_bounds__(256) void read_kernel(const u32x4 *buf, size_t n, uint32_t *sink)
+{
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    uint32_t x = 0;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const u32x4 v = buf[i];
+        x ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    __shared__ uint32_t red[256];
+    red[threadIdx.x] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t y = 0;
+        for (int i = 0; i < 256; ++i) y ^= red[i];
+        sink[blockIdx.x] = y;
+    }
+}
+
+__global__ __launch_bounds__(256) void copy_kernel(u32x4 *dst, const u32x4 *src, size_t n)
+{
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+        dst[i] = src[i];
+}
+
+}  // namespace
+
+int launch_decode(const DecodeArgs &a, int head_dim, void *stream)
+{
+    if (a.n_items <= 0) return 0;
+    const dim3 grid((a.n_items + kWavesPerBlock - 1) / kWavesPerBlock);
+    const dim3 block(kWaveSize * kWavesPerBlock);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (head_dim == 128)
+        hipLaunchKernelGGL(decode_kernel<128>, grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL(decode_kernel<64>, grid, block, 0, s, a);
+    return (int)hipGetLastError();
+}
+
+int launch_merge(const MergeArgs &a, int head_dim, void *stream)
+{
+    const int64_t waves = (int64_t)a.R * a.Hq;
+    if (waves <= 0) return 0;
+    const dim3 grid((unsigned)((waves + 3) / 4));
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (head_dim == 128)
+        hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(256), 0, s, a);
+    return (int)hipGetLastError();
+}
+
+static unsigned grid_for(size_t n)
+{
+    size_t g = (n + 255) / 256;
+    if (g > 8192) g = 8192;
+    if (g < 1) g = 1;
+    return (unsigned)g;
+}
+
+int launch_fill(void *buf, size_t words, uint32_t value, void *stream)
+{
+    hipLaunchKernelGGL(fill_kernel, dim3(grid_for(words)), dim3(256), 0,
+                       reinterpret_cast<hipStream_t>(stream), (uint32_t *)buf, words, value);
+    return (int)hipGetLastError();
+}
+
+int launch_read(const void *buf, size_t vec16, void *sink, void *stream)
+{
+    hipLaunchKernelGGL(read_kernel, dim3(grid_for(vec16)), dim3(256), 0,
+                       reinterpret_cast<hipStream_t>(stream), (const u32x4 *)buf, vec16,
+                       (uint32_t *)sink);
+    return (int)hipGetLastError();
+}
+
+int launch_copy(void *dst, const void *src, size_t vec16, void *stream)
+{
+    hipLaunchKernelGGL(copy_kernel, dim3(grid_for(vec16)), dim3(256), 0,
+                       reinterpret_cast<hipStream_t>(stream), (u32x4 *)dst, (const u32x4 *)src,
+                       vec16);
+    return (int)hipGetLastError();
+}
+
+const char *hip_error_string(int err)
+{
+    return hipGetErrorString((hipError_t)err);
+}
+
+}  // namespace cap

@@ -1,0 +1,102 @@
+"""Device-memory plumbing around the C ABI: holds torch tensors for the
+inputs, the page table, the plan, the partial workspace and the output, and
+calls the libcap entry points on the current torch stream.  PyTorch provides
+memory and streams only; all attention arithmetic happens in libcap."""
+from __future__ import annotations
+
+import numpy as np
+
+from . import cap
+
+
+def _dev_u16(torch, a: np.ndarray, device):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device)
+
+
+class TreeDecoder:
+    """One radix tree resident on the GPU, ready to plan and decode steps.
+
+    tree: a ``workloads.Tree`` (or any object with the same attributes);
+    q, k_pool, v_pool: uint16 bf16-bit arrays in the layouts of include/cap.h.
+    """
+
+    def __init__(self, tree, q, k_pool, v_pool, device="cuda", **plan_opts):
+        import torch
+        self.torch = torch
+        self.device = torch.device(device)
+        if self.device.type != "cuda" or not torch.cuda.is_available():
+            raise RuntimeError("TreeDecoder needs a GPU (ROCm) device")
+        self.tree_host = tree
+        self.R, self.Hq, self.D = int(tree.num_requests), int(tree.num_q_heads), int(tree.head_dim)
+        self.q = _dev_u16(torch, q, self.device)
+        self.k = _dev_u16(torch, k_pool, self.device)
+        self.v = _dev_u16(torch, v_pool, self.device)
+        self.out = torch.empty((self.R, self.Hq, self.D), dtype=torch.int16, device=self.device)
+        nbytes = cap.cap_tree_device_bytes(tree)
+        self.tree_buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        self.tree = cap.cap_tree_upload(tree, self.tree_buf.data_ptr(), nbytes, self.stream())
+        self.plan_h = 0
+        self.plan_buf = None
+        self.ws = None
+        self.stats = None
+        self.plan(**plan_opts)
+
+    def stream(self) -> int:
+        return self.torch.cuda.current_stream(self.device).cuda_stream
+
+    def plan(self, **opts):
+        torch = self.torch
+        if self.plan_h:
+            torch.cuda.current_stream(self.device).synchronize()
+            cap.cap_plan_free(self.plan_h)
+            self.plan_h = 0
+        self.plan_h = cap.cap_plan_step(self.tree, **opts)
+        self.stats = cap.cap_plan_get_stats(self.plan_h)
+        pb = int(self.stats["plan_device_bytes"])
+        wb = int(self.stats["workspace_bytes"])
+        if self.plan_buf is None or self.plan_buf.numel() < pb:
+            self.plan_buf = torch.empty(pb, dtype=torch.uint8, device=self.device)
+        if self.ws is None or self.ws.numel() * 4 < wb:
+            self.ws = torch.empty(max(wb // 4, 64), dtype=torch.float32, device=self.device)
+        cap.cap_plan_upload(self.plan_h, self.plan_buf.data_ptr(), self.plan_buf.numel(), self.stream())
+        return self.stats
+
+    def poison_workspace(self):
+        """Fill the partial workspace with NaN (tests: unwritten slots show up)."""
+        self.ws.fill_(float("nan"))
+
+    def decode(self):
+        cap.cap_decode_attention(self.plan_h, self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(),
+                                 self.ws.data_ptr(), self.ws.numel() * 4, self.stream())
+
+    def merge(self):
+        cap.cap_merge_partials(self.plan_h, self.ws.data_ptr(), self.ws.numel() * 4,
+                               self.out.data_ptr(), self.stream())
+
+    def step(self):
+        self.decode()
+        self.merge()
+
+    def output_bits(self) -> np.ndarray:
+        self.torch.cuda.current_stream(self.device).synchronize()
+        return self.out.cpu().numpy().view(np.uint16)
+
+    def output(self) -> np.ndarray:
+        b = self.output_bits().astype(np.uint32) << 16
+        return b.view(np.float32)
+
+    def close(self):
+        if self.plan_h or self.tree:
+            self.torch.cuda.synchronize(self.device)
+        if self.plan_h:
+            cap.cap_plan_free(self.plan_h)
+            self.plan_h = 0
+        if self.tree:
+            cap.cap_tree_free(self.tree)
+            self.tree = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

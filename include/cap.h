@@ -1,0 +1,224 @@
+/*
+ * cap.h -- C ABI of libcap: single-step decode attention over a paged
+ * radix-tree KV cache on AMD MI355X (gfx950), where every request under a
+ * tree node is served by one stream of that node's KV per step.
+ *
+ * Source of the operation: the Capillary Kernels project page (abstract,
+ * first paragraph) states the problem -- a radix-tree KV cache lets decode
+ * requests reuse common context prefixes, yet conventional attention kernels
+ * load each request's KV tiles independently, so shared prefixes are fetched
+ * again and again.  Its second paragraph gives the three ingredients this ABI
+ * exposes as separate calls: a per-decoding-step cost model that picks the
+ * query grouping (cap_plan_step), an attention kernel in which work that
+ * shares a KV prefix reads it once and emits partial attention results
+ * (cap_decode_attention), and the combination of those partial results
+ * (cap_merge_partials).  The page gives no formula; the attention computed
+ * is standard scaled-dot-product softmax attention of each request's one
+ * decode query over its whole root-to-leaf context (no mask, no bias).
+ *
+ * Conventions for every call:
+ *  - Plain C; no exceptions cross the boundary.  The return code is the only
+ *    error channel; cap_last_error() gives a human-readable message for the
+ *    last failure on the calling thread.
+ *  - A call that fails validation has no side effects (nothing launched,
+ *    nothing copied, no handle created).
+ *  - The library never allocates device memory and never synchronises the
+ *    device.  The caller owns every device buffer and passes raw device
+ *    pointers plus a stream (a hipStream_t; NULL = the null stream).  The
+ *    library owns only its host-side handles.
+ *  - Launch failures map to CAP_ERR_HIP; device faults surface at the
+ *    caller's next synchronisation.
+ *
+ * Data layouts (all bf16 values are IEEE bfloat16 bit patterns):
+ *  - Page size P = 16 tokens.  Every tree node starts on a fresh page and
+ *    owns ceil(tokens/16) pages; its last page may be partial.  Slots past a
+ *    node's last token are never read into the result (they may hold NaN).
+ *  - K pool: bf16 [num_pool_pages][Hkv][D/8][P][8].  Within one
+ *    (page, KV head) block, token slot t, dim d is at ((d/8)*P + t)*8 + d%8.
+ *  - V pool: bf16 [num_pool_pages][Hkv][D][P].  Within one block, (t, d) is
+ *    at d*P + t (tokens contiguous for each dim).
+ *  - q:   bf16 [R][Hq][D], request-major, in the tree's request order.
+ *  - out: bf16 [R][Hq][D], rounded to nearest-even from fp32.
+ *  - Query head h reads KV head h / (Hq/Hkv).
+ */
+#ifndef CAP_H
+#define CAP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CAP_ABI_VERSION 1
+
+typedef enum cap_status {
+    CAP_OK = 0,
+    CAP_ERR_INVALID_ARG = 1,   /* NULL pointer, bad option value, size overflow */
+    CAP_ERR_BAD_TREE = 2,      /* tree or request paths are malformed */
+    CAP_ERR_WORKSPACE = 3,     /* a caller buffer is smaller than required / misaligned */
+    CAP_ERR_UNSUPPORTED = 4,   /* shape outside the supported envelope */
+    CAP_ERR_HIP = 5,           /* a HIP runtime call or kernel launch failed */
+    CAP_ERR_STATE = 6          /* handle used in the wrong state (e.g. plan not uploaded) */
+} cap_status;
+
+/* A hipStream_t, passed through untouched. */
+typedef void *cap_stream_t;
+
+/* Attention shape.  Supported: head_dim in {64, 128}; page_size == 16;
+ * num_q_heads % num_kv_heads == 0 with G = num_q_heads / num_kv_heads in
+ * {1, 2, 4, 8, 16, 32}; sm_scale finite and > 0 (usually 1/sqrt(head_dim)). */
+typedef struct cap_attn_desc {
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t page_size;
+    float sm_scale;
+} cap_attn_desc;
+
+/* Paged radix tree and request paths.  All pointers are HOST pointers; the
+ * arrays are copied during cap_tree_upload and may be freed after it returns.
+ *  parent[N]          parent node id, -1 for a root; parent[i] < i.
+ *  num_tokens[N]      tokens held by node i (>= 0; 0 allowed, e.g. a sentinel root).
+ *  page_offsets[N+1]  CSR into page_ids; node i owns exactly ceil(num_tokens[i]/16)
+ *                     pages page_ids[page_offsets[i] .. page_offsets[i+1]).
+ *  page_ids[..]       physical page indices into the K/V pools, each in
+ *                     [0, num_pool_pages), no page owned twice.
+ *  path_offsets[R+1]  CSR into path_nodes; request r's path runs from a root
+ *                     down to the node where its context ends; consecutive
+ *                     entries are parent and child.  Every request must have
+ *                     at least one context token.  Several requests may share
+ *                     a path or end at an internal node. */
+typedef struct cap_tree_desc {
+    int32_t num_nodes;
+    const int32_t *parent;
+    const int32_t *num_tokens;
+    const int64_t *page_offsets;
+    const int32_t *page_ids;
+    int32_t num_requests;
+    const int32_t *path_offsets;
+    const int32_t *path_nodes;
+    int64_t num_pool_pages;
+} cap_tree_desc;
+
+/* Planner options.  Zero-initialise for defaults (then set what you need);
+ * cap_plan_opts_default() fills the defaults explicitly. */
+typedef struct cap_plan_opts {
+    int32_t share_mode;       /* -1 auto (cost model), 0 fold all (unshared baseline:
+                                 every request streams its whole context), 1 share
+                                 every non-empty node, 2 auto (same as -1) */
+    int32_t split_pages;      /* 0 auto; else the most KV pages one work item streams */
+    int32_t max_rows;         /* 0 auto (32); query rows per work item: 16 or 32 */
+    int32_t num_cus;          /* 0 = 256 (MI355X); used by the cost model */
+    int32_t waves_per_cu;     /* 0 = 4; resident work items per CU in the cost model */
+    float rounds;             /* 0 = 2.0; target work-item rounds per resident slot */
+    float share_margin;       /* 0 = 1.0; share a node only if saved bytes exceed
+                                 margin x added partial bytes */
+    int32_t reserved[4];
+} cap_plan_opts;
+
+/* Plan summary (host-side numbers; bytes are per decode step). */
+typedef struct cap_plan_stats {
+    int64_t num_items;            /* work items (one wavefront each) */
+    int64_t num_tasks;            /* (page run, request group) pairs; items = tasks x Hkv */
+    int64_t num_groups;           /* request groups after share/fold decisions */
+    int64_t partial_rows;         /* partial slots = partial_rows x Hq */
+    int64_t workspace_bytes;      /* required partial workspace */
+    int64_t plan_device_bytes;    /* required plan device buffer */
+    int64_t tree_device_bytes;    /* device page table size */
+    int64_t kv_bytes_streamed;    /* K+V bytes the items read (pages x row groups x heads) */
+    int64_t kv_bytes_unique;      /* K+V bytes of the tree's tokens (each once) */
+    int64_t kv_bytes_unshared;    /* K+V bytes if every request read its own context */
+    int64_t partial_bytes;        /* partial bytes written (= read by the merge) */
+    int32_t max_partials_per_request;
+    int32_t max_pages_per_item;
+    double plan_host_us;          /* host time spent in cap_plan_step */
+} cap_plan_stats;
+
+typedef struct cap_tree cap_tree;   /* opaque host handles */
+typedef struct cap_plan cap_plan;
+
+/* Work item as stored in the plan (exposed for inspection and tests). */
+typedef struct cap_work_item {
+    int32_t stream_off;   /* first entry of its page run in the plan's page stream */
+    int32_t npages;       /* pages in the run (>= 1) */
+    int32_t head;         /* KV head */
+    int32_t row_off;      /* first entry of its request list in the plan's row table */
+    int32_t nreq;         /* requests served; query rows = nreq x G */
+    int32_t slot_base;    /* partial row of its first request */
+} cap_work_item;
+
+/* Read-only host view of a plan (pointers valid until cap_plan_free).
+ * Page-stream entry e: tree page index = e >> 5, valid tokens = (e & 31) + 1.
+ * Partial slot of item row i (request position i/G, query head head*G + i%G):
+ *   (slot_base + i/G) * Hq + head*G + i%G.
+ * Request r's partial rows: merge_rows[merge_off[r] .. merge_off[r+1]). */
+typedef struct cap_plan_view {
+    int32_t num_items;         const cap_work_item *items;
+    int32_t stream_len;        const int32_t *stream;
+    int32_t rows_len;          const int32_t *rows;
+    int32_t num_requests;      const int32_t *merge_off;  const int32_t *merge_rows;
+} cap_plan_view;
+
+int32_t cap_abi_version(void);
+const char *cap_last_error(void);
+void cap_plan_opts_default(cap_plan_opts *opts);
+
+/* Bytes of device memory the tree's page table needs (4 x total pages, >= 256). */
+cap_status cap_tree_device_bytes(const cap_attn_desc *attn, const cap_tree_desc *tree,
+                                 size_t *bytes);
+
+/* Validate the tree, derive node->requests lists and context lengths, and copy
+ * the page table into dev_buf (>= cap_tree_device_bytes, 16-byte aligned) with
+ * one asynchronous host-to-device copy on `stream`.  dev_buf may be NULL: the
+ * tree is then validated and can be planned, but not used for decoding.
+ * The host arrays may be freed on return.  On success *out owns a handle the
+ * caller releases with cap_tree_free (after the stream has passed the copy).
+ * Errors: CAP_ERR_INVALID_ARG (NULL desc/out), CAP_ERR_UNSUPPORTED (shape),
+ * CAP_ERR_BAD_TREE (parents, page counts, page ids, paths, empty requests),
+ * CAP_ERR_WORKSPACE (dev_bytes too small), CAP_ERR_HIP (copy failed). */
+cap_status cap_tree_upload(const cap_attn_desc *attn, const cap_tree_desc *tree,
+                           void *dev_buf, size_t dev_bytes, cap_stream_t stream,
+                           cap_tree **out);
+void cap_tree_free(cap_tree *tree);
+
+/* Per-step planner (host only, no device calls): share/fold decisions per
+ * node, KV split lengths, request groups, work-item order, partial slots and
+ * the per-request merge lists.  opts may be NULL (defaults).  The plan refers
+ * to `tree`, which must outlive it.  Errors: CAP_ERR_INVALID_ARG. */
+cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts, cap_plan **out);
+cap_status cap_plan_get_stats(const cap_plan *plan, cap_plan_stats *stats);
+cap_status cap_plan_get_view(const cap_plan *plan, cap_plan_view *view);
+
+/* Copy the plan into dev_buf (>= stats.plan_device_bytes, 256-byte aligned)
+ * with one asynchronous host-to-device copy.  The plan keeps the host copy
+ * alive; free the plan only after the stream has passed this copy.
+ * Errors: CAP_ERR_INVALID_ARG, CAP_ERR_WORKSPACE, CAP_ERR_STATE (tree has no
+ * device page table), CAP_ERR_HIP. */
+cap_status cap_plan_upload(cap_plan *plan, void *dev_buf, size_t bytes, cap_stream_t stream);
+
+/* Launch the decode kernel: every work item streams its KV pages once for
+ * all its query rows and writes (m, l, o) partials -- m the running maximum
+ * of the base-2-scaled logits, l the sum of exponentials, o the unnormalised
+ * weighted sum of V, fp32 -- into `workspace`
+ * (>= stats.workspace_bytes, 256-byte aligned).  q, k_pool, v_pool: device
+ * pointers in the layouts above, 16-byte aligned.  Errors:
+ * CAP_ERR_INVALID_ARG, CAP_ERR_WORKSPACE, CAP_ERR_STATE (plan not uploaded),
+ * CAP_ERR_HIP. */
+cap_status cap_decode_attention(const cap_plan *plan, const void *q, const void *k_pool,
+                                const void *v_pool, void *workspace, size_t ws_bytes,
+                                cap_stream_t stream);
+
+/* Launch the merge kernel: for each (request, query head) combine its
+ * partials with log-sum-exp rescaling and write bf16 `out`.  Must follow
+ * cap_decode_attention on the same stream with the same workspace.
+ * Errors: as cap_decode_attention. */
+cap_status cap_merge_partials(const cap_plan *plan, const void *workspace, size_t ws_bytes,
+                              void *out, cap_stream_t stream);
+void cap_plan_free(cap_plan *plan);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CAP_H */

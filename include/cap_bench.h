@@ -1,0 +1,40 @@
+/*
+ * cap_bench.h -- measurement helpers exported by libcap (not part of the
+ * attention path).  They exist so that timings of the attention kernels can
+ * be taken with inputs resident in HBM rather than in on-chip caches, and so
+ * that HBM-traffic counters can be calibrated against kernels of known size.
+ * The CREDIT summary (section III.D, "Baseline Timing") warns that cache
+ * residency makes peak-bandwidth assumptions unreliable; these helpers make
+ * that effect controllable.
+ *
+ * All pointers are device pointers owned by the caller; sizes are bytes and
+ * must be multiples of 16 with 16-byte aligned buffers.  Each call launches
+ * one kernel on `stream` (a hipStream_t) and returns CAP_ERR_INVALID_ARG for
+ * bad sizes/pointers or CAP_ERR_HIP if the launch fails.
+ */
+#ifndef CAP_BENCH_H
+#define CAP_BENCH_H
+
+#include "cap.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Write `value` to every 32-bit word of buf (evicts caches when buf is larger
+ * than L2 + the 256 MB Infinity Cache). */
+cap_status cap_bench_fill(void *buf, size_t bytes, uint32_t value, cap_stream_t stream);
+
+/* Read every byte of buf once (128-bit loads, grid-stride) and write one
+ * 32-bit word per workgroup into sink (>= 4 x 8192 bytes) so the reads are not
+ * dead.  Its time gives the achievable HBM read rate. */
+cap_status cap_bench_read(const void *buf, size_t bytes, void *sink, cap_stream_t stream);
+
+/* Plain copy of `bytes` from src to dst: reads and writes a known byte count,
+ * for scaling FETCH_SIZE / WRITE_SIZE counters. */
+cap_status cap_bench_copy(void *dst, const void *src, size_t bytes, cap_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CAP_BENCH_H */

@@ -1,0 +1,195 @@
+"""Host-side tests of the C ABI (no GPU): exported symbols, tree validation,
+and the planner's coverage property.  Trees are uploaded with dev_buf = NULL,
+which validates and plans without touching a device."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from decode_attention_prefix_amd import cap
+from decode_attention_prefix_amd import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in ("cap.h", "cap_bench.h"):
+        src = open(os.path.join(ROOT, "include", h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(cap_[a-z0-9_]+)\s*\(",
+                             src, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    L = cap.lib()
+    names = declared_functions()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(L, n), f"libcap.so does not export {n}"
+    assert set(cap.EXPORTED) == names
+    assert cap.cap_abi_version() == 1
+
+
+def small_tree(**over):
+    rng = np.random.default_rng(0)
+    nt, par, paths = [40, 17, 33, 5], [-1, 0, 0, 2], [[0, 1], [0, 2, 3], [0, 2]]
+    t = wl.tree_from_lengths(nt, par, paths, 8, 2, 64, page_perm_rng=rng)
+    for k, v in over.items():
+        setattr(t, k, v)
+    return t
+
+
+def expect(code, tree):
+    with pytest.raises(cap.CapError) as e:
+        cap.cap_tree_upload(tree)
+    assert e.value.status == code, str(e.value)
+
+
+def test_valid_tree_uploads_host_only():
+    h = cap.cap_tree_upload(small_tree())
+    assert h
+    cap.cap_tree_free(h)
+
+
+def test_tree_validation_errors():
+    BAD, UNS, ARG = 2, 4, 1
+    t = small_tree()
+    expect(BAD, small_tree(parent=np.array([-1, 0, 3, 2], np.int32)))          # parent after child
+    expect(BAD, small_tree(parent=np.array([-1, 1, 0, 2], np.int32)))          # self parent
+    expect(BAD, small_tree(num_tokens=np.array([40, 17, 33, 17], np.int32)))   # page count mismatch
+    ids = t.page_ids.copy(); ids[0] = t.num_pool_pages
+    expect(BAD, small_tree(page_ids=ids))                                      # page outside pool
+    ids = t.page_ids.copy(); ids[1] = ids[0]
+    expect(BAD, small_tree(page_ids=ids))                                      # page owned twice
+    expect(BAD, small_tree(path_nodes=np.array([0, 1, 0, 3, 0, 2], np.int32)))  # skips a node
+    expect(BAD, small_tree(path_nodes=np.array([1, 1, 0, 2, 3, 0], np.int32)))  # starts below a root
+    # a request with no context tokens
+    z = wl.tree_from_lengths([0, 0], [-1, 0], [[0, 1]], 8, 2, 64)
+    expect(BAD, z)
+    expect(UNS, small_tree(num_q_heads=6, num_kv_heads=4))                     # Hq % Hkv
+    expect(UNS, small_tree(head_dim=96))
+    expect(UNS, small_tree(page_size=32))
+    expect(UNS, small_tree(num_q_heads=128, num_kv_heads=2))                   # G = 64
+    expect(ARG, small_tree(sm_scale=float("nan")))
+
+
+def test_planner_rejects_bad_options():
+    h = cap.cap_tree_upload(small_tree())
+    try:
+        for kw in ({"share_mode": 5}, {"max_rows": 24}, {"split_pages": -1}, {"rounds": -1.0}):
+            with pytest.raises(cap.CapError) as e:
+                cap.cap_plan_step(h, **kw)
+            assert e.value.status == 1
+    finally:
+        cap.cap_tree_free(h)
+
+
+def test_plan_upload_needs_device_tree():
+    h = cap.cap_tree_upload(small_tree())
+    p = cap.cap_plan_step(h)
+    try:
+        with pytest.raises(cap.CapError) as e:
+            cap.cap_plan_upload(p, 1 << 20, 1 << 20)
+        assert e.value.status == 6
+        with pytest.raises(cap.CapError) as e:
+            cap.cap_decode_attention(p, 256, 256, 256, 256, 1 << 20)
+        assert e.value.status == 6
+    finally:
+        cap.cap_plan_free(p)
+        cap.cap_tree_free(h)
+
+
+def check_coverage(tree, plan_handle, max_rows=32):
+    """Every (request, KV head) sees exactly its context tokens once; every
+    partial slot is written by exactly one item row; merge lists match."""
+    v = cap.cap_plan_get_view(plan_handle)
+    st = cap.cap_plan_get_stats(plan_handle)
+    Hq, Hkv = tree.num_q_heads, tree.num_kv_heads
+    G = Hq // Hkv
+    R = tree.num_requests
+    # expected: per request, multiset of (tree page index, valid tokens)
+    want = {}
+    for r in range(R):
+        s = []
+        for n in tree.path(r):
+            for p in range(int(tree.page_offsets[n]), int(tree.page_offsets[n + 1])):
+                nt = min(16, int(tree.num_tokens[n]) - 16 * (p - int(tree.page_offsets[n])))
+                s.append((p, nt))
+        want[r] = sorted(s)
+    got = {(r, h): [] for r in range(R) for h in range(Hkv)}
+    slot_writes = np.zeros(int(st["partial_rows"]) * Hq, np.int64)
+    slot_rows_of = {r: set() for r in range(R)}
+    for so, npg, head, ro, nreq, sb in v["items"]:
+        assert npg >= 1 and 0 <= head < Hkv and 1 <= nreq and nreq * G <= max_rows
+        ents = v["stream"][so:so + npg]
+        pages = [(int(e) >> 5, (int(e) & 31) + 1) for e in ents]
+        for qpos, r in enumerate(v["rows"][ro:ro + nreq]):
+            got[(int(r), int(head))].extend(pages)
+            for i in range(G):
+                slot_writes[(sb + qpos) * Hq + head * G + i] += 1
+            slot_rows_of[int(r)].add(int(sb + qpos))
+    for (r, h), s in got.items():
+        assert sorted(s) == want[r], f"request {r} head {h}"
+    assert np.all(slot_writes == 1)
+    for r in range(R):
+        ml = v["merge_rows"][v["merge_off"][r]:v["merge_off"][r + 1]]
+        assert len(set(ml.tolist())) == len(ml)
+        assert set(ml.tolist()) == slot_rows_of[r]
+    assert st["num_items"] == len(v["items"])
+    return st
+
+
+@pytest.mark.parametrize("share_mode", [-1, 0, 1])
+@pytest.mark.parametrize("split_pages", [0, 1, 3, 64])
+def test_planner_coverage_random_trees(share_mode, split_pages):
+    for seed in range(8):
+        rng = np.random.default_rng(seed)
+        Hq, Hkv = [(8, 2), (32, 8), (16, 1), (4, 4)][seed % 4]
+        nt, par, paths = wl.make_random_tree(rng, num_requests=int(rng.integers(1, 20)), max_depth=4,
+                                             max_len=90, num_q_heads=Hq, num_kv_heads=Hkv,
+                                             head_dim=64, internal_end_prob=0.3,
+                                             empty_root=bool(seed % 2), min_len=0)
+        t = wl.tree_from_lengths(nt, par, paths, Hq, Hkv, 64, page_perm_rng=rng)
+        h = cap.cap_tree_upload(t)
+        try:
+            for max_rows in (16, 32):
+                if Hq // Hkv > max_rows:
+                    continue
+                p = cap.cap_plan_step(h, share_mode=share_mode, split_pages=split_pages,
+                                      max_rows=max_rows)
+                try:
+                    check_coverage(t, p, max_rows)
+                finally:
+                    cap.cap_plan_free(p)
+        finally:
+            cap.cap_tree_free(h)
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_planner_coverage_configs(cfg):
+    rng = np.random.default_rng([0, cfg])
+    nt, par, paths, Hq, Hkv, D = wl._config_shape(cfg, rng)
+    t = wl.tree_from_lengths(nt, par, paths, Hq, Hkv, D, page_perm_rng=rng)
+    h = cap.cap_tree_upload(t)
+    try:
+        for mode in (-1, 0, 1):
+            p = cap.cap_plan_step(h, share_mode=mode)
+            try:
+                st = check_coverage(t, p)
+                stats = wl.tree_stats(t)
+                assert st["kv_bytes_unique"] == stats["unique_kv_bytes"]
+                assert st["kv_bytes_unshared"] == stats["unshared_kv_bytes"]
+                if mode == 0 and cfg != 4:
+                    assert st["kv_bytes_streamed"] >= stats["unshared_kv_bytes"]
+                if mode == 1:
+                    # every node streamed once per request subgroup
+                    assert st["kv_bytes_streamed"] >= stats["unique_kv_bytes"]
+            finally:
+                cap.cap_plan_free(p)
+    finally:
+        cap.cap_tree_free(h)

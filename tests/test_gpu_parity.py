@@ -1,0 +1,126 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Bar: |gpu - oracle| <= 4e-3 + 4e-3 * |oracle| for every output element, no
+NaN/Inf.  Pool tails and unused pool pages hold NaN and the partial workspace
+is NaN-poisoned before every run, so an unmasked read or an unwritten slot
+fails the test.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from decode_attention_prefix_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 4e-3
+RTOL = 4e-3
+
+
+def _torch():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def run_gpu(w, **opts):
+    _torch()
+    from decode_attention_prefix_amd.decoder import TreeDecoder
+    dec = TreeDecoder(w.tree, w.q, w.k_pool, w.v_pool, **opts)
+    try:
+        dec.poison_workspace()
+        dec.step()
+        return dec.output(), dec.output_bits(), dec.stats
+    finally:
+        dec.close()
+
+
+def check(out, ref, what=""):
+    assert out.shape == ref.shape
+    assert np.all(np.isfinite(out)), f"{what}: non-finite output"
+    err = np.abs(out.astype(np.float64) - ref)
+    bound = ATOL + RTOL * np.abs(ref)
+    viol = err - bound
+    worst = np.unravel_index(int(np.argmax(viol)), viol.shape)
+    assert np.all(err <= bound), (f"{what}: max violation {viol.max():.3e} at {worst}, "
+                                  f"gpu {out[worst]:.6f} ref {ref[worst]:.6f}")
+    return float(err.max())
+
+
+_ORACLE_CACHE = {}
+
+
+def config_case(cfg):
+    if cfg not in _ORACLE_CACHE:
+        w = wl.make_config(cfg, keep_tokens=(cfg == 4))
+        ref = oracle.decode(w.tree, w.q, w.k_pool, w.v_pool)
+        _ORACLE_CACHE.clear()
+        _ORACLE_CACHE[cfg] = (w, ref)
+    return _ORACLE_CACHE[cfg]
+
+
+def test_config0_all_plan_variants():
+    w, ref = config_case(0)
+    for mode in (-1, 0, 1):
+        for split in (0, 1, 3, 100):
+            for rows in (16, 32):
+                out, _, _ = run_gpu(w, share_mode=mode, split_pages=split, max_rows=rows)
+                check(out, ref, f"cfg0 mode={mode} split={split} rows={rows}")
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_full_configs(cfg):
+    w, ref = config_case(cfg)
+    print(f"config {cfg}: {wl.tree_stats(w.tree)}", flush=True)
+    out, _, st = run_gpu(w)
+    e = check(out, ref, f"cfg{cfg} auto")
+    print(f"config {cfg}: max abs err {e:.3e}; plan {st}", flush=True)
+    if cfg == 4:
+        ctl = wl.control_workload(w)
+        out_c, _, _ = run_gpu(ctl)
+        check(out_c, ref, "cfg4 control batch")
+
+
+@pytest.mark.parametrize("cfg,mode", [(1, 0), (1, 1), (2, 1), (3, 1)])
+def test_full_configs_forced_modes(cfg, mode):
+    w, ref = config_case(cfg)
+    out, _, _ = run_gpu(w, share_mode=mode)
+    check(out, ref, f"cfg{cfg} mode={mode}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("HqHkv", [(8, 8), (8, 2), (32, 8), (16, 2), (32, 1)])
+def test_random_small_trees(D, HqHkv):
+    Hq, Hkv = HqHkv
+    for seed in range(4):
+        rng = np.random.default_rng([seed, D, Hq, Hkv])
+        nt, par, paths = wl.make_random_tree(rng, num_requests=int(rng.integers(1, 24)), max_depth=4,
+                                             max_len=100, num_q_heads=Hq, num_kv_heads=Hkv,
+                                             head_dim=D, internal_end_prob=0.3,
+                                             empty_root=bool(seed % 2), min_len=0)
+        w = wl.make_workload(nt, par, paths, Hq, Hkv, D, rng, extra_pool_pages=5)
+        ref = oracle.decode(w.tree, w.q, w.k_pool, w.v_pool)
+        for opts in ({}, {"share_mode": 1, "split_pages": 1}, {"share_mode": 0},
+                     {"split_pages": 2, "max_rows": 16 if Hq // Hkv <= 16 else 32}):
+            out, _, _ = run_gpu(w, **opts)
+            check(out, ref, f"seed={seed} D={D} Hq={Hq} Hkv={Hkv} {opts}")
+
+
+def test_large_logits_and_single_token_requests():
+    """Stretched logits (softmax close to one-hot) and 1-token contexts."""
+    rng = np.random.default_rng(77)
+    nt, par, paths = [1, 300, 1, 17], [-1, -1, 1, 1], [[0], [1], [1, 2], [1, 3], [0]]
+    q = rng.standard_normal((5, 16, 128)).astype(np.float32) * 4
+    w = wl.make_workload(nt, par, paths, 16, 4, 128, rng, q_values=q)
+    ref = oracle.decode(w.tree, w.q, w.k_pool, w.v_pool)
+    for opts in ({}, {"share_mode": 1, "split_pages": 1}):
+        out, _, _ = run_gpu(w, **opts)
+        check(out, ref, f"stretched {opts}")
+
+
+def test_bitwise_deterministic():
+    w, _ = config_case(0)
+    _, b1, _ = run_gpu(w, split_pages=2)
+    _, b2, _ = run_gpu(w, split_pages=2)
+    assert np.array_equal(b1, b2)
