@@ -78,6 +78,8 @@ def main():
     ap.add_argument("--rounds", type=float, default=0.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--read-probe-mb", type=int, default=2048)
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="also run one plain copy of this size (calibrates HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -237,6 +239,15 @@ def main():
             "sample": f"whole workload ({w.tree.num_requests} requests), one run, {t_or:.2f} s",
             "cpu": cpu_model(),
         }
+    if args.copy_probe_mb > 0:
+        nb = args.copy_probe_mb << 20
+        src = torch.empty(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty(nb, dtype=torch.uint8, device=dev)
+        cap.cap_bench_fill(src.data_ptr(), nb, 1, sp)
+        cap.cap_bench_fill(flush.data_ptr(), flush.numel(), 0, sp)
+        cap.cap_bench_copy(dst.data_ptr(), src.data_ptr(), nb, sp)
+        torch.cuda.synchronize(dev)
+        result["copy_probe_bytes"] = nb
     dec.close()
     print(json.dumps(result), flush=True)
 

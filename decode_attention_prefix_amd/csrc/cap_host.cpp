@@ -298,11 +298,12 @@ struct Planner {
                 W += (int64_t)g.entries.size() * rg * Hkv;
             }
             if (o.split_pages > 0) {
-                target_pages = o.split_pages;
+                target_pages = std::min(o.split_pages, cap::kMaxPagesPerItem);
                 break;
             }
             const double slots = (double)o.num_cus * o.waves_per_cu * o.rounds;
             target_pages = (int)std::max<int64_t>(4, (int64_t)std::ceil((double)W / slots));
+            target_pages = std::min(target_pages, cap::kMaxPagesPerItem);
         }
     }
 };

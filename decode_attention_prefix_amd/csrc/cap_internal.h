@@ -13,6 +13,7 @@ constexpr int kPage = 16;            // tokens per page
 constexpr int kWaveSize = 64;        // CDNA wavefront
 constexpr int kWavesPerBlock = 4;    // waves per workgroup in the decode kernel
 constexpr int kRowsPerItem = 32;     // query rows one wave can hold (two 16-row MFMA blocks)
+constexpr int kMaxPagesPerItem = 64; // a wave keeps its item's page table one page per lane
 
 // One wave's work: a run of KV pages of one KV head applied to up to 32
 // query rows (nreq requests x G query heads).  Same layout as cap_work_item.

@@ -70,37 +70,39 @@ struct Step {
     int nt0, nt1;                   // valid tokens in page 0 / page 1 (nt1 = 0: no page)
 };
 
+// Issue the loads of one 2-page step.  The page table of the item is held in
+// lanes (lane i: physical page and valid tokens of page i), so a step's page
+// ids come from v_readlane without a scalar-memory round trip.  Every call
+// issues the same number of loads whatever the step (a missing second page
+// re-reads the first; steps past the end re-read the last), so the wait
+// counts of the software pipeline stay exact.
 template <int D>
-__device__ __forceinline__ void load_step(Step<D> &f, const DecodeArgs &a, const WorkItem &it,
-                                          int s, int n, int c)
+__device__ __forceinline__ void load_step(Step<D> &f, const DecodeArgs &a, int head, int npages,
+                                          int s, int lane_pid, int lane_nt, int n, int c)
 {
     const int64_t blk = (int64_t)kPage * D;             // elements per (page, head)
-    const int e0 = a.stream[it.stream_off + 2 * s];
-    const bool has1 = 2 * s + 1 < it.npages;
-    const int64_t p0 = a.tree_pages[e0 >> 5];
-    f.nt0 = (e0 & 31) + 1;
-    const uint16_t *kb = a.k_pool + (p0 * a.Hkv + it.head) * blk;
-    const uint16_t *vb = a.v_pool + (p0 * a.Hkv + it.head) * blk;
+    const int nsteps = (npages + 1) >> 1;
+    const int ss = s < nsteps ? s : nsteps - 1;
+    const int i0 = 2 * ss;
+    const bool has1 = i0 + 1 < npages;
+    const int i1 = has1 ? i0 + 1 : i0;
+    const int64_t p0 = __builtin_amdgcn_readlane(lane_pid, i0);
+    const int64_t p1 = __builtin_amdgcn_readlane(lane_pid, i1);
+    f.nt0 = __builtin_amdgcn_readlane(lane_nt, i0);
+    f.nt1 = has1 ? __builtin_amdgcn_readlane(lane_nt, i1) : 0;
+    const uint16_t *kb0 = a.k_pool + (p0 * a.Hkv + head) * blk;
+    const uint16_t *vb0 = a.v_pool + (p0 * a.Hkv + head) * blk;
+    const uint16_t *kb1 = a.k_pool + (p1 * a.Hkv + head) * blk;
+    const uint16_t *vb1 = a.v_pool + (p1 * a.Hkv + head) * blk;
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) f.k0[i] = ld16(kb + ((4 * i + c) * kPage + n) * 8);
+    for (int i = 0; i < D / 32; ++i) {
+        f.k0[i] = ld16(kb0 + ((4 * i + c) * kPage + n) * 8);
+        f.k1[i] = ld16(kb1 + ((4 * i + c) * kPage + n) * 8);
+    }
 #pragma unroll
-    for (int j = 0; j < D / 16; ++j) f.v0[j] = ld8(vb + (16 * j + n) * kPage + 4 * c);
-    if (has1) {
-        const int e1 = a.stream[it.stream_off + 2 * s + 1];
-        const int64_t p1 = a.tree_pages[e1 >> 5];
-        f.nt1 = (e1 & 31) + 1;
-        const uint16_t *kb1 = a.k_pool + (p1 * a.Hkv + it.head) * blk;
-        const uint16_t *vb1 = a.v_pool + (p1 * a.Hkv + it.head) * blk;
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i) f.k1[i] = ld16(kb1 + ((4 * i + c) * kPage + n) * 8);
-#pragma unroll
-        for (int j = 0; j < D / 16; ++j) f.v1[j] = ld8(vb1 + (16 * j + n) * kPage + 4 * c);
-    } else {
-        f.nt1 = 0;
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i) f.k1[i] = u32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int j = 0; j < D / 16; ++j) f.v1[j] = u32x2{0, 0};
+    for (int j = 0; j < D / 16; ++j) {
+        f.v0[j] = ld8(vb0 + (16 * j + n) * kPage + 4 * c);
+        f.v1[j] = ld8(vb1 + (16 * j + n) * kPage + 4 * c);
     }
 }
 
@@ -220,16 +222,28 @@ __global__ __launch_bounds__(kWaveSize * kWavesPerBlock) void decode_kernel(Deco
     float m_run[2] = {-INFINITY, -INFINITY};
     float l_run[2] = {0.f, 0.f};
 
-    // Two register buffers: the loads of step s+1 are in flight while step s computes.
+    // Page table of the item, one page per lane (items hold at most 64 pages).
+    int lane_pid = 0, lane_nt = 0;
+    if (lane < it.npages) {
+        const int e = a.stream[it.stream_off + lane];
+        lane_pid = a.tree_pages[e >> 5];
+        lane_nt = (e & 31) + 1;
+    }
+
+    // Three register buffers: two steps are in flight while one computes.
     const int nsteps = (it.npages + 1) >> 1;
-    Step<D> fa, fb;
-    load_step<D>(fa, a, it, 0, n, c);
-    for (int s = 0; s < nsteps; s += 2) {
-        if (s + 1 < nsteps) load_step<D>(fb, a, it, s + 1, n, c);
+    Step<D> fa, fb, fc;
+    load_step<D>(fa, a, it.head, it.npages, 0, lane_pid, lane_nt, n, c);
+    load_step<D>(fb, a, it.head, it.npages, 1, lane_pid, lane_nt, n, c);
+    for (int s = 0; s < nsteps; s += 3) {
+        load_step<D>(fc, a, it.head, it.npages, s + 2, lane_pid, lane_nt, n, c);
         compute_step<D>(fa, qf, o, m_run, l_run, two, a.scale_log2, c);
         if (s + 1 >= nsteps) break;
-        if (s + 2 < nsteps) load_step<D>(fa, a, it, s + 2, n, c);
+        load_step<D>(fa, a, it.head, it.npages, s + 3, lane_pid, lane_nt, n, c);
         compute_step<D>(fb, qf, o, m_run, l_run, two, a.scale_log2, c);
+        if (s + 2 >= nsteps) break;
+        load_step<D>(fb, a, it.head, it.npages, s + 4, lane_pid, lane_nt, n, c);
+        compute_step<D>(fc, qf, o, m_run, l_run, two, a.scale_log2, c);
     }
 
     // Partials: slot = (slot_base + row / G) * Hq + head * G + row % G.
@@ -254,36 +268,76 @@ __global__ __launch_bounds__(kWaveSize * kWavesPerBlock) void decode_kernel(Deco
 }
 
 // One wave per (request, query head): out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i.
+// The (m, l) pairs of up to 64 partials are loaded one per lane, M and the
+// weights come from wave reductions, and the o rows (D floats each) are
+// accumulated with eight row loads in flight.  More than 64 partials are
+// taken in blocks of 64 with the running result rescaled between blocks.
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int k = 32; k >= 1; k >>= 1) v = fmaxf(v, __shfl_xor(v, k));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int k = 32; k >= 1; k >>= 1) v += __shfl_xor(v, k);
+    return v;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a)
 {
-    constexpr int V = D / 64;   // values per lane
+    constexpr int V = D / 64;   // o values per lane
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
     if (wid >= a.R * a.Hq) return;
     const int r = wid / a.Hq, h = wid % a.Hq;
     const int beg = a.merge_off[r], end = a.merge_off[r + 1];
-    float M = -INFINITY;
-    for (int k = beg; k < end; ++k) {
-        const int64_t slot = (int64_t)a.merge_rows[k] * a.Hq + h;
-        if (a.part_l[slot] > 0.f) M = fmaxf(M, a.part_m[slot]);
-    }
-    float L = 0.f;
+    float M = -INFINITY, L = 0.f;
     float acc[V];
 #pragma unroll
     for (int v = 0; v < V; ++v) acc[v] = 0.f;
-    for (int k = beg; k < end; ++k) {
-        const int64_t slot = (int64_t)a.merge_rows[k] * a.Hq + h;
-        const float l = a.part_l[slot];
-        const float w = l > 0.f ? fast_exp2(a.part_m[slot] - M) : 0.f;
-        L += w * l;
-        const float *po = a.part_o + slot * D + lane * V;
-        if (V == 2) {
-            const f32x2 x = *reinterpret_cast<const f32x2 *>(po);
-            acc[0] += w * x[0];
-            acc[V - 1] += w * x[1];
-        } else {
-            acc[0] += w * po[0];
+    for (int kb = beg; kb < end; kb += 64) {
+        const int cnt = min(64, end - kb);
+        int slot = 0;
+        float m = -INFINITY, l = 0.f;
+        if (lane < cnt) {
+            slot = a.merge_rows[kb + lane] * a.Hq + h;
+            l = a.part_l[slot];
+            m = l > 0.f ? a.part_m[slot] : -INFINITY;
+        }
+        const float M_new = fmaxf(M, wave_max(m));
+        const float w = (l > 0.f) ? fast_exp2(m - M_new) : 0.f;
+        const float rescale = fast_exp2(M - M_new);   // 0 on the first block
+        L = L * rescale + wave_sum(w * l);
+#pragma unroll
+        for (int v = 0; v < V; ++v) acc[v] *= rescale;
+        M = M_new;
+        for (int k0 = 0; k0 < cnt; k0 += 8) {
+            float x[8][V];
+            float wk[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int k = min(k0 + u, cnt - 1);
+                const int64_t sl = __builtin_amdgcn_readlane(slot, k);
+                const float wu = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
+                wk[u] = (k0 + u < cnt) ? wu : 0.f;
+                const float *po = a.part_o + sl * D + lane * V;
+                if (V == 2) {
+                    const f32x2 y = *reinterpret_cast<const f32x2 *>(po);
+                    x[u][0] = y[0];
+                    x[u][V - 1] = y[1];
+                } else {
+                    x[u][0] = po[0];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int v = 0; v < V; ++v) acc[v] += wk[u] * x[u][v];
         }
     }
     const float inv = 1.0f / L;

@@ -108,7 +108,8 @@ typedef struct cap_plan_opts {
     int32_t share_mode;       /* -1 auto (cost model), 0 fold all (unshared baseline:
                                  every request streams its whole context), 1 share
                                  every non-empty node, 2 auto (same as -1) */
-    int32_t split_pages;      /* 0 auto; else the most KV pages one work item streams */
+    int32_t split_pages;      /* 0 auto; else the most KV pages one work item streams
+                                 (values above 64 are treated as 64) */
     int32_t max_rows;         /* 0 auto (32); query rows per work item: 16 or 32 */
     int32_t num_cus;          /* 0 = 256 (MI355X); used by the cost model */
     int32_t waves_per_cu;     /* 0 = 4; resident work items per CU in the cost model */

@@ -125,7 +125,7 @@ def check_coverage(tree, plan_handle, max_rows=32):
     slot_writes = np.zeros(int(st["partial_rows"]) * Hq, np.int64)
     slot_rows_of = {r: set() for r in range(R)}
     for so, npg, head, ro, nreq, sb in v["items"]:
-        assert npg >= 1 and 0 <= head < Hkv and 1 <= nreq and nreq * G <= max_rows
+        assert 1 <= npg <= 64 and 0 <= head < Hkv and 1 <= nreq and nreq * G <= max_rows
         ents = v["stream"][so:so + npg]
         pages = [(int(e) >> 5, (int(e) & 31) + 1) for e in ents]
         for qpos, r in enumerate(v["rows"][ro:ro + nreq]):
