@@ -3,8 +3,10 @@
 
 A step is one pass of the whole path -- decode kernel (partials) + merge
 kernel (bf16 output) -- over one synthetic batch whose inputs are resident
-in HBM.  Before every step (warm-up and timed) a 1 GiB fill evicts L2 and
-the 256 MB Infinity Cache, so KV is read from HBM, not from cache.  Step time
+in HBM.  Before every step (warm-up and timed) a 1 GiB read of another
+buffer evicts L2 and the 256 MB Infinity Cache, so KV is read from HBM, not
+from cache; a read leaves clean lines behind, so no write-back of the flush
+competes with the step.  Step time
 is the HIP-event time of the two kernels on the stream they run on; the
 planner and the uploads run once, before timing.
 
@@ -123,9 +125,14 @@ def main():
     sink = torch.empty(8192, dtype=torch.int32, device=dev)
     flush = torch.empty(max(args.flush_mb, 1) << 20, dtype=torch.uint8, device=dev)
     cap.cap_bench_fill(probe.data_ptr(), probe_bytes, 0x3F803F80, sp)
+    cap.cap_bench_fill(flush.data_ptr(), flush.numel(), 0, sp)
+
+    def evict():
+        cap.cap_bench_read(flush.data_ptr(), flush.numel(), sink.data_ptr(), sp)
+
     read_ms = []
     for _ in range(5):
-        cap.cap_bench_fill(flush.data_ptr(), flush.numel(), 0, sp)
+        evict()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         cap.cap_bench_read(probe.data_ptr(), probe_bytes, sink.data_ptr(), sp)
@@ -137,7 +144,7 @@ def main():
 
     def one_step(evs=None):
         if args.flush_mb > 0:
-            cap.cap_bench_fill(flush.data_ptr(), flush.numel(), 0, sp)
+            evict()
         if evs is not None:
             evs[0].record(stream)
         dec.decode()
@@ -244,7 +251,7 @@ def main():
         src = torch.empty(nb, dtype=torch.uint8, device=dev)
         dst = torch.empty(nb, dtype=torch.uint8, device=dev)
         cap.cap_bench_fill(src.data_ptr(), nb, 1, sp)
-        cap.cap_bench_fill(flush.data_ptr(), flush.numel(), 0, sp)
+        evict()
         cap.cap_bench_copy(dst.data_ptr(), src.data_ptr(), nb, sp)
         torch.cuda.synchronize(dev)
         result["copy_probe_bytes"] = nb

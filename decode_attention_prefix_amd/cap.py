@@ -53,7 +53,8 @@ class PlanOpts(ctypes.Structure):
     _fields_ = [("share_mode", ctypes.c_int32), ("split_pages", ctypes.c_int32),
                 ("max_rows", ctypes.c_int32), ("num_cus", ctypes.c_int32),
                 ("waves_per_cu", ctypes.c_int32), ("rounds", ctypes.c_float),
-                ("share_margin", ctypes.c_float), ("reserved", ctypes.c_int32 * 4)]
+                ("share_margin", ctypes.c_float), ("kernel_variant", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 3)]
 
 
 class PlanStats(ctypes.Structure):

@@ -83,6 +83,7 @@ struct cap_plan {
     size_t off_items = 0, off_stream = 0, off_rows = 0, off_moff = 0, off_mrows = 0, dev_bytes = 0;
     std::vector<unsigned char> host_image;
     void *dev = nullptr;
+    int variant = 0;
 };
 
 namespace {
@@ -311,7 +312,8 @@ struct Planner {
 void fill_defaults(cap_plan_opts &o)
 {
     if (o.share_mode == 2) o.share_mode = -1;
-    if (o.max_rows == 0) o.max_rows = 32;
+    if (o.max_rows == 0 && o.kernel_variant >= 1 && o.kernel_variant <= 4)
+        o.max_rows = cap::variant_rows(o.kernel_variant);
     if (o.num_cus == 0) o.num_cus = 256;
     if (o.waves_per_cu == 0) o.waves_per_cu = 4;
     if (o.rounds == 0.f) o.rounds = 2.0f;
@@ -331,7 +333,7 @@ void cap_plan_opts_default(cap_plan_opts *opts)
     if (!opts) return;
     std::memset(opts, 0, sizeof *opts);
     opts->share_mode = -1;
-    fill_defaults(*opts);
+    fill_defaults(*opts);   // kernel_variant and max_rows stay 0 (chosen per tree)
 }
 
 cap_status cap_tree_device_bytes(const cap_attn_desc *attn, const cap_tree_desc *tree, size_t *bytes)
@@ -384,11 +386,18 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
     const auto t0 = std::chrono::steady_clock::now();
     cap_plan_opts o;
     if (opts_in) o = *opts_in; else cap_plan_opts_default(&o);
+    if (o.kernel_variant == 0)   // groups wider than 16 rows need a 32-row build
+        o.kernel_variant = (tree->G > 16 || o.max_rows == 32) ? 1 : cap::default_variant();
     fill_defaults(o);
     if (o.share_mode < -1 || o.share_mode > 1)
         return fail(CAP_ERR_INVALID_ARG, "share_mode %d not in {-1, 0, 1, 2}", o.share_mode);
+    if (o.kernel_variant < 1 || o.kernel_variant > 4)
+        return fail(CAP_ERR_INVALID_ARG, "kernel_variant %d not in 0..4", o.kernel_variant);
     if (o.max_rows != 16 && o.max_rows != 32)
         return fail(CAP_ERR_INVALID_ARG, "max_rows %d not in {16, 32}", o.max_rows);
+    if (o.max_rows > cap::variant_rows(o.kernel_variant))
+        return fail(CAP_ERR_INVALID_ARG, "max_rows %d exceeds the %d rows of kernel variant %d",
+                    o.max_rows, cap::variant_rows(o.kernel_variant), o.kernel_variant);
     if (o.max_rows < tree->G)
         return fail(CAP_ERR_INVALID_ARG, "max_rows %d below the GQA group %d", o.max_rows, tree->G);
     if (o.split_pages < 0 || o.num_cus < 0 || o.waves_per_cu < 0 || !(o.rounds > 0.f) ||
@@ -398,6 +407,7 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
     cap_plan *p = new (std::nothrow) cap_plan();
     if (!p) return fail(CAP_ERR_INVALID_ARG, "out of host memory");
     p->tree = tree;
+    p->variant = o.kernel_variant;
     const int Hkv = tree->attn.num_kv_heads, Hq = tree->attn.num_q_heads, D = tree->attn.head_dim;
     Planner pl(*tree, o);
     pl.build_groups();
@@ -562,7 +572,7 @@ cap_status cap_decode_attention(const cap_plan *plan, const void *q, const void 
     a.Hkv = plan->tree->attn.num_kv_heads;
     a.G = plan->tree->G;
     a.scale_log2 = (float)((double)plan->tree->attn.sm_scale * 1.4426950408889634);
-    const int e = cap::launch_decode(a, plan->tree->attn.head_dim, stream);
+    const int e = cap::launch_decode(a, plan->tree->attn.head_dim, plan->variant, stream);
     if (e != 0) return fail(CAP_ERR_HIP, "decode launch failed: %s", cap::hip_error_string(e));
     return CAP_OK;
 }

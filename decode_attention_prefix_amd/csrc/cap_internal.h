@@ -54,7 +54,11 @@ struct MergeArgs {
 };
 
 // Kernel launchers (cap_kernels.hip); return the hipError_t as int.
-int launch_decode(const DecodeArgs &a, int head_dim, void *stream);
+// Decode kernel variants (rows per wave / KV buffers / waves per SIMD):
+// 1: 32 / 3 / 1, 2: 32 / 2 / 2, 3: 16 / 3 / 1, 4: 16 / 2 / 2.
+int launch_decode(const DecodeArgs &a, int head_dim, int variant, void *stream);
+int variant_rows(int variant);
+int default_variant();
 int launch_merge(const MergeArgs &a, int head_dim, void *stream);
 int launch_fill(void *buf, size_t words, uint32_t value, void *stream);
 int launch_read(const void *buf, size_t vec16, void *sink, void *stream);

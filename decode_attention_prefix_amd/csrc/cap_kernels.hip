@@ -62,11 +62,17 @@ __device__ __forceinline__ float fast_exp2(float x)
     return __builtin_amdgcn_exp2f(x);
 }
 
+// Rows rescale their accumulators only when their maximum logit (base-2
+// units) exceeds the reference they were accumulated against by more than
+// this; otherwise p = 2^(x - m_ref) <= 2^8 stays exact enough in fp32 and
+// bf16, and (m_ref, l, o) is still a valid partial for any reference.
+constexpr float kRescaleThreshold = 8.0f;
+
 // KV fragments of one 2-page step, already in MFMA operand layout.
 template <int D>
 struct Step {
     u32x4 k0[D / 32], k1[D / 32];   // QK A operands, page 0 / page 1
-    u32x2 v0[D / 16], v1[D / 16];   // PV A operand halves, page 0 / page 1
+    u32x4 v[D / 16];                // PV A operands: .xy page 0, .zw page 1
     int nt0, nt1;                   // valid tokens in page 0 / page 1 (nt1 = 0: no page)
 };
 
@@ -101,41 +107,53 @@ __device__ __forceinline__ void load_step(Step<D> &f, const DecodeArgs &a, int h
     }
 #pragma unroll
     for (int j = 0; j < D / 16; ++j) {
-        f.v0[j] = ld8(vb0 + (16 * j + n) * kPage + 4 * c);
-        f.v1[j] = ld8(vb1 + (16 * j + n) * kPage + 4 * c);
+        const u32x2 x0 = ld8(vb0 + (16 * j + n) * kPage + 4 * c);
+        const u32x2 x1 = ld8(vb1 + (16 * j + n) * kPage + 4 * c);
+        f.v[j] = u32x4{x0.x, x0.y, x1.x, x1.y};
     }
 }
 
-// Zero the V elements of tokens >= nt in a page's fragments (they may hold
-// NaN; 0 * NaN would otherwise poison the MFMA sum).
+// Zero the V elements of tokens >= nt (page 0: .xy, page 1: .zw) -- those
+// slots may hold NaN, and 0 * NaN would poison the MFMA sum.
 template <int D>
-__device__ __forceinline__ void mask_v(u32x2 (&v)[D / 16], int nt, int c)
+__device__ __forceinline__ void mask_v(u32x4 (&v)[D / 16], int nt0, int nt1, int c)
 {
     const int t = 4 * c;
-    const uint32_t w0 = (t + 0 < nt ? 0x0000FFFFu : 0u) | (t + 1 < nt ? 0xFFFF0000u : 0u);
-    const uint32_t w1 = (t + 2 < nt ? 0x0000FFFFu : 0u) | (t + 3 < nt ? 0xFFFF0000u : 0u);
+    const uint32_t a0 = (t + 0 < nt0 ? 0x0000FFFFu : 0u) | (t + 1 < nt0 ? 0xFFFF0000u : 0u);
+    const uint32_t a1 = (t + 2 < nt0 ? 0x0000FFFFu : 0u) | (t + 3 < nt0 ? 0xFFFF0000u : 0u);
+    const uint32_t b0 = (t + 0 < nt1 ? 0x0000FFFFu : 0u) | (t + 1 < nt1 ? 0xFFFF0000u : 0u);
+    const uint32_t b1 = (t + 2 < nt1 ? 0x0000FFFFu : 0u) | (t + 3 < nt1 ? 0xFFFF0000u : 0u);
 #pragma unroll
     for (int j = 0; j < D / 16; ++j) {
-        v[j].x &= w0;
-        v[j].y &= w1;
+        v[j].x &= a0;
+        v[j].y &= a1;
+        v[j].z &= b0;
+        v[j].w &= b1;
     }
 }
 
-template <int D>
-__device__ __forceinline__ void compute_step(Step<D> &f, const u32x4 (&qf)[2][D / 32],
-                                             f32x4 (&o)[2][D / 16], float (&m_run)[2],
-                                             float (&l_run)[2], bool two, float scale, int c)
+// max over the four lanes n, n+16, n+32, n+48 that hold one query row
+__device__ __forceinline__ float row_max4(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v),
+                                                    __builtin_bit_cast(uint32_t, v), false, false);
+    v = fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+    const auto q = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v),
+                                                    __builtin_bit_cast(uint32_t, v), false, false);
+    return fmaxf(__builtin_bit_cast(float, q[0]), __builtin_bit_cast(float, q[1]));
+}
+
+template <int D, int RB>
+__device__ __forceinline__ void compute_step(Step<D> &f, const u32x4 (&qf)[RB][D / 32],
+                                             f32x4 (&o)[RB][D / 16], float (&m_ref)[RB],
+                                             float (&l_run)[RB], int nblk, float scale, int c)
 {
     const bool has1 = f.nt1 > 0;
-    if (f.nt0 < kPage) mask_v<D>(f.v0, f.nt0, c);
-    if (f.nt1 < kPage) mask_v<D>(f.v1, f.nt1, c);
-    u32x4 vf[D / 16];
-#pragma unroll
-    for (int j = 0; j < D / 16; ++j) vf[j] = u32x4{f.v0[j].x, f.v0[j].y, f.v1[j].x, f.v1[j].y};
+    if (f.nt0 < kPage || f.nt1 < kPage) mask_v<D>(f.v, f.nt0, f.nt1, c);
 
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        if (b == 1 && !two) break;
+    for (int b = 0; b < RB; ++b) {
+        if (b >= nblk) break;
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < D / 32; ++i) s0 = mfma(f.k0[i], qf[b][i], s0);
@@ -146,8 +164,8 @@ __device__ __forceinline__ void compute_step(Step<D> &f, const u32x4 (&qf)[2][D 
         float x[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            x[j] = s0[j] * scale;
-            x[4 + j] = s1[j] * scale;
+            x[j] = s0[j];
+            x[4 + j] = s1[j];
         }
         if (f.nt0 < kPage) {
 #pragma unroll
@@ -157,37 +175,44 @@ __device__ __forceinline__ void compute_step(Step<D> &f, const u32x4 (&qf)[2][D 
 #pragma unroll
             for (int j = 0; j < 4; ++j) x[4 + j] = (4 * c + j < f.nt1) ? x[4 + j] : -INFINITY;
         }
-        float mx = x[0];
+        float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        mx = row_max4(mx) * scale;                       // base-2 units (scale > 0)
+        const bool need = mx > m_ref[b] + kRescaleThreshold;
+        if (__builtin_amdgcn_ballot_w64(need)) {         // wave-uniform, rare after the first step
+            const float m_new = need ? mx : m_ref[b];
+            const float alpha = fast_exp2(m_ref[b] - m_new);   // 1 if unchanged, 0 from -inf
+            m_ref[b] = m_new;
+            l_run[b] *= alpha;
 #pragma unroll
-        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run[b], mx);
-        const float alpha = fast_exp2(m_run[b] - m_new);
-        m_run[b] = m_new;
+            for (int j = 0; j < D / 16; ++j) o[b][j] *= alpha;
+        }
+        const float mneg = -m_ref[b];
         float p[8];
         float psum = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            p[j] = fast_exp2(x[j] - m_new);
+            p[j] = fast_exp2(__builtin_fmaf(x[j], scale, mneg));
             psum += p[j];
         }
-        l_run[b] = l_run[b] * alpha + psum;
+        l_run[b] += psum;
         bf16x8 pb;
 #pragma unroll
         for (int j = 0; j < 8; ++j) pb[j] = (__bf16)p[j];
         const u32x4 pw = __builtin_bit_cast(u32x4, pb);
 #pragma unroll
-        for (int j = 0; j < D / 16; ++j) {
-            o[b][j] *= alpha;
-            o[b][j] = mfma(vf[j], pw, o[b][j]);
-        }
+        for (int j = 0; j < D / 16; ++j) o[b][j] = mfma(f.v[j], pw, o[b][j]);
     }
 }
 
-template <int D>
-__global__ __launch_bounds__(kWaveSize * kWavesPerBlock) void decode_kernel(DecodeArgs a)
+// RB: 16-row MFMA blocks a wave holds (rows per item <= 16 RB).
+// NBUF: register buffers of the KV pipeline (NBUF-1 steps in flight).
+// WPE: waves per SIMD the register budget is sized for.
+template <int D, int RB, int NBUF, int WPE>
+__global__ __launch_bounds__(kWaveSize * kWavesPerBlock) __attribute__((amdgpu_waves_per_eu(WPE)))
+void decode_kernel(DecodeArgs a)
 {
+    static_assert(NBUF == 2 || NBUF == 3, "two or three KV buffers");
     const int lane = threadIdx.x & (kWaveSize - 1);
     const int n = lane & 15, c = lane >> 4;
     const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
@@ -195,12 +220,12 @@ __global__ __launch_bounds__(kWaveSize * kWavesPerBlock) void decode_kernel(Deco
     const WorkItem it = a.items[wid];
     const int G = a.G;
     const int nrows = it.nreq * G;
-    const bool two = nrows > 16;
+    const int nblk = (nrows + 15) >> 4;
 
     // Q fragments (B operand of QK): lane (n, c) holds row 16b+n, dims 8(4i+c)..+7.
-    u32x4 qf[2][D / 32];
+    u32x4 qf[RB][D / 32];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < RB; ++b) {
         const int row = 16 * b + n;
         if (row < nrows) {
             const int req = a.rows[it.row_off + row / G];
@@ -214,13 +239,17 @@ __global__ __launch_bounds__(kWaveSize * kWavesPerBlock) void decode_kernel(Deco
         }
     }
 
-    f32x4 o[2][D / 16];
+    f32x4 o[RB][D / 16];
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < RB; ++b)
 #pragma unroll
         for (int j = 0; j < D / 16; ++j) o[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run[2] = {-INFINITY, -INFINITY};
-    float l_run[2] = {0.f, 0.f};
+    float m_ref[RB], l_run[RB];
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+        m_ref[b] = -INFINITY;
+        l_run[b] = 0.f;
+    }
 
     // Page table of the item, one page per lane (items hold at most 64 pages).
     int lane_pid = 0, lane_nt = 0;
@@ -230,26 +259,39 @@ __global__ __launch_bounds__(kWaveSize * kWavesPerBlock) void decode_kernel(Deco
         lane_nt = (e & 31) + 1;
     }
 
-    // Three register buffers: two steps are in flight while one computes.
     const int nsteps = (it.npages + 1) >> 1;
-    Step<D> fa, fb, fc;
+    const float sc = a.scale_log2;
+    Step<D> fa, fb;
     load_step<D>(fa, a, it.head, it.npages, 0, lane_pid, lane_nt, n, c);
-    load_step<D>(fb, a, it.head, it.npages, 1, lane_pid, lane_nt, n, c);
-    for (int s = 0; s < nsteps; s += 3) {
-        load_step<D>(fc, a, it.head, it.npages, s + 2, lane_pid, lane_nt, n, c);
-        compute_step<D>(fa, qf, o, m_run, l_run, two, a.scale_log2, c);
-        if (s + 1 >= nsteps) break;
-        load_step<D>(fa, a, it.head, it.npages, s + 3, lane_pid, lane_nt, n, c);
-        compute_step<D>(fb, qf, o, m_run, l_run, two, a.scale_log2, c);
-        if (s + 2 >= nsteps) break;
-        load_step<D>(fb, a, it.head, it.npages, s + 4, lane_pid, lane_nt, n, c);
-        compute_step<D>(fc, qf, o, m_run, l_run, two, a.scale_log2, c);
+    if constexpr (NBUF == 2) {
+        // one step in flight while one computes
+        for (int s = 0; s < nsteps; s += 2) {
+            load_step<D>(fb, a, it.head, it.npages, s + 1, lane_pid, lane_nt, n, c);
+            compute_step<D, RB>(fa, qf, o, m_ref, l_run, nblk, sc, c);
+            if (s + 1 >= nsteps) break;
+            load_step<D>(fa, a, it.head, it.npages, s + 2, lane_pid, lane_nt, n, c);
+            compute_step<D, RB>(fb, qf, o, m_ref, l_run, nblk, sc, c);
+        }
+    } else {
+        // two steps in flight while one computes
+        Step<D> fc;
+        load_step<D>(fb, a, it.head, it.npages, 1, lane_pid, lane_nt, n, c);
+        for (int s = 0; s < nsteps; s += 3) {
+            load_step<D>(fc, a, it.head, it.npages, s + 2, lane_pid, lane_nt, n, c);
+            compute_step<D, RB>(fa, qf, o, m_ref, l_run, nblk, sc, c);
+            if (s + 1 >= nsteps) break;
+            load_step<D>(fa, a, it.head, it.npages, s + 3, lane_pid, lane_nt, n, c);
+            compute_step<D, RB>(fb, qf, o, m_ref, l_run, nblk, sc, c);
+            if (s + 2 >= nsteps) break;
+            load_step<D>(fb, a, it.head, it.npages, s + 4, lane_pid, lane_nt, n, c);
+            compute_step<D, RB>(fc, qf, o, m_ref, l_run, nblk, sc, c);
+        }
     }
 
     // Partials: slot = (slot_base + row / G) * Hq + head * G + row % G.
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        if (b == 1 && !two) break;
+    for (int b = 0; b < RB; ++b) {
+        if (b >= nblk) break;
         float l = l_run[b];
         l += __shfl_xor(l, 16);
         l += __shfl_xor(l, 32);
@@ -260,7 +302,7 @@ __global__ __launch_bounds__(kWaveSize * kWavesPerBlock) void decode_kernel(Deco
 #pragma unroll
             for (int j = 0; j < D / 16; ++j) *reinterpret_cast<f32x4 *>(po + 16 * j) = o[b][j];
             if (c == 0) {
-                a.part_m[slot] = m_run[b];
+                a.part_m[slot] = m_ref[b];
                 a.part_l[slot] = l;
             }
         }
@@ -358,9 +400,16 @@ __global__ __launch_bounds__(256) void fill_kernel(uint32_t *buf, size_t words, 
 
 __global__ __launch_bounds__(256) void read_kernel(const u32x4 *buf, size_t n, uint32_t *sink)
 {
+    // four independent 16-byte loads in flight per lane per iteration
     const size_t stride = (size_t)gridDim.x * blockDim.x;
     uint32_t x = 0;
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < n; i += 4 * stride) {
+        const u32x4 v0 = buf[i], v1 = buf[i + stride], v2 = buf[i + 2 * stride], v3 = buf[i + 3 * stride];
+        x ^= v0.x ^ v0.y ^ v0.z ^ v0.w ^ v1.x ^ v1.y ^ v1.z ^ v1.w;
+        x ^= v2.x ^ v2.y ^ v2.z ^ v2.w ^ v3.x ^ v3.y ^ v3.z ^ v3.w;
+    }
+    for (; i < n; i += stride) {
         const u32x4 v = buf[i];
         x ^= v.x ^ v.y ^ v.z ^ v.w;
     }
@@ -369,7 +418,7 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4 *buf, size_t n, u
     __syncthreads();
     if (threadIdx.x == 0) {
         uint32_t y = 0;
-        for (int i = 0; i < 256; ++i) y ^= red[i];
+        for (int k = 0; k < 256; ++k) y ^= red[k];
         sink[blockIdx.x] = y;
     }
 }
@@ -383,18 +432,36 @@ __global__ __launch_bounds__(256) void copy_kernel(u32x4 *dst, const u32x4 *src,
 
 }  // namespace
 
-int launch_decode(const DecodeArgs &a, int head_dim, void *stream)
+template <int D>
+static void launch_variant(int variant, dim3 grid, dim3 block, hipStream_t s, const DecodeArgs &a)
+{
+    switch (variant) {
+    case 1: hipLaunchKernelGGL((decode_kernel<D, 2, 3, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<D, 2, 2, 2>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((decode_kernel<D, 1, 3, 1>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((decode_kernel<D, 1, 2, 2>), grid, block, 0, s, a); break;
+    }
+}
+
+int launch_decode(const DecodeArgs &a, int head_dim, int variant, void *stream)
 {
     if (a.n_items <= 0) return 0;
     const dim3 grid((a.n_items + kWavesPerBlock - 1) / kWavesPerBlock);
     const dim3 block(kWaveSize * kWavesPerBlock);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (head_dim == 128)
-        hipLaunchKernelGGL(decode_kernel<128>, grid, block, 0, s, a);
+        launch_variant<128>(variant, grid, block, s, a);
     else
-        hipLaunchKernelGGL(decode_kernel<64>, grid, block, 0, s, a);
+        launch_variant<64>(variant, grid, block, s, a);
     return (int)hipGetLastError();
 }
+
+int variant_rows(int variant)
+{
+    return (variant == 1 || variant == 2) ? 32 : 16;
+}
+
+int default_variant() { return 4; }
 
 int launch_merge(const MergeArgs &a, int head_dim, void *stream)
 {

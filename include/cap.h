@@ -110,13 +110,17 @@ typedef struct cap_plan_opts {
                                  every non-empty node, 2 auto (same as -1) */
     int32_t split_pages;      /* 0 auto; else the most KV pages one work item streams
                                  (values above 64 are treated as 64) */
-    int32_t max_rows;         /* 0 auto (32); query rows per work item: 16 or 32 */
+    int32_t max_rows;         /* 0 auto (the kernel variant's rows per wave); query rows
+                                 per work item: 16 or 32, at most the variant's */
     int32_t num_cus;          /* 0 = 256 (MI355X); used by the cost model */
     int32_t waves_per_cu;     /* 0 = 4; resident work items per CU in the cost model */
     float rounds;             /* 0 = 2.0; target work-item rounds per resident slot */
     float share_margin;       /* 0 = 1.0; share a node only if saved bytes exceed
                                  margin x added partial bytes */
-    int32_t reserved[4];
+    int32_t kernel_variant;   /* 0 auto; 1..4 pick a decode-kernel build: query rows per
+                                 wave / KV register buffers / waves per SIMD =
+                                 1: 32/3/1, 2: 32/2/2, 3: 16/3/1, 4: 16/2/2 */
+    int32_t reserved[3];
 } cap_plan_opts;
 
 /* Plan summary (host-side numbers; bytes are per decode step). */

@@ -81,7 +81,8 @@ def test_tree_validation_errors():
 def test_planner_rejects_bad_options():
     h = cap.cap_tree_upload(small_tree())
     try:
-        for kw in ({"share_mode": 5}, {"max_rows": 24}, {"split_pages": -1}, {"rounds": -1.0}):
+        for kw in ({"share_mode": 5}, {"max_rows": 24}, {"split_pages": -1}, {"rounds": -1.0},
+                   {"kernel_variant": 7}, {"max_rows": 32, "kernel_variant": 4}):
             with pytest.raises(cap.CapError) as e:
                 cap.cap_plan_step(h, **kw)
             assert e.value.status == 1
@@ -157,11 +158,11 @@ def test_planner_coverage_random_trees(share_mode, split_pages):
         t = wl.tree_from_lengths(nt, par, paths, Hq, Hkv, 64, page_perm_rng=rng)
         h = cap.cap_tree_upload(t)
         try:
-            for max_rows in (16, 32):
+            for max_rows, variant in ((16, 4), (16, 3), (32, 1), (32, 2)):
                 if Hq // Hkv > max_rows:
                     continue
                 p = cap.cap_plan_step(h, share_mode=share_mode, split_pages=split_pages,
-                                      max_rows=max_rows)
+                                      max_rows=max_rows, kernel_variant=variant)
                 try:
                     check_coverage(t, p, max_rows)
                 finally:
@@ -178,7 +179,8 @@ def test_planner_coverage_configs(cfg):
     h = cap.cap_tree_upload(t)
     try:
         for mode in (-1, 0, 1):
-            p = cap.cap_plan_step(h, share_mode=mode)
+            p = cap.cap_plan_step(h, share_mode=mode,
+                                  kernel_variant=1 if Hq // Hkv > 16 else 0)
             try:
                 st = check_coverage(t, p)
                 stats = wl.tree_stats(t)

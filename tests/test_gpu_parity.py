@@ -64,9 +64,9 @@ def test_config0_all_plan_variants():
     w, ref = config_case(0)
     for mode in (-1, 0, 1):
         for split in (0, 1, 3, 100):
-            for rows in (16, 32):
-                out, _, _ = run_gpu(w, share_mode=mode, split_pages=split, max_rows=rows)
-                check(out, ref, f"cfg0 mode={mode} split={split} rows={rows}")
+            for variant in (1, 2, 3, 4):
+                out, _, _ = run_gpu(w, share_mode=mode, split_pages=split, kernel_variant=variant)
+                check(out, ref, f"cfg0 mode={mode} split={split} variant={variant}")
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4])
@@ -89,6 +89,13 @@ def test_full_configs_forced_modes(cfg, mode):
     check(out, ref, f"cfg{cfg} mode={mode}")
 
 
+@pytest.mark.parametrize("variant", [1, 2, 3, 4])
+def test_kernel_variants_full_config(variant):
+    w, ref = config_case(3)
+    out, _, _ = run_gpu(w, kernel_variant=variant)
+    check(out, ref, f"cfg3 variant={variant}")
+
+
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("HqHkv", [(8, 8), (8, 2), (32, 8), (16, 2), (32, 1)])
 def test_random_small_trees(D, HqHkv):
@@ -101,8 +108,11 @@ def test_random_small_trees(D, HqHkv):
                                              empty_root=bool(seed % 2), min_len=0)
         w = wl.make_workload(nt, par, paths, Hq, Hkv, D, rng, extra_pool_pages=5)
         ref = oracle.decode(w.tree, w.q, w.k_pool, w.v_pool)
-        for opts in ({}, {"share_mode": 1, "split_pages": 1}, {"share_mode": 0},
-                     {"split_pages": 2, "max_rows": 16 if Hq // Hkv <= 16 else 32}):
+        big = Hq // Hkv > 16
+        for opts in ({"kernel_variant": 1 if big else 0},
+                     {"share_mode": 1, "split_pages": 1, "kernel_variant": 2 if big else 3},
+                     {"share_mode": 0, "kernel_variant": 1},
+                     {"split_pages": 2, "kernel_variant": 2}):
             out, _, _ = run_gpu(w, **opts)
             check(out, ref, f"seed={seed} D={D} Hq={Hq} Hkv={Hkv} {opts}")
 
@@ -114,7 +124,7 @@ def test_large_logits_and_single_token_requests():
     q = rng.standard_normal((5, 16, 128)).astype(np.float32) * 4
     w = wl.make_workload(nt, par, paths, 16, 4, 128, rng, q_values=q)
     ref = oracle.decode(w.tree, w.q, w.k_pool, w.v_pool)
-    for opts in ({}, {"share_mode": 1, "split_pages": 1}):
+    for opts in ({}, {"share_mode": 1, "split_pages": 1}, {"kernel_variant": 1}):
         out, _, _ = run_gpu(w, **opts)
         check(out, ref, f"stretched {opts}")
 
