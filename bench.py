@@ -76,7 +76,8 @@ def main():
     ap.add_argument("--flush-mb", type=int, default=1024)
     ap.add_argument("--share", type=int, default=-1, help="-1 auto, 0 fold all, 1 share all")
     ap.add_argument("--split-pages", type=int, default=0)
-    ap.add_argument("--max-rows", type=int, default=0)
+    ap.add_argument("--shared-rows", type=int, default=0,
+                    help="groups with more query rows than this use shared workgroups (0: 32)")
     ap.add_argument("--rounds", type=float, default=0.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--read-probe-mb", type=int, default=2048)
@@ -110,8 +111,8 @@ def main():
     st_tree = wl.tree_stats(w.tree)
     t_gen = time.perf_counter() - t_gen
     opts = {"share_mode": args.share, "split_pages": args.split_pages}
-    if args.max_rows:
-        opts["max_rows"] = args.max_rows
+    if args.shared_rows:
+        opts["shared_rows"] = args.shared_rows
     if args.rounds:
         opts["rounds"] = args.rounds
     dec = TreeDecoder(w.tree, w.q, w.k_pool, w.v_pool, device=dev, **opts)
@@ -204,7 +205,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
-            "kernel": "decode_kernel<128>" if w.tree.head_dim == 128 else "decode_kernel<64>",
+            "kernel": f"decode_kernel<{w.tree.head_dim}>",
             "algorithmic_bytes_per_launch": alg_bytes_decode,
             "decode_us_mean": round(dec_mean * 1e3, 3),
         },
@@ -223,7 +224,7 @@ def main():
         "bytes": {"unique_kv": uniq, "unshared_kv": st_tree["unshared_kv_bytes"],
                   "kv_streamed_by_items": plan["kv_bytes_streamed"],
                   "partial": plan["partial_bytes"], "q": st_tree["q_bytes"], "out": st_tree["out_bytes"]},
-        "plan": {k: plan[k] for k in ("num_items", "num_tasks", "num_groups", "partial_rows",
+        "plan": {k: plan[k] for k in ("num_items", "num_shared_items", "num_tasks", "num_groups", "partial_rows",
                                       "max_partials_per_request", "max_pages_per_item")},
         "plan_host_us": round(plan["plan_host_us"], 1),
         "flush_mb": args.flush_mb,

@@ -51,15 +51,14 @@ class TreeDesc(ctypes.Structure):
 
 class PlanOpts(ctypes.Structure):
     _fields_ = [("share_mode", ctypes.c_int32), ("split_pages", ctypes.c_int32),
-                ("max_rows", ctypes.c_int32), ("num_cus", ctypes.c_int32),
+                ("shared_rows", ctypes.c_int32), ("num_cus", ctypes.c_int32),
                 ("waves_per_cu", ctypes.c_int32), ("rounds", ctypes.c_float),
-                ("share_margin", ctypes.c_float), ("kernel_variant", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 3)]
+                ("share_margin", ctypes.c_float), ("reserved", ctypes.c_int32 * 4)]
 
 
 class PlanStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
-        "num_items", "num_tasks", "num_groups", "partial_rows", "workspace_bytes",
+        "num_items", "num_shared_items", "num_tasks", "num_groups", "partial_rows", "workspace_bytes",
         "plan_device_bytes", "tree_device_bytes", "kv_bytes_streamed", "kv_bytes_unique",
         "kv_bytes_unshared", "partial_bytes")] + [
         ("max_partials_per_request", ctypes.c_int32), ("max_pages_per_item", ctypes.c_int32),
@@ -72,7 +71,8 @@ class WorkItemC(ctypes.Structure):
 
 
 class PlanView(ctypes.Structure):
-    _fields_ = [("num_items", ctypes.c_int32), ("items", ctypes.POINTER(WorkItemC)),
+    _fields_ = [("num_shared_items", ctypes.c_int32), ("shared_items", ctypes.POINTER(WorkItemC)),
+                ("num_items", ctypes.c_int32), ("items", ctypes.POINTER(WorkItemC)),
                 ("stream_len", ctypes.c_int32), ("stream", ctypes.POINTER(ctypes.c_int32)),
                 ("rows_len", ctypes.c_int32), ("rows", ctypes.POINTER(ctypes.c_int32)),
                 ("num_requests", ctypes.c_int32), ("merge_off", ctypes.POINTER(ctypes.c_int32)),
@@ -210,7 +210,9 @@ def cap_plan_get_view(plan: int) -> dict:
         a = np.ctypeslib.as_array(ctypes.cast(ptr, ctypes.POINTER(ctypes.c_int32)), (n * width,))
         return a.copy().reshape((n, width) if width > 1 else (n,))
 
-    return {"items": arr(v.items, v.num_items, 6), "stream": arr(v.stream, v.stream_len),
+    return {"items": arr(v.items, v.num_items, 6),
+            "shared_items": arr(v.shared_items, v.num_shared_items, 6),
+            "stream": arr(v.stream, v.stream_len),
             "rows": arr(v.rows, v.rows_len),
             "merge_off": arr(v.merge_off, v.num_requests + 1),
             "merge_rows": arr(v.merge_rows, int(arr(v.merge_off, v.num_requests + 1)[-1]))}

@@ -75,15 +75,15 @@ struct cap_tree {
 struct cap_plan {
     const cap_tree *tree = nullptr;
     cap_plan_stats stats{};
-    std::vector<WorkItem> items;
+    std::vector<WorkItem> shared_items;   // one workgroup each
+    std::vector<WorkItem> items;          // private: one wave each
     std::vector<int32_t> stream;      // (tree page index << 5) | (ntok - 1)
     std::vector<int32_t> rows;        // request ids
     std::vector<int32_t> merge_off, merge_rows;
     // device image
-    size_t off_items = 0, off_stream = 0, off_rows = 0, off_moff = 0, off_mrows = 0, dev_bytes = 0;
+    size_t off_shared = 0, off_items = 0, off_stream = 0, off_rows = 0, off_moff = 0, off_mrows = 0, dev_bytes = 0;
     std::vector<unsigned char> host_image;
     void *dev = nullptr;
-    int variant = 0;
 };
 
 namespace {
@@ -238,8 +238,16 @@ struct Planner {
         }
     }
 
-    int rows_per_item() const { return o.max_rows; }
-    int reqs_per_item() const { return std::max(1, rows_per_item() / G); }
+    // Groups wider than the threshold run as shared workgroup items (up to
+    // 256 rows each), the rest as private one-wave items (up to 16 rows).
+    bool is_shared(int64_t nreq) const
+    {
+        return G > cap::kPrivateRows || nreq * G > o.shared_rows;
+    }
+    int reqs_per_item(int64_t nreq) const
+    {
+        return is_shared(nreq) ? cap::kSharedRows / G : cap::kPrivateRows / G;
+    }
 
     int64_t estimate_chunks(int64_t pages) const
     {
@@ -295,7 +303,8 @@ struct Planner {
                 if (t.parent[n] == -1) walk(n, {}, 0);
             int64_t W = 0;   // item-pages if nothing were split
             for (const Group &g : groups) {
-                const int64_t rg = ((int64_t)g.reqs.size() + reqs_per_item() - 1) / reqs_per_item();
+                const int64_t nreq = (int64_t)g.reqs.size();
+                const int64_t rg = (nreq + reqs_per_item(nreq) - 1) / reqs_per_item(nreq);
                 W += (int64_t)g.entries.size() * rg * Hkv;
             }
             if (o.split_pages > 0) {
@@ -312,10 +321,9 @@ struct Planner {
 void fill_defaults(cap_plan_opts &o)
 {
     if (o.share_mode == 2) o.share_mode = -1;
-    if (o.max_rows == 0 && o.kernel_variant >= 1 && o.kernel_variant <= 4)
-        o.max_rows = cap::variant_rows(o.kernel_variant);
+    if (o.shared_rows == 0) o.shared_rows = 32;
     if (o.num_cus == 0) o.num_cus = 256;
-    if (o.waves_per_cu == 0) o.waves_per_cu = 4;
+    if (o.waves_per_cu == 0) o.waves_per_cu = 8;
     if (o.rounds == 0.f) o.rounds = 2.0f;
     if (o.share_margin == 0.f) o.share_margin = 1.0f;
 }
@@ -333,7 +341,7 @@ void cap_plan_opts_default(cap_plan_opts *opts)
     if (!opts) return;
     std::memset(opts, 0, sizeof *opts);
     opts->share_mode = -1;
-    fill_defaults(*opts);   // kernel_variant and max_rows stay 0 (chosen per tree)
+    fill_defaults(*opts);
 }
 
 cap_status cap_tree_device_bytes(const cap_attn_desc *attn, const cap_tree_desc *tree, size_t *bytes)
@@ -386,20 +394,11 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
     const auto t0 = std::chrono::steady_clock::now();
     cap_plan_opts o;
     if (opts_in) o = *opts_in; else cap_plan_opts_default(&o);
-    if (o.kernel_variant == 0)   // groups wider than 16 rows need a 32-row build
-        o.kernel_variant = (tree->G > 16 || o.max_rows == 32) ? 1 : cap::default_variant();
     fill_defaults(o);
     if (o.share_mode < -1 || o.share_mode > 1)
         return fail(CAP_ERR_INVALID_ARG, "share_mode %d not in {-1, 0, 1, 2}", o.share_mode);
-    if (o.kernel_variant < 1 || o.kernel_variant > 4)
-        return fail(CAP_ERR_INVALID_ARG, "kernel_variant %d not in 0..4", o.kernel_variant);
-    if (o.max_rows != 16 && o.max_rows != 32)
-        return fail(CAP_ERR_INVALID_ARG, "max_rows %d not in {16, 32}", o.max_rows);
-    if (o.max_rows > cap::variant_rows(o.kernel_variant))
-        return fail(CAP_ERR_INVALID_ARG, "max_rows %d exceeds the %d rows of kernel variant %d",
-                    o.max_rows, cap::variant_rows(o.kernel_variant), o.kernel_variant);
-    if (o.max_rows < tree->G)
-        return fail(CAP_ERR_INVALID_ARG, "max_rows %d below the GQA group %d", o.max_rows, tree->G);
+    if (o.shared_rows < 0)
+        return fail(CAP_ERR_INVALID_ARG, "shared_rows %d is negative", o.shared_rows);
     if (o.split_pages < 0 || o.num_cus < 0 || o.waves_per_cu < 0 || !(o.rounds > 0.f) ||
         !(o.share_margin > 0.f))
         return fail(CAP_ERR_INVALID_ARG, "negative planner option");
@@ -407,13 +406,12 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
     cap_plan *p = new (std::nothrow) cap_plan();
     if (!p) return fail(CAP_ERR_INVALID_ARG, "out of host memory");
     p->tree = tree;
-    p->variant = o.kernel_variant;
     const int Hkv = tree->attn.num_kv_heads, Hq = tree->attn.num_q_heads, D = tree->attn.head_dim;
     Planner pl(*tree, o);
     pl.build_groups();
 
     // tasks: (page run, request subgroup); balanced splits of both
-    struct Task { int32_t so, np, ro, nr, sb; int64_t cost; };
+    struct Task { int32_t so, np, ro, nr, sb; bool shared; };
     std::vector<Task> tasks;
     std::vector<std::vector<int32_t>> req_rows(tree->R);
     int32_t slot_rows = 0;
@@ -421,7 +419,8 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
         const int64_t npg = (int64_t)g.entries.size();
         const int64_t k = std::max<int64_t>(1, (npg + pl.target_pages - 1) / pl.target_pages);
         const int nreq = (int)g.reqs.size();
-        const int rg = (nreq + pl.reqs_per_item() - 1) / pl.reqs_per_item();
+        const bool shared = pl.is_shared(nreq);
+        const int rg = (nreq + pl.reqs_per_item(nreq) - 1) / pl.reqs_per_item(nreq);
         const int32_t so0 = (int32_t)p->stream.size();
         p->stream.insert(p->stream.end(), g.entries.begin(), g.entries.end());
         const int32_t ro0 = (int32_t)p->rows.size();
@@ -430,8 +429,7 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
             const int64_t pb = npg * ci / k, pe = npg * (ci + 1) / k;
             for (int ri = 0; ri < rg; ++ri) {
                 const int rb = (int)((int64_t)nreq * ri / rg), re = (int)((int64_t)nreq * (ri + 1) / rg);
-                Task tk{(int32_t)(so0 + pb), (int32_t)(pe - pb), ro0 + rb, re - rb, slot_rows,
-                        (pe - pb) * 16};
+                Task tk{(int32_t)(so0 + pb), (int32_t)(pe - pb), ro0 + rb, re - rb, slot_rows, shared};
                 for (int q = rb; q < re; ++q) req_rows[g.reqs[q]].push_back(slot_rows + (q - rb));
                 slot_rows += re - rb;
                 tasks.push_back(tk);
@@ -443,13 +441,14 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
                      [](const Task &a, const Task &b) { return a.np > b.np; });
     // items: for each page run, for each KV head, its request subgroups back to
     // back, so the waves that read the same pages share a workgroup (and its L1)
-    p->items.reserve(tasks.size() * Hkv);
     for (size_t i = 0; i < tasks.size();) {
         size_t j = i + 1;
         while (j < tasks.size() && tasks[j].so == tasks[i].so && tasks[j].np == tasks[i].np) ++j;
         for (int h = 0; h < Hkv; ++h)
-            for (size_t k = i; k < j; ++k)
-                p->items.push_back(WorkItem{tasks[k].so, tasks[k].np, h, tasks[k].ro, tasks[k].nr, tasks[k].sb});
+            for (size_t k = i; k < j; ++k) {
+                const WorkItem w{tasks[k].so, tasks[k].np, h, tasks[k].ro, tasks[k].nr, tasks[k].sb};
+                (tasks[k].shared ? p->shared_items : p->items).push_back(w);
+            }
         i = j;
     }
     p->merge_off.assign(tree->R + 1, 0);
@@ -460,14 +459,17 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
         maxp = std::max<int32_t>(maxp, (int32_t)req_rows[r].size());
     }
 
-    // device image: items | stream | rows | merge_off | merge_rows
-    p->off_items = 0;
-    p->off_stream = align_up(p->items.size() * sizeof(WorkItem));
+    // device image: shared items | private items | stream | rows | merge_off | merge_rows
+    p->off_shared = 0;
+    p->off_items = align_up(p->shared_items.size() * sizeof(WorkItem));
+    p->off_stream = p->off_items + align_up(p->items.size() * sizeof(WorkItem));
     p->off_rows = p->off_stream + align_up(p->stream.size() * 4);
     p->off_moff = p->off_rows + align_up(p->rows.size() * 4);
     p->off_mrows = p->off_moff + align_up(p->merge_off.size() * 4);
     p->dev_bytes = std::max<size_t>(p->off_mrows + align_up(p->merge_rows.size() * 4), kAlign);
     p->host_image.assign(p->dev_bytes, 0);
+    std::memcpy(p->host_image.data() + p->off_shared, p->shared_items.data(),
+                p->shared_items.size() * sizeof(WorkItem));
     std::memcpy(p->host_image.data() + p->off_items, p->items.data(), p->items.size() * sizeof(WorkItem));
     std::memcpy(p->host_image.data() + p->off_stream, p->stream.data(), p->stream.size() * 4);
     std::memcpy(p->host_image.data() + p->off_rows, p->rows.data(), p->rows.size() * 4);
@@ -476,6 +478,7 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
 
     cap_plan_stats &s = p->stats;
     s.num_items = (int64_t)p->items.size();
+    s.num_shared_items = (int64_t)p->shared_items.size();
     s.num_tasks = (int64_t)tasks.size();
     s.num_groups = (int64_t)pl.groups.size();
     s.partial_rows = slot_rows;
@@ -507,6 +510,8 @@ cap_status cap_plan_get_stats(const cap_plan *plan, cap_plan_stats *stats)
 cap_status cap_plan_get_view(const cap_plan *plan, cap_plan_view *v)
 {
     if (!plan || !v) return fail(CAP_ERR_INVALID_ARG, "NULL argument");
+    v->num_shared_items = (int32_t)plan->shared_items.size();
+    v->shared_items = reinterpret_cast<const cap_work_item *>(plan->shared_items.data());
     v->num_items = (int32_t)plan->items.size();
     v->items = reinterpret_cast<const cap_work_item *>(plan->items.data());
     v->stream_len = (int32_t)plan->stream.size();
@@ -560,7 +565,9 @@ cap_status cap_decode_attention(const cap_plan *plan, const void *q, const void 
     cap_status st = split_workspace(plan, workspace, ws_bytes, &a.part_o, &a.part_m, &a.part_l);
     if (st != CAP_OK) return st;
     const char *d = static_cast<const char *>(plan->dev);
+    a.shared_items = reinterpret_cast<const WorkItem *>(d + plan->off_shared);
     a.items = reinterpret_cast<const WorkItem *>(d + plan->off_items);
+    a.n_shared = (int32_t)plan->shared_items.size();
     a.stream = reinterpret_cast<const int32_t *>(d + plan->off_stream);
     a.rows = reinterpret_cast<const int32_t *>(d + plan->off_rows);
     a.tree_pages = plan->tree->dev_pages;
@@ -572,7 +579,7 @@ cap_status cap_decode_attention(const cap_plan *plan, const void *q, const void 
     a.Hkv = plan->tree->attn.num_kv_heads;
     a.G = plan->tree->G;
     a.scale_log2 = (float)((double)plan->tree->attn.sm_scale * 1.4426950408889634);
-    const int e = cap::launch_decode(a, plan->tree->attn.head_dim, plan->variant, stream);
+    const int e = cap::launch_decode(a, plan->tree->attn.head_dim, stream);
     if (e != 0) return fail(CAP_ERR_HIP, "decode launch failed: %s", cap::hip_error_string(e));
     return CAP_OK;
 }

@@ -11,12 +11,15 @@ namespace cap {
 // Layout constants of the paged KV cache.
 constexpr int kPage = 16;            // tokens per page
 constexpr int kWaveSize = 64;        // CDNA wavefront
-constexpr int kWavesPerBlock = 4;    // waves per workgroup in the decode kernel
-constexpr int kRowsPerItem = 32;     // query rows one wave can hold (two 16-row MFMA blocks)
+constexpr int kSharedThreads = 512;  // decode workgroup: eight waves
+constexpr int kPrivateRows = 16;     // query rows of a private (one-wave) item
+constexpr int kSharedRows = 256;     // query rows of a shared (one-workgroup) item: 8 waves x 32
+constexpr int kRowsPerItem = 32;     // the GQA group must divide this
 constexpr int kMaxPagesPerItem = 64; // a wave keeps its item's page table one page per lane
 
-// One wave's work: a run of KV pages of one KV head applied to up to 32
-// query rows (nreq requests x G query heads).  Same layout as cap_work_item.
+// A run of KV pages of one KV head applied to nreq requests x G query heads:
+// up to 16 rows for a private item (one wave), up to 256 for a shared item
+// (one workgroup).  Same layout as cap_work_item.
 struct WorkItem {
     int32_t stream_off;
     int32_t npages;
@@ -28,7 +31,8 @@ struct WorkItem {
 static_assert(sizeof(WorkItem) == sizeof(cap_work_item), "work item layout");
 
 struct DecodeArgs {
-    const WorkItem *items;
+    const WorkItem *shared_items;  // one workgroup each
+    const WorkItem *items;         // private: one wave each
     const int32_t *stream;       // page-stream entries: (tree page index << 5) | (ntok - 1)
     const int32_t *tree_pages;   // tree page index -> physical page
     const int32_t *rows;         // request ids of each item's request list
@@ -38,6 +42,7 @@ struct DecodeArgs {
     float *part_o;               // [slots][D]
     float *part_m;               // [slots]
     float *part_l;               // [slots]
+    int32_t n_shared;
     int32_t n_items;
     int32_t Hq, Hkv, G;
     float scale_log2;            // sm_scale * log2(e)
@@ -54,11 +59,7 @@ struct MergeArgs {
 };
 
 // Kernel launchers (cap_kernels.hip); return the hipError_t as int.
-// Decode kernel variants (rows per wave / KV buffers / waves per SIMD):
-// 1: 32 / 3 / 1, 2: 32 / 2 / 2, 3: 16 / 3 / 1, 4: 16 / 2 / 2.
-int launch_decode(const DecodeArgs &a, int head_dim, int variant, void *stream);
-int variant_rows(int variant);
-int default_variant();
+int launch_decode(const DecodeArgs &a, int head_dim, void *stream);
 int launch_merge(const MergeArgs &a, int head_dim, void *stream);
 int launch_fill(void *buf, size_t words, uint32_t value, void *stream);
 int launch_read(const void *buf, size_t vec16, void *sink, void *stream);

@@ -135,12 +135,8 @@ __device__ __forceinline__ void mask_v(u32x4 (&v)[D / 16], int nt0, int nt1, int
 // max over the four lanes n, n+16, n+32, n+48 that hold one query row
 __device__ __forceinline__ float row_max4(float v)
 {
-    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v),
-                                                    __builtin_bit_cast(uint32_t, v), false, false);
-    v = fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
-    const auto q = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v),
-                                                    __builtin_bit_cast(uint32_t, v), false, false);
-    return fmaxf(__builtin_bit_cast(float, q[0]), __builtin_bit_cast(float, q[1]));
+    v = fmaxf(v, __shfl_xor(v, 16));
+    return fmaxf(v, __shfl_xor(v, 32));
 }
 
 template <int D, int RB>
@@ -205,28 +201,16 @@ __device__ __forceinline__ void compute_step(Step<D> &f, const u32x4 (&qf)[RB][D
     }
 }
 
-// RB: 16-row MFMA blocks a wave holds (rows per item <= 16 RB).
-// NBUF: register buffers of the KV pipeline (NBUF-1 steps in flight).
-// WPE: waves per SIMD the register budget is sized for.
-template <int D, int RB, int NBUF, int WPE>
-__global__ __launch_bounds__(kWaveSize * kWavesPerBlock) __attribute__((amdgpu_waves_per_eu(WPE)))
-void decode_kernel(DecodeArgs a)
+// Q fragments (B operand of QK) for rows row0 + 16b + n of an item: lane
+// (n, c) holds dims 8(4i+c)..+7.  Rows past nrows are zero.
+template <int D, int RB>
+__device__ __forceinline__ void load_q(u32x4 (&qf)[RB][D / 32], const DecodeArgs &a, const WorkItem &it,
+                                       int row0, int nrows, int n, int c)
 {
-    static_assert(NBUF == 2 || NBUF == 3, "two or three KV buffers");
-    const int lane = threadIdx.x & (kWaveSize - 1);
-    const int n = lane & 15, c = lane >> 4;
-    const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6));
-    if (wid >= a.n_items) return;
-    const WorkItem it = a.items[wid];
     const int G = a.G;
-    const int nrows = it.nreq * G;
-    const int nblk = (nrows + 15) >> 4;
-
-    // Q fragments (B operand of QK): lane (n, c) holds row 16b+n, dims 8(4i+c)..+7.
-    u32x4 qf[RB][D / 32];
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
-        const int row = 16 * b + n;
+        const int row = row0 + 16 * b + n;
         if (row < nrows) {
             const int req = a.rows[it.row_off + row / G];
             const int h = it.head * G + row % G;
@@ -238,64 +222,23 @@ void decode_kernel(DecodeArgs a)
             for (int i = 0; i < D / 32; ++i) qf[b][i] = u32x4{0, 0, 0, 0};
         }
     }
+}
 
-    f32x4 o[RB][D / 16];
-#pragma unroll
-    for (int b = 0; b < RB; ++b)
-#pragma unroll
-        for (int j = 0; j < D / 16; ++j) o[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_ref[RB], l_run[RB];
-#pragma unroll
-    for (int b = 0; b < RB; ++b) {
-        m_ref[b] = -INFINITY;
-        l_run[b] = 0.f;
-    }
-
-    // Page table of the item, one page per lane (items hold at most 64 pages).
-    int lane_pid = 0, lane_nt = 0;
-    if (lane < it.npages) {
-        const int e = a.stream[it.stream_off + lane];
-        lane_pid = a.tree_pages[e >> 5];
-        lane_nt = (e & 31) + 1;
-    }
-
-    const int nsteps = (it.npages + 1) >> 1;
-    const float sc = a.scale_log2;
-    Step<D> fa, fb;
-    load_step<D>(fa, a, it.head, it.npages, 0, lane_pid, lane_nt, n, c);
-    if constexpr (NBUF == 2) {
-        // one step in flight while one computes
-        for (int s = 0; s < nsteps; s += 2) {
-            load_step<D>(fb, a, it.head, it.npages, s + 1, lane_pid, lane_nt, n, c);
-            compute_step<D, RB>(fa, qf, o, m_ref, l_run, nblk, sc, c);
-            if (s + 1 >= nsteps) break;
-            load_step<D>(fa, a, it.head, it.npages, s + 2, lane_pid, lane_nt, n, c);
-            compute_step<D, RB>(fb, qf, o, m_ref, l_run, nblk, sc, c);
-        }
-    } else {
-        // two steps in flight while one computes
-        Step<D> fc;
-        load_step<D>(fb, a, it.head, it.npages, 1, lane_pid, lane_nt, n, c);
-        for (int s = 0; s < nsteps; s += 3) {
-            load_step<D>(fc, a, it.head, it.npages, s + 2, lane_pid, lane_nt, n, c);
-            compute_step<D, RB>(fa, qf, o, m_ref, l_run, nblk, sc, c);
-            if (s + 1 >= nsteps) break;
-            load_step<D>(fa, a, it.head, it.npages, s + 3, lane_pid, lane_nt, n, c);
-            compute_step<D, RB>(fb, qf, o, m_ref, l_run, nblk, sc, c);
-            if (s + 2 >= nsteps) break;
-            load_step<D>(fb, a, it.head, it.npages, s + 4, lane_pid, lane_nt, n, c);
-            compute_step<D, RB>(fc, qf, o, m_ref, l_run, nblk, sc, c);
-        }
-    }
-
-    // Partials: slot = (slot_base + row / G) * Hq + head * G + row % G.
+// Partials of rows row0 + 16b + n: slot = (slot_base + row / G) * Hq + head * G + row % G.
+template <int D, int RB>
+__device__ __forceinline__ void write_partials(const DecodeArgs &a, const WorkItem &it, int row0, int nrows,
+                                               int nblk, const f32x4 (&o)[RB][D / 16],
+                                               const float (&m_ref)[RB], const float (&l_run)[RB], int n,
+                                               int c)
+{
+    const int G = a.G;
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
         if (b >= nblk) break;
         float l = l_run[b];
         l += __shfl_xor(l, 16);
         l += __shfl_xor(l, 32);
-        const int row = 16 * b + n;
+        const int row = row0 + 16 * b + n;
         if (row < nrows) {
             const int64_t slot = (int64_t)(it.slot_base + row / G) * a.Hq + it.head * G + row % G;
             float *po = a.part_o + slot * D + 4 * c;
@@ -307,6 +250,200 @@ void decode_kernel(DecodeArgs a)
             }
         }
     }
+}
+
+// Page table of an item, one page per lane (items hold at most 64 pages).
+__device__ __forceinline__ void load_page_table(const DecodeArgs &a, const WorkItem &it, int lane,
+                                                int &lane_pid, int &lane_nt)
+{
+    lane_pid = 0;
+    lane_nt = 0;
+    if (lane < it.npages) {
+        const int e = a.stream[it.stream_off + lane];
+        lane_pid = a.tree_pages[e >> 5];
+        lane_nt = (e & 31) + 1;
+    }
+}
+
+// ---------------------------------------------------------------- private path
+// One wave, one item of at most 16 rows; its KV fragments come straight from
+// HBM into registers, one 2-page step in flight while the previous computes.
+template <int D>
+__device__ __forceinline__ void private_item(const DecodeArgs &a, const WorkItem &it, int lane, int n, int c)
+{
+    const int nrows = it.nreq * a.G;
+    u32x4 qf[1][D / 32];
+    load_q<D, 1>(qf, a, it, 0, nrows, n, c);
+    f32x4 o[1][D / 16];
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) o[0][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_ref[1] = {-INFINITY}, l_run[1] = {0.f};
+    int lane_pid, lane_nt;
+    load_page_table(a, it, lane, lane_pid, lane_nt);
+
+    const int nsteps = (it.npages + 1) >> 1;
+    const float sc = a.scale_log2;
+    Step<D> fa, fb;
+    load_step<D>(fa, a, it.head, it.npages, 0, lane_pid, lane_nt, n, c);
+    for (int s = 0; s < nsteps; s += 2) {
+        load_step<D>(fb, a, it.head, it.npages, s + 1, lane_pid, lane_nt, n, c);
+        compute_step<D, 1>(fa, qf, o, m_ref, l_run, 1, sc, c);
+        if (s + 1 >= nsteps) break;
+        load_step<D>(fa, a, it.head, it.npages, s + 2, lane_pid, lane_nt, n, c);
+        compute_step<D, 1>(fb, qf, o, m_ref, l_run, 1, sc, c);
+    }
+    write_partials<D, 1>(a, it, 0, nrows, 1, o, m_ref, l_run, n, c);
+}
+
+// ----------------------------------------------------------------- shared path
+// One workgroup, one item of up to 256 rows (nreq x G).  The eight waves
+// stream each 2-page step of KV once, cooperatively (128-bit loads, D/64 per
+// thread per step, four steps in flight in registers), stage it in a
+// double-buffered LDS tile, and each wave applies the tile to its own 32
+// rows.  One barrier per step.
+template <int D>
+struct Stage {
+    u32x4 x[D / 64];
+};
+
+template <int D>
+__device__ __forceinline__ void issue_stage(Stage<D> &st, const DecodeArgs &a, int head, int npages, int s,
+                                            int lane_pid, int tid)
+{
+    const int64_t blk = (int64_t)kPage * D;
+    const int nsteps = (npages + 1) >> 1;
+    const int ss = s < nsteps ? s : nsteps - 1;
+    const int i0 = 2 * ss;
+    const int i1 = i0 + 1 < npages ? i0 + 1 : i0;
+    const int64_t p0 = __builtin_amdgcn_readlane(lane_pid, i0);
+    const int64_t p1 = __builtin_amdgcn_readlane(lane_pid, i1);
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) {
+        const int p = tid + k * kSharedThreads;     // 16-byte piece of the 4-block stage
+        const int b = p / (2 * D);                  // 0 K page0, 1 K page1, 2 V page0, 3 V page1 (wave-uniform)
+        const int64_t page = (b & 1) ? p1 : p0;
+        const uint16_t *pool = (b & 2) ? a.v_pool : a.k_pool;
+        st.x[k] = ld16(pool + (page * a.Hkv + head) * blk + (p % (2 * D)) * 8);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void write_stage(const Stage<D> &st, uint16_t *slot, int tid)
+{
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k)
+        *reinterpret_cast<u32x4 *>(slot + (tid + k * kSharedThreads) * 8) = st.x[k];
+}
+
+// MFMA fragments of one step from an LDS tile laid out as the four page blocks.
+template <int D>
+__device__ __forceinline__ void lds_step(Step<D> &f, const uint16_t *slot, int npages, int s, int lane_nt,
+                                         int n, int c)
+{
+    const int blk = kPage * D;
+    const int i0 = 2 * s;
+    const bool has1 = i0 + 1 < npages;
+    f.nt0 = __builtin_amdgcn_readlane(lane_nt, i0);
+    f.nt1 = has1 ? __builtin_amdgcn_readlane(lane_nt, i0 + 1) : 0;
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+        f.k0[i] = *reinterpret_cast<const u32x4 *>(slot + ((4 * i + c) * kPage + n) * 8);
+        f.k1[i] = *reinterpret_cast<const u32x4 *>(slot + blk + ((4 * i + c) * kPage + n) * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) {
+        const u32x2 x0 = *reinterpret_cast<const u32x2 *>(slot + 2 * blk + (16 * j + n) * kPage + 4 * c);
+        const u32x2 x1 = *reinterpret_cast<const u32x2 *>(slot + 3 * blk + (16 * j + n) * kPage + 4 * c);
+        f.v[j] = u32x4{x0.x, x0.y, x1.x, x1.y};
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void shared_item(const DecodeArgs &a, const WorkItem &it, uint16_t *lds, int tid,
+                                            int lane, int n, int c)
+{
+    const int wave = tid >> 6;
+    const int nrows = it.nreq * a.G;
+    const int row0 = 32 * wave;
+    const int nblk = nrows > row0 ? min(2, (nrows - row0 + 15) >> 4) : 0;
+    u32x4 qf[2][D / 32];
+    load_q<D, 2>(qf, a, it, row0, nrows, n, c);
+    f32x4 o[2][D / 16];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) o[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_ref[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+    int lane_pid, lane_nt;
+    load_page_table(a, it, lane, lane_pid, lane_nt);
+
+    const int nsteps = (it.npages + 1) >> 1;
+    const float sc = a.scale_log2;
+    uint16_t *slot0 = lds, *slot1 = lds + 4 * kPage * D;
+    const int h = it.head, np = it.npages;
+    Step<D> f;
+    Stage<D> r0, r1, r2, r3;                        // stage q lives in r[q % 4] until written to LDS
+    issue_stage<D>(r0, a, h, np, 0, lane_pid, tid);
+    issue_stage<D>(r1, a, h, np, 1, lane_pid, tid);
+    issue_stage<D>(r2, a, h, np, 2, lane_pid, tid);
+    issue_stage<D>(r3, a, h, np, 3, lane_pid, tid);
+    write_stage<D>(r0, slot0, tid);
+    __syncthreads();
+    issue_stage<D>(r0, a, h, np, 4, lane_pid, tid);
+    for (int s = 0; s < nsteps; s += 4) {
+        if (nblk) {
+            lds_step<D>(f, slot0, np, s, lane_nt, n, c);
+            compute_step<D, 2>(f, qf, o, m_ref, l_run, nblk, sc, c);
+        }
+        write_stage<D>(r1, slot1, tid);
+        issue_stage<D>(r1, a, h, np, s + 5, lane_pid, tid);
+        __syncthreads();
+        if (s + 1 >= nsteps) break;
+        if (nblk) {
+            lds_step<D>(f, slot1, np, s + 1, lane_nt, n, c);
+            compute_step<D, 2>(f, qf, o, m_ref, l_run, nblk, sc, c);
+        }
+        write_stage<D>(r2, slot0, tid);
+        issue_stage<D>(r2, a, h, np, s + 6, lane_pid, tid);
+        __syncthreads();
+        if (s + 2 >= nsteps) break;
+        if (nblk) {
+            lds_step<D>(f, slot0, np, s + 2, lane_nt, n, c);
+            compute_step<D, 2>(f, qf, o, m_ref, l_run, nblk, sc, c);
+        }
+        write_stage<D>(r3, slot1, tid);
+        issue_stage<D>(r3, a, h, np, s + 7, lane_pid, tid);
+        __syncthreads();
+        if (s + 3 >= nsteps) break;
+        if (nblk) {
+            lds_step<D>(f, slot1, np, s + 3, lane_nt, n, c);
+            compute_step<D, 2>(f, qf, o, m_ref, l_run, nblk, sc, c);
+        }
+        write_stage<D>(r0, slot0, tid);
+        issue_stage<D>(r0, a, h, np, s + 8, lane_pid, tid);
+        __syncthreads();
+    }
+    write_partials<D, 2>(a, it, row0, nrows, nblk, o, m_ref, l_run, n, c);
+}
+
+// Workgroups [0, n_shared) run one shared item each; the rest run eight
+// private items each (one per wave).
+template <int D>
+__global__ __launch_bounds__(kSharedThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_kernel(DecodeArgs a)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 4 * kPage * D];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWaveSize - 1);
+    const int n = lane & 15, c = lane >> 4;
+    const int bid = blockIdx.x;
+    if (bid < a.n_shared) {
+        shared_item<D>(a, a.shared_items[bid], lds, tid, lane, n, c);
+        return;
+    }
+    const int wi = __builtin_amdgcn_readfirstlane((bid - a.n_shared) * (kSharedThreads / kWaveSize) + (tid >> 6));
+    if (wi >= a.n_items) return;
+    private_item<D>(a, a.items[wi], lane, n, c);
 }
 
 // One wave per (request, query head): out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i.
@@ -432,36 +569,18 @@ __global__ __launch_bounds__(256) void copy_kernel(u32x4 *dst, const u32x4 *src,
 
 }  // namespace
 
-template <int D>
-static void launch_variant(int variant, dim3 grid, dim3 block, hipStream_t s, const DecodeArgs &a)
+int launch_decode(const DecodeArgs &a, int head_dim, void *stream)
 {
-    switch (variant) {
-    case 1: hipLaunchKernelGGL((decode_kernel<D, 2, 3, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<D, 2, 2, 2>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((decode_kernel<D, 1, 3, 1>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((decode_kernel<D, 1, 2, 2>), grid, block, 0, s, a); break;
-    }
-}
-
-int launch_decode(const DecodeArgs &a, int head_dim, int variant, void *stream)
-{
-    if (a.n_items <= 0) return 0;
-    const dim3 grid((a.n_items + kWavesPerBlock - 1) / kWavesPerBlock);
-    const dim3 block(kWaveSize * kWavesPerBlock);
+    const int private_wg = (a.n_items + kSharedThreads / kWaveSize - 1) / (kSharedThreads / kWaveSize);
+    const int nwg = a.n_shared + private_wg;
+    if (nwg <= 0) return 0;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (head_dim == 128)
-        launch_variant<128>(variant, grid, block, s, a);
+        hipLaunchKernelGGL(decode_kernel<128>, dim3(nwg), dim3(kSharedThreads), 0, s, a);
     else
-        launch_variant<64>(variant, grid, block, s, a);
+        hipLaunchKernelGGL(decode_kernel<64>, dim3(nwg), dim3(kSharedThreads), 0, s, a);
     return (int)hipGetLastError();
 }
-
-int variant_rows(int variant)
-{
-    return (variant == 1 || variant == 2) ? 32 : 16;
-}
-
-int default_variant() { return 4; }
 
 int launch_merge(const MergeArgs &a, int head_dim, void *stream)
 {

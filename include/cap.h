@@ -110,22 +110,22 @@ typedef struct cap_plan_opts {
                                  every non-empty node, 2 auto (same as -1) */
     int32_t split_pages;      /* 0 auto; else the most KV pages one work item streams
                                  (values above 64 are treated as 64) */
-    int32_t max_rows;         /* 0 auto (the kernel variant's rows per wave); query rows
-                                 per work item: 16 or 32, at most the variant's */
+    int32_t shared_rows;      /* 0 = 32: request groups with more query rows than this
+                                 (requests x G) are served by shared workgroup items of
+                                 up to 256 rows; the others by one-wave private items of
+                                 up to 16 rows.  G > 16 always uses shared items */
     int32_t num_cus;          /* 0 = 256 (MI355X); used by the cost model */
-    int32_t waves_per_cu;     /* 0 = 4; resident work items per CU in the cost model */
+    int32_t waves_per_cu;     /* 0 = 8; resident waves per CU in the cost model */
     float rounds;             /* 0 = 2.0; target work-item rounds per resident slot */
     float share_margin;       /* 0 = 1.0; share a node only if saved bytes exceed
                                  margin x added partial bytes */
-    int32_t kernel_variant;   /* 0 auto; 1..4 pick a decode-kernel build: query rows per
-                                 wave / KV register buffers / waves per SIMD =
-                                 1: 32/3/1, 2: 32/2/2, 3: 16/3/1, 4: 16/2/2 */
-    int32_t reserved[3];
+    int32_t reserved[4];
 } cap_plan_opts;
 
 /* Plan summary (host-side numbers; bytes are per decode step). */
 typedef struct cap_plan_stats {
-    int64_t num_items;            /* work items (one wavefront each) */
+    int64_t num_items;            /* private work items (one wavefront each) */
+    int64_t num_shared_items;     /* shared work items (one 8-wave workgroup each) */
     int64_t num_tasks;            /* (page run, request group) pairs; items = tasks x Hkv */
     int64_t num_groups;           /* request groups after share/fold decisions */
     int64_t partial_rows;         /* partial slots = partial_rows x Hq */
@@ -144,10 +144,12 @@ typedef struct cap_plan_stats {
 typedef struct cap_tree cap_tree;   /* opaque host handles */
 typedef struct cap_plan cap_plan;
 
-/* Work item as stored in the plan (exposed for inspection and tests). */
+/* Work item as stored in the plan (exposed for inspection and tests).  A
+ * private item is one wavefront and serves up to 16 query rows; a shared item
+ * is one 8-wave workgroup and serves up to 256. */
 typedef struct cap_work_item {
     int32_t stream_off;   /* first entry of its page run in the plan's page stream */
-    int32_t npages;       /* pages in the run (>= 1) */
+    int32_t npages;       /* pages in the run (1..64) */
     int32_t head;         /* KV head */
     int32_t row_off;      /* first entry of its request list in the plan's row table */
     int32_t nreq;         /* requests served; query rows = nreq x G */
@@ -160,6 +162,7 @@ typedef struct cap_work_item {
  *   (slot_base + i/G) * Hq + head*G + i%G.
  * Request r's partial rows: merge_rows[merge_off[r] .. merge_off[r+1]). */
 typedef struct cap_plan_view {
+    int32_t num_shared_items;  const cap_work_item *shared_items;
     int32_t num_items;         const cap_work_item *items;
     int32_t stream_len;        const int32_t *stream;
     int32_t rows_len;          const int32_t *rows;

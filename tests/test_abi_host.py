@@ -81,8 +81,8 @@ def test_tree_validation_errors():
 def test_planner_rejects_bad_options():
     h = cap.cap_tree_upload(small_tree())
     try:
-        for kw in ({"share_mode": 5}, {"max_rows": 24}, {"split_pages": -1}, {"rounds": -1.0},
-                   {"kernel_variant": 7}, {"max_rows": 32, "kernel_variant": 4}):
+        for kw in ({"share_mode": 5}, {"shared_rows": -3}, {"split_pages": -1}, {"rounds": -1.0},
+                   {"share_margin": -1.0}):
             with pytest.raises(cap.CapError) as e:
                 cap.cap_plan_step(h, **kw)
             assert e.value.status == 1
@@ -105,7 +105,7 @@ def test_plan_upload_needs_device_tree():
         cap.cap_tree_free(h)
 
 
-def check_coverage(tree, plan_handle, max_rows=32):
+def check_coverage(tree, plan_handle):
     """Every (request, KV head) sees exactly its context tokens once; every
     partial slot is written by exactly one item row; merge lists match."""
     v = cap.cap_plan_get_view(plan_handle)
@@ -125,15 +125,16 @@ def check_coverage(tree, plan_handle, max_rows=32):
     got = {(r, h): [] for r in range(R) for h in range(Hkv)}
     slot_writes = np.zeros(int(st["partial_rows"]) * Hq, np.int64)
     slot_rows_of = {r: set() for r in range(R)}
-    for so, npg, head, ro, nreq, sb in v["items"]:
-        assert 1 <= npg <= 64 and 0 <= head < Hkv and 1 <= nreq and nreq * G <= max_rows
-        ents = v["stream"][so:so + npg]
-        pages = [(int(e) >> 5, (int(e) & 31) + 1) for e in ents]
-        for qpos, r in enumerate(v["rows"][ro:ro + nreq]):
-            got[(int(r), int(head))].extend(pages)
-            for i in range(G):
-                slot_writes[(sb + qpos) * Hq + head * G + i] += 1
-            slot_rows_of[int(r)].add(int(sb + qpos))
+    for items, max_rows in ((v["items"], 16), (v["shared_items"], 256)):
+        for so, npg, head, ro, nreq, sb in items:
+            assert 1 <= npg <= 64 and 0 <= head < Hkv and 1 <= nreq and nreq * G <= max_rows
+            ents = v["stream"][so:so + npg]
+            pages = [(int(e) >> 5, (int(e) & 31) + 1) for e in ents]
+            for qpos, r in enumerate(v["rows"][ro:ro + nreq]):
+                got[(int(r), int(head))].extend(pages)
+                for i in range(G):
+                    slot_writes[(sb + qpos) * Hq + head * G + i] += 1
+                slot_rows_of[int(r)].add(int(sb + qpos))
     for (r, h), s in got.items():
         assert sorted(s) == want[r], f"request {r} head {h}"
     assert np.all(slot_writes == 1)
@@ -142,6 +143,9 @@ def check_coverage(tree, plan_handle, max_rows=32):
         assert len(set(ml.tolist())) == len(ml)
         assert set(ml.tolist()) == slot_rows_of[r]
     assert st["num_items"] == len(v["items"])
+    assert st["num_shared_items"] == len(v["shared_items"])
+    if G > 16:
+        assert len(v["items"]) == 0
     return st
 
 
@@ -150,21 +154,19 @@ def check_coverage(tree, plan_handle, max_rows=32):
 def test_planner_coverage_random_trees(share_mode, split_pages):
     for seed in range(8):
         rng = np.random.default_rng(seed)
-        Hq, Hkv = [(8, 2), (32, 8), (16, 1), (4, 4)][seed % 4]
-        nt, par, paths = wl.make_random_tree(rng, num_requests=int(rng.integers(1, 20)), max_depth=4,
+        Hq, Hkv = [(8, 2), (32, 8), (32, 1), (4, 4)][seed % 4]
+        nt, par, paths = wl.make_random_tree(rng, num_requests=int(rng.integers(1, 80)), max_depth=4,
                                              max_len=90, num_q_heads=Hq, num_kv_heads=Hkv,
                                              head_dim=64, internal_end_prob=0.3,
                                              empty_root=bool(seed % 2), min_len=0)
         t = wl.tree_from_lengths(nt, par, paths, Hq, Hkv, 64, page_perm_rng=rng)
         h = cap.cap_tree_upload(t)
         try:
-            for max_rows, variant in ((16, 4), (16, 3), (32, 1), (32, 2)):
-                if Hq // Hkv > max_rows:
-                    continue
+            for shared_rows in (0, 1, 8, 1 << 30):
                 p = cap.cap_plan_step(h, share_mode=share_mode, split_pages=split_pages,
-                                      max_rows=max_rows, kernel_variant=variant)
+                                      shared_rows=shared_rows)
                 try:
-                    check_coverage(t, p, max_rows)
+                    check_coverage(t, p)
                 finally:
                     cap.cap_plan_free(p)
         finally:
@@ -179,8 +181,7 @@ def test_planner_coverage_configs(cfg):
     h = cap.cap_tree_upload(t)
     try:
         for mode in (-1, 0, 1):
-            p = cap.cap_plan_step(h, share_mode=mode,
-                                  kernel_variant=1 if Hq // Hkv > 16 else 0)
+            p = cap.cap_plan_step(h, share_mode=mode)
             try:
                 st = check_coverage(t, p)
                 stats = wl.tree_stats(t)

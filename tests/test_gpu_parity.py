@@ -64,9 +64,9 @@ def test_config0_all_plan_variants():
     w, ref = config_case(0)
     for mode in (-1, 0, 1):
         for split in (0, 1, 3, 100):
-            for variant in (1, 2, 3, 4):
-                out, _, _ = run_gpu(w, share_mode=mode, split_pages=split, kernel_variant=variant)
-                check(out, ref, f"cfg0 mode={mode} split={split} variant={variant}")
+            for shared_rows in (0, 1, 1 << 30):
+                out, _, _ = run_gpu(w, share_mode=mode, split_pages=split, shared_rows=shared_rows)
+                check(out, ref, f"cfg0 mode={mode} split={split} shared_rows={shared_rows}")
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4])
@@ -89,11 +89,12 @@ def test_full_configs_forced_modes(cfg, mode):
     check(out, ref, f"cfg{cfg} mode={mode}")
 
 
-@pytest.mark.parametrize("variant", [1, 2, 3, 4])
-def test_kernel_variants_full_config(variant):
+@pytest.mark.parametrize("shared_rows", [1, 1 << 30])
+def test_shared_and_private_paths_full_config(shared_rows):
+    """Every group on shared workgroups, or every group on private waves."""
     w, ref = config_case(3)
-    out, _, _ = run_gpu(w, kernel_variant=variant)
-    check(out, ref, f"cfg3 variant={variant}")
+    out, _, _ = run_gpu(w, shared_rows=shared_rows, split_pages=24)
+    check(out, ref, f"cfg3 shared_rows={shared_rows}")
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -102,17 +103,15 @@ def test_random_small_trees(D, HqHkv):
     Hq, Hkv = HqHkv
     for seed in range(4):
         rng = np.random.default_rng([seed, D, Hq, Hkv])
-        nt, par, paths = wl.make_random_tree(rng, num_requests=int(rng.integers(1, 24)), max_depth=4,
+        nt, par, paths = wl.make_random_tree(rng, num_requests=int(rng.integers(1, 90)), max_depth=4,
                                              max_len=100, num_q_heads=Hq, num_kv_heads=Hkv,
                                              head_dim=D, internal_end_prob=0.3,
                                              empty_root=bool(seed % 2), min_len=0)
         w = wl.make_workload(nt, par, paths, Hq, Hkv, D, rng, extra_pool_pages=5)
         ref = oracle.decode(w.tree, w.q, w.k_pool, w.v_pool)
-        big = Hq // Hkv > 16
-        for opts in ({"kernel_variant": 1 if big else 0},
-                     {"share_mode": 1, "split_pages": 1, "kernel_variant": 2 if big else 3},
-                     {"share_mode": 0, "kernel_variant": 1},
-                     {"split_pages": 2, "kernel_variant": 2}):
+        for opts in ({}, {"share_mode": 1, "split_pages": 1, "shared_rows": 1},
+                     {"share_mode": 0, "shared_rows": 1 << 30},
+                     {"split_pages": 3, "shared_rows": 1}, {"split_pages": 2}):
             out, _, _ = run_gpu(w, **opts)
             check(out, ref, f"seed={seed} D={D} Hq={Hq} Hkv={Hkv} {opts}")
 
@@ -124,7 +123,7 @@ def test_large_logits_and_single_token_requests():
     q = rng.standard_normal((5, 16, 128)).astype(np.float32) * 4
     w = wl.make_workload(nt, par, paths, 16, 4, 128, rng, q_values=q)
     ref = oracle.decode(w.tree, w.q, w.k_pool, w.v_pool)
-    for opts in ({}, {"share_mode": 1, "split_pages": 1}, {"kernel_variant": 1}):
+    for opts in ({}, {"share_mode": 1, "split_pages": 1}, {"shared_rows": 1}):
         out, _, _ = run_gpu(w, **opts)
         check(out, ref, f"stretched {opts}")
 
