@@ -52,7 +52,7 @@ class TreeDesc(ctypes.Structure):
 class PlanOpts(ctypes.Structure):
     _fields_ = [("share_mode", ctypes.c_int32), ("split_pages", ctypes.c_int32),
                 ("shared_rows", ctypes.c_int32), ("num_cus", ctypes.c_int32),
-                ("waves_per_cu", ctypes.c_int32), ("rounds", ctypes.c_float),
+                ("shared_cost", ctypes.c_float), ("rounds", ctypes.c_float),
                 ("share_margin", ctypes.c_float), ("reserved", ctypes.c_int32 * 4)]
 
 
@@ -67,12 +67,11 @@ class PlanStats(ctypes.Structure):
 
 class WorkItemC(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("stream_off", "npages", "head", "row_off", "nreq", "slot_base")]
+                ("stream_off", "npages", "head", "row_off", "nreq", "slot_base", "mode", "reserved")]
 
 
 class PlanView(ctypes.Structure):
-    _fields_ = [("num_shared_items", ctypes.c_int32), ("shared_items", ctypes.POINTER(WorkItemC)),
-                ("num_items", ctypes.c_int32), ("items", ctypes.POINTER(WorkItemC)),
+    _fields_ = [("num_items", ctypes.c_int32), ("items", ctypes.POINTER(WorkItemC)),
                 ("stream_len", ctypes.c_int32), ("stream", ctypes.POINTER(ctypes.c_int32)),
                 ("rows_len", ctypes.c_int32), ("rows", ctypes.POINTER(ctypes.c_int32)),
                 ("num_requests", ctypes.c_int32), ("merge_off", ctypes.POINTER(ctypes.c_int32)),
@@ -200,7 +199,7 @@ def cap_plan_get_stats(plan: int) -> dict:
 
 
 def cap_plan_get_view(plan: int) -> dict:
-    """Copies of the plan's host arrays (items as an int32 [n][6] array)."""
+    """Copies of the plan's host arrays (items as an int32 [n][8] array)."""
     v = PlanView()
     _check(lib().cap_plan_get_view(ctypes.c_void_p(plan), ctypes.byref(v)))
 
@@ -210,8 +209,7 @@ def cap_plan_get_view(plan: int) -> dict:
         a = np.ctypeslib.as_array(ctypes.cast(ptr, ctypes.POINTER(ctypes.c_int32)), (n * width,))
         return a.copy().reshape((n, width) if width > 1 else (n,))
 
-    return {"items": arr(v.items, v.num_items, 6),
-            "shared_items": arr(v.shared_items, v.num_shared_items, 6),
+    return {"items": arr(v.items, v.num_items, 8),
             "stream": arr(v.stream, v.stream_len),
             "rows": arr(v.rows, v.rows_len),
             "merge_off": arr(v.merge_off, v.num_requests + 1),

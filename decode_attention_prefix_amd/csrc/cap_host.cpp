@@ -75,13 +75,12 @@ struct cap_tree {
 struct cap_plan {
     const cap_tree *tree = nullptr;
     cap_plan_stats stats{};
-    std::vector<WorkItem> shared_items;   // one workgroup each
-    std::vector<WorkItem> items;          // private: one wave each
+    std::vector<WorkItem> items;          // one workgroup each
     std::vector<int32_t> stream;      // (tree page index << 5) | (ntok - 1)
     std::vector<int32_t> rows;        // request ids
     std::vector<int32_t> merge_off, merge_rows;
     // device image
-    size_t off_shared = 0, off_items = 0, off_stream = 0, off_rows = 0, off_moff = 0, off_mrows = 0, dev_bytes = 0;
+    size_t off_items = 0, off_stream = 0, off_rows = 0, off_moff = 0, off_mrows = 0, dev_bytes = 0;
     std::vector<unsigned char> host_image;
     void *dev = nullptr;
 };
@@ -216,7 +215,8 @@ struct Planner {
     int D, Hkv, G;
     int64_t head_tok_bytes;        // K+V bytes per token per KV head
     int64_t partial_row_bytes;     // partial bytes per query row (o, m, l)
-    int target_pages = 0;
+    double unit = 0;               // target cost of one work item (cost units)
+    int max_pages = 0;             // largest page run of any item
     std::vector<Group> groups;
 
     Planner(const cap_tree &tree, const cap_plan_opts &opts) : t(tree), o(opts)
@@ -249,11 +249,26 @@ struct Planner {
         return is_shared(nreq) ? cap::kSharedRows / G : cap::kPrivateRows / G;
     }
 
-    int64_t estimate_chunks(int64_t pages) const
+    // Cost of streaming `pages` pages for one item, in private-page units: a
+    // shared item also runs the MFMA/softmax work of up to 256 rows, which
+    // makes its pages dearer (o.shared_cost).
+    double page_cost(bool shared) const { return shared ? (double)o.shared_cost : 1.0; }
+
+    // Page runs of `pages` pages for a group, split so each item costs about
+    // `unit` and fits the kernel's page-table limits.
+    int64_t chunks(int64_t pages, bool shared) const
     {
-        const int tp = target_pages > 0 ? target_pages : 16;
-        return std::max<int64_t>(1, (pages + tp - 1) / tp);
+        const int64_t cap = shared ? cap::kMaxSharedPages : cap::kMaxPrivatePages;
+        int64_t k = (pages + cap - 1) / cap;
+        if (o.split_pages > 0) {
+            k = std::max<int64_t>(k, (pages + o.split_pages - 1) / o.split_pages);
+        } else if (unit > 0) {
+            k = std::max<int64_t>(k, (int64_t)std::ceil(pages * page_cost(shared) / unit));
+        }
+        return std::max<int64_t>(1, std::min<int64_t>(k, pages));
     }
+
+    int64_t estimate_chunks(int64_t pages) const { return chunks(pages, true); }
 
     bool decide_share(int n, int64_t prefix_tokens) const
     {
@@ -295,25 +310,20 @@ struct Planner {
 
     void build_groups()
     {
-        // first pass with a provisional chunk size, then refine the target
-        // using the resulting work volume and plan again
+        // first pass with a provisional item size, then size items so that
+        // the total cost fills every CU about `rounds` times, and plan again
+        // (the share/fold test depends on the split)
         for (int pass = 0; pass < 2; ++pass) {
             groups.clear();
             for (int n = 0; n < t.N; ++n)
                 if (t.parent[n] == -1) walk(n, {}, 0);
-            int64_t W = 0;   // item-pages if nothing were split
+            double W = 0;   // total cost if nothing were split
             for (const Group &g : groups) {
                 const int64_t nreq = (int64_t)g.reqs.size();
                 const int64_t rg = (nreq + reqs_per_item(nreq) - 1) / reqs_per_item(nreq);
-                W += (int64_t)g.entries.size() * rg * Hkv;
+                W += (double)g.entries.size() * rg * Hkv * page_cost(is_shared(nreq));
             }
-            if (o.split_pages > 0) {
-                target_pages = std::min(o.split_pages, cap::kMaxPagesPerItem);
-                break;
-            }
-            const double slots = (double)o.num_cus * o.waves_per_cu * o.rounds;
-            target_pages = (int)std::max<int64_t>(4, (int64_t)std::ceil((double)W / slots));
-            target_pages = std::min(target_pages, cap::kMaxPagesPerItem);
+            unit = std::max(4.0, W / ((double)o.num_cus * o.rounds));
         }
     }
 };
@@ -321,9 +331,9 @@ struct Planner {
 void fill_defaults(cap_plan_opts &o)
 {
     if (o.share_mode == 2) o.share_mode = -1;
-    if (o.shared_rows == 0) o.shared_rows = 32;
+    if (o.shared_rows == 0) o.shared_rows = cap::kPrivateRows;
     if (o.num_cus == 0) o.num_cus = 256;
-    if (o.waves_per_cu == 0) o.waves_per_cu = 8;
+    if (o.shared_cost == 0.f) o.shared_cost = 4.0f;
     if (o.rounds == 0.f) o.rounds = 2.0f;
     if (o.share_margin == 0.f) o.share_margin = 1.0f;
 }
@@ -399,7 +409,7 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
         return fail(CAP_ERR_INVALID_ARG, "share_mode %d not in {-1, 0, 1, 2}", o.share_mode);
     if (o.shared_rows < 0)
         return fail(CAP_ERR_INVALID_ARG, "shared_rows %d is negative", o.shared_rows);
-    if (o.split_pages < 0 || o.num_cus < 0 || o.waves_per_cu < 0 || !(o.rounds > 0.f) ||
+    if (o.split_pages < 0 || o.num_cus < 0 || !(o.shared_cost > 0.f) || !(o.rounds > 0.f) ||
         !(o.share_margin > 0.f))
         return fail(CAP_ERR_INVALID_ARG, "negative planner option");
 
@@ -411,15 +421,15 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
     pl.build_groups();
 
     // tasks: (page run, request subgroup); balanced splits of both
-    struct Task { int32_t so, np, ro, nr, sb; bool shared; };
+    struct Task { int32_t so, np, ro, nr, sb; bool shared; double cost; };
     std::vector<Task> tasks;
     std::vector<std::vector<int32_t>> req_rows(tree->R);
     int32_t slot_rows = 0;
     for (const Group &g : pl.groups) {
         const int64_t npg = (int64_t)g.entries.size();
-        const int64_t k = std::max<int64_t>(1, (npg + pl.target_pages - 1) / pl.target_pages);
         const int nreq = (int)g.reqs.size();
         const bool shared = pl.is_shared(nreq);
+        const int64_t k = pl.chunks(npg, shared);
         const int rg = (nreq + pl.reqs_per_item(nreq) - 1) / pl.reqs_per_item(nreq);
         const int32_t so0 = (int32_t)p->stream.size();
         p->stream.insert(p->stream.end(), g.entries.begin(), g.entries.end());
@@ -429,27 +439,34 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
             const int64_t pb = npg * ci / k, pe = npg * (ci + 1) / k;
             for (int ri = 0; ri < rg; ++ri) {
                 const int rb = (int)((int64_t)nreq * ri / rg), re = (int)((int64_t)nreq * (ri + 1) / rg);
-                Task tk{(int32_t)(so0 + pb), (int32_t)(pe - pb), ro0 + rb, re - rb, slot_rows, shared};
+                Task tk{(int32_t)(so0 + pb), (int32_t)(pe - pb), ro0 + rb, re - rb, slot_rows, shared,
+                        (double)(pe - pb) * pl.page_cost(shared)};
                 for (int q = rb; q < re; ++q) req_rows[g.reqs[q]].push_back(slot_rows + (q - rb));
                 slot_rows += re - rb;
                 tasks.push_back(tk);
+                pl.max_pages = std::max<int>(pl.max_pages, (int)(pe - pb));
             }
         }
     }
-    // longest runs first; the row subgroups of one run stay adjacent
+    // costliest first within each kind (the hardware dispatches workgroups in
+    // order, so this is greedy longest-processing-time scheduling), and the two
+    // kinds interleaved evenly so that compute-heavy shared items and
+    // memory-heavy private items run side by side on the CUs; one item per
+    // task and KV head, the heads of a task back to back
     std::stable_sort(tasks.begin(), tasks.end(),
-                     [](const Task &a, const Task &b) { return a.np > b.np; });
-    // items: for each page run, for each KV head, its request subgroups back to
-    // back, so the waves that read the same pages share a workgroup (and its L1)
-    for (size_t i = 0; i < tasks.size();) {
-        size_t j = i + 1;
-        while (j < tasks.size() && tasks[j].so == tasks[i].so && tasks[j].np == tasks[i].np) ++j;
+                     [](const Task &a, const Task &b) { return a.cost > b.cost; });
+    std::vector<const Task *> sh, pr;
+    for (const Task &tk : tasks) (tk.shared ? sh : pr).push_back(&tk);
+    p->items.reserve(tasks.size() * Hkv);
+    size_t i_sh = 0, i_pr = 0;
+    while (i_sh < sh.size() || i_pr < pr.size()) {
+        // pick the kind that is further behind its share of the sequence
+        const bool take_sh = i_pr >= pr.size() ||
+                             (i_sh < sh.size() && (double)i_sh * pr.size() <= (double)i_pr * sh.size());
+        const Task &tk = take_sh ? *sh[i_sh++] : *pr[i_pr++];
         for (int h = 0; h < Hkv; ++h)
-            for (size_t k = i; k < j; ++k) {
-                const WorkItem w{tasks[k].so, tasks[k].np, h, tasks[k].ro, tasks[k].nr, tasks[k].sb};
-                (tasks[k].shared ? p->shared_items : p->items).push_back(w);
-            }
-        i = j;
+            p->items.push_back(WorkItem{tk.so, tk.np, h, tk.ro, tk.nr, tk.sb,
+                                        tk.shared ? cap::kModeShared : cap::kModePrivate, 0});
     }
     p->merge_off.assign(tree->R + 1, 0);
     int32_t maxp = 0;
@@ -459,17 +476,14 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
         maxp = std::max<int32_t>(maxp, (int32_t)req_rows[r].size());
     }
 
-    // device image: shared items | private items | stream | rows | merge_off | merge_rows
-    p->off_shared = 0;
-    p->off_items = align_up(p->shared_items.size() * sizeof(WorkItem));
-    p->off_stream = p->off_items + align_up(p->items.size() * sizeof(WorkItem));
+    // device image: items | stream | rows | merge_off | merge_rows
+    p->off_items = 0;
+    p->off_stream = align_up(p->items.size() * sizeof(WorkItem));
     p->off_rows = p->off_stream + align_up(p->stream.size() * 4);
     p->off_moff = p->off_rows + align_up(p->rows.size() * 4);
     p->off_mrows = p->off_moff + align_up(p->merge_off.size() * 4);
     p->dev_bytes = std::max<size_t>(p->off_mrows + align_up(p->merge_rows.size() * 4), kAlign);
     p->host_image.assign(p->dev_bytes, 0);
-    std::memcpy(p->host_image.data() + p->off_shared, p->shared_items.data(),
-                p->shared_items.size() * sizeof(WorkItem));
     std::memcpy(p->host_image.data() + p->off_items, p->items.data(), p->items.size() * sizeof(WorkItem));
     std::memcpy(p->host_image.data() + p->off_stream, p->stream.data(), p->stream.size() * 4);
     std::memcpy(p->host_image.data() + p->off_rows, p->rows.data(), p->rows.size() * 4);
@@ -478,7 +492,8 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
 
     cap_plan_stats &s = p->stats;
     s.num_items = (int64_t)p->items.size();
-    s.num_shared_items = (int64_t)p->shared_items.size();
+    s.num_shared_items = 0;
+    for (const WorkItem &w : p->items) s.num_shared_items += w.mode == cap::kModeShared;
     s.num_tasks = (int64_t)tasks.size();
     s.num_groups = (int64_t)pl.groups.size();
     s.partial_rows = slot_rows;
@@ -494,7 +509,7 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
     s.kv_bytes_unshared = tree->sum_ctx * 4LL * D * Hkv;
     s.partial_bytes = (int64_t)slots * (4LL * D + 8);
     s.max_partials_per_request = maxp;
-    s.max_pages_per_item = pl.target_pages;
+    s.max_pages_per_item = pl.max_pages;
     s.plan_host_us = std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count();
     *out = p;
     return CAP_OK;
@@ -510,8 +525,6 @@ cap_status cap_plan_get_stats(const cap_plan *plan, cap_plan_stats *stats)
 cap_status cap_plan_get_view(const cap_plan *plan, cap_plan_view *v)
 {
     if (!plan || !v) return fail(CAP_ERR_INVALID_ARG, "NULL argument");
-    v->num_shared_items = (int32_t)plan->shared_items.size();
-    v->shared_items = reinterpret_cast<const cap_work_item *>(plan->shared_items.data());
     v->num_items = (int32_t)plan->items.size();
     v->items = reinterpret_cast<const cap_work_item *>(plan->items.data());
     v->stream_len = (int32_t)plan->stream.size();
@@ -565,9 +578,7 @@ cap_status cap_decode_attention(const cap_plan *plan, const void *q, const void 
     cap_status st = split_workspace(plan, workspace, ws_bytes, &a.part_o, &a.part_m, &a.part_l);
     if (st != CAP_OK) return st;
     const char *d = static_cast<const char *>(plan->dev);
-    a.shared_items = reinterpret_cast<const WorkItem *>(d + plan->off_shared);
     a.items = reinterpret_cast<const WorkItem *>(d + plan->off_items);
-    a.n_shared = (int32_t)plan->shared_items.size();
     a.stream = reinterpret_cast<const int32_t *>(d + plan->off_stream);
     a.rows = reinterpret_cast<const int32_t *>(d + plan->off_rows);
     a.tree_pages = plan->tree->dev_pages;

@@ -11,15 +11,20 @@ namespace cap {
 // Layout constants of the paged KV cache.
 constexpr int kPage = 16;            // tokens per page
 constexpr int kWaveSize = 64;        // CDNA wavefront
-constexpr int kSharedThreads = 512;  // decode workgroup: eight waves
+constexpr int kWaves = 4;            // waves per decode workgroup
+constexpr int kSharedThreads = kWaves * kWaveSize;
+constexpr int kStages = 2;           // shared path: KV steps in flight in registers
 constexpr int kPrivateRows = 16;     // query rows of a private (one-wave) item
-constexpr int kSharedRows = 256;     // query rows of a shared (one-workgroup) item: 8 waves x 32
+constexpr int kSharedRows = 32 * kWaves;  // query rows of a shared item: 32 per wave
 constexpr int kRowsPerItem = 32;     // the GQA group must divide this
-constexpr int kMaxPagesPerItem = 64; // a wave keeps its item's page table one page per lane
+constexpr int kMaxSharedPages = 64;   // a shared item's waves each keep its page table, one page per lane
+constexpr int kMaxPrivatePages = 64 * kWaves; // a private item: 64 pages per wave
+constexpr int kModePrivate = 0, kModeShared = 1;
 
-// A run of KV pages of one KV head applied to nreq requests x G query heads:
-// up to 16 rows for a private item (one wave), up to 256 for a shared item
-// (one workgroup).  Same layout as cap_work_item.
+// A run of KV pages of one KV head applied to nreq requests x G query heads,
+// run by one workgroup: up to 16 rows and kMaxPrivatePages pages for a
+// private item, up to kSharedRows rows and 64 pages for a shared item.  Same
+// layout as cap_work_item.
 struct WorkItem {
     int32_t stream_off;
     int32_t npages;
@@ -27,12 +32,13 @@ struct WorkItem {
     int32_t row_off;
     int32_t nreq;
     int32_t slot_base;
+    int32_t mode;                // kModePrivate / kModeShared
+    int32_t reserved;
 };
 static_assert(sizeof(WorkItem) == sizeof(cap_work_item), "work item layout");
 
 struct DecodeArgs {
-    const WorkItem *shared_items;  // one workgroup each
-    const WorkItem *items;         // private: one wave each
+    const WorkItem *items;         // one workgroup each
     const int32_t *stream;       // page-stream entries: (tree page index << 5) | (ntok - 1)
     const int32_t *tree_pages;   // tree page index -> physical page
     const int32_t *rows;         // request ids of each item's request list
@@ -42,7 +48,6 @@ struct DecodeArgs {
     float *part_o;               // [slots][D]
     float *part_m;               // [slots]
     float *part_l;               // [slots]
-    int32_t n_shared;
     int32_t n_items;
     int32_t Hq, Hkv, G;
     float scale_log2;            // sm_scale * log2(e)

@@ -132,72 +132,103 @@ __device__ __forceinline__ void mask_v(u32x4 (&v)[D / 16], int nt0, int nt1, int
     }
 }
 
-// max over the four lanes n, n+16, n+32, n+48 that hold one query row
+// max over the four lanes n, n+16, n+32, n+48 that hold one query row, with
+// gfx950's lane-half swaps (VALU, no LDS round trip): swapping lane halves of
+// two copies and taking the max gives an xor-32, then an xor-16 reduction.
+// Written as one asm block because this compiler folds max(first result,
+// second result) of the swap intrinsic to the first result; the s_nop covers
+// the VALU-write-to-permlane-read wait states.
 __device__ __forceinline__ float row_max4(float v)
 {
-    v = fmaxf(v, __shfl_xor(v, 16));
-    return fmaxf(v, __shfl_xor(v, 32));
+    float a = v, b = v;
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_permlane32_swap_b32 %0, %1\n\t"
+        "v_max_f32 %0, %0, %1\n\t"
+        "v_mov_b32 %1, %0\n\t"
+        "s_nop 1\n\t"
+        "v_permlane16_swap_b32 %0, %1\n\t"
+        "v_max_f32 %0, %0, %1"
+        : "+v"(a), "+v"(b));
+    return a;
 }
 
-template <int D, int RB>
+// One 2-page step for up to RB 16-row blocks, in phases so the blocks'
+// independent work can overlap: all QK MFMAs, then masking and row maxima,
+// one (rare) rescale, the probabilities, then all PV MFMAs.  A missing second
+// page (nt1 = 0) is masked like any tail.  MASKV: zero V tails in registers
+// (the shared path zeroes them when it stages the tile in LDS instead).
+template <int D, int RB, bool MASKV>
 __device__ __forceinline__ void compute_step(Step<D> &f, const u32x4 (&qf)[RB][D / 32],
                                              f32x4 (&o)[RB][D / 16], float (&m_ref)[RB],
                                              float (&l_run)[RB], int nblk, float scale, int c)
 {
-    const bool has1 = f.nt1 > 0;
-    if (f.nt0 < kPage || f.nt1 < kPage) mask_v<D>(f.v, f.nt0, f.nt1, c);
-
+    if constexpr (MASKV) {
+        if (f.nt0 < kPage || f.nt1 < kPage) mask_v<D>(f.v, f.nt0, f.nt1, c);
+    }
+    f32x4 s0[RB], s1[RB];
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
-        if (b >= nblk) break;
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+        s0[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        s1[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (RB == 1 || b < nblk) {
 #pragma unroll
-        for (int i = 0; i < D / 32; ++i) s0 = mfma(f.k0[i], qf[b][i], s0);
-        if (has1) {
-#pragma unroll
-            for (int i = 0; i < D / 32; ++i) s1 = mfma(f.k1[i], qf[b][i], s1);
+            for (int i = 0; i < D / 32; ++i) {
+                s0[b] = mfma(f.k0[i], qf[b][i], s0[b]);
+                s1[b] = mfma(f.k1[i], qf[b][i], s1[b]);
+            }
         }
-        float x[8];
+    }
+    const int lim0 = f.nt0 - 4 * c, lim1 = f.nt1 - 4 * c;   // lane holds tokens 4c..4c+3
+    float x[RB][8], mx[RB];
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            x[j] = s0[j];
-            x[4 + j] = s1[j];
+            x[b][j] = j < lim0 ? s0[b][j] : -INFINITY;
+            x[b][4 + j] = j < lim1 ? s1[b][j] : -INFINITY;
         }
-        if (f.nt0 < kPage) {
+        mx[b] = fmaxf(fmaxf(fmaxf(x[b][0], x[b][1]), fmaxf(x[b][2], x[b][3])),
+                      fmaxf(fmaxf(x[b][4], x[b][5]), fmaxf(x[b][6], x[b][7])));
+    }
+    bool need = false;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) x[j] = (4 * c + j < f.nt0) ? x[j] : -INFINITY;
-        }
-        if (f.nt1 < kPage) {
+    for (int b = 0; b < RB; ++b) {
+        mx[b] = row_max4(mx[b]) * scale;                 // base-2 units (scale > 0)
+        need |= mx[b] > m_ref[b] + kRescaleThreshold;
+    }
+    if (__builtin_amdgcn_ballot_w64(need)) {             // wave-uniform, rare after the first step
 #pragma unroll
-            for (int j = 0; j < 4; ++j) x[4 + j] = (4 * c + j < f.nt1) ? x[4 + j] : -INFINITY;
-        }
-        float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-        mx = row_max4(mx) * scale;                       // base-2 units (scale > 0)
-        const bool need = mx > m_ref[b] + kRescaleThreshold;
-        if (__builtin_amdgcn_ballot_w64(need)) {         // wave-uniform, rare after the first step
-            const float m_new = need ? mx : m_ref[b];
+        for (int b = 0; b < RB; ++b) {
+            const float m_new = mx[b] > m_ref[b] + kRescaleThreshold ? mx[b] : m_ref[b];
             const float alpha = fast_exp2(m_ref[b] - m_new);   // 1 if unchanged, 0 from -inf
             m_ref[b] = m_new;
             l_run[b] *= alpha;
 #pragma unroll
             for (int j = 0; j < D / 16; ++j) o[b][j] *= alpha;
         }
-        const float mneg = -m_ref[b];
-        float p[8];
-        float psum = 0.f;
+    }
+    u32x4 pw[RB];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            p[j] = fast_exp2(__builtin_fmaf(x[j], scale, mneg));
-            psum += p[j];
-        }
-        l_run[b] += psum;
+    for (int b = 0; b < RB; ++b) {
+        const float mneg = -m_ref[b];
+        float psum = 0.f;
         bf16x8 pb;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) pb[j] = (__bf16)p[j];
-        const u32x4 pw = __builtin_bit_cast(u32x4, pb);
+        for (int j = 0; j < 8; ++j) {
+            const float p = fast_exp2(__builtin_fmaf(x[b][j], scale, mneg));
+            psum += p;
+            pb[j] = (__bf16)p;
+        }
+        l_run[b] += psum;
+        pw[b] = __builtin_bit_cast(u32x4, pb);
+    }
 #pragma unroll
-        for (int j = 0; j < D / 16; ++j) o[b][j] = mfma(f.v[j], pw, o[b][j]);
+    for (int b = 0; b < RB; ++b) {
+        if (RB == 1 || b < nblk) {
+#pragma unroll
+            for (int j = 0; j < D / 16; ++j) o[b][j] = mfma(f.v[j], pw[b], o[b][j]);
+        }
     }
 }
 
@@ -252,58 +283,114 @@ __device__ __forceinline__ void write_partials(const DecodeArgs &a, const WorkIt
     }
 }
 
-// Page table of an item, one page per lane (items hold at most 64 pages).
-__device__ __forceinline__ void load_page_table(const DecodeArgs &a, const WorkItem &it, int lane,
-                                                int &lane_pid, int &lane_nt)
+// Page table of pages [first, first + count) of an item, one page per lane
+// (count <= 64).
+__device__ __forceinline__ void load_page_table(const DecodeArgs &a, const WorkItem &it, int first, int count,
+                                                int lane, int &lane_pid, int &lane_nt)
 {
     lane_pid = 0;
     lane_nt = 0;
-    if (lane < it.npages) {
-        const int e = a.stream[it.stream_off + lane];
+    if (lane < count) {
+        const int e = a.stream[it.stream_off + first + lane];
         lane_pid = a.tree_pages[e >> 5];
         lane_nt = (e & 31) + 1;
     }
 }
 
 // ---------------------------------------------------------------- private path
-// One wave, one item of at most 16 rows; its KV fragments come straight from
-// HBM into registers, one 2-page step in flight while the previous computes.
+// One workgroup, one item of at most 16 rows.  The waves split the item's
+// 2-page steps into contiguous sub-streams, one per wave; each streams its
+// pages straight from HBM into registers (one step in flight while the
+// previous computes) and keeps its own (m, l, o).  At the end the waves put
+// their statistics in LDS and the workgroup writes one merged partial.
 template <int D>
-__device__ __forceinline__ void private_item(const DecodeArgs &a, const WorkItem &it, int lane, int n, int c)
+__device__ __forceinline__ void private_item(const DecodeArgs &a, const WorkItem &it, float *mrg, int tid,
+                                             int lane, int n, int c)
 {
+    const int wave = tid >> 6;
     const int nrows = it.nreq * a.G;
+    const int nsteps_all = (it.npages + 1) >> 1;
+    const int s_begin = nsteps_all * wave / kWaves, s_end = nsteps_all * (wave + 1) / kWaves;
+    const int first = 2 * s_begin;
+    const int count = min(it.npages, 2 * s_end) - first;      // this wave's pages (may be 0)
+
     u32x4 qf[1][D / 32];
     load_q<D, 1>(qf, a, it, 0, nrows, n, c);
     f32x4 o[1][D / 16];
 #pragma unroll
     for (int j = 0; j < D / 16; ++j) o[0][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_ref[1] = {-INFINITY}, l_run[1] = {0.f};
-    int lane_pid, lane_nt;
-    load_page_table(a, it, lane, lane_pid, lane_nt);
-
-    const int nsteps = (it.npages + 1) >> 1;
-    const float sc = a.scale_log2;
-    Step<D> fa, fb;
-    load_step<D>(fa, a, it.head, it.npages, 0, lane_pid, lane_nt, n, c);
-    for (int s = 0; s < nsteps; s += 2) {
-        load_step<D>(fb, a, it.head, it.npages, s + 1, lane_pid, lane_nt, n, c);
-        compute_step<D, 1>(fa, qf, o, m_ref, l_run, 1, sc, c);
-        if (s + 1 >= nsteps) break;
-        load_step<D>(fa, a, it.head, it.npages, s + 2, lane_pid, lane_nt, n, c);
-        compute_step<D, 1>(fb, qf, o, m_ref, l_run, 1, sc, c);
+    if (count > 0) {
+        int lane_pid, lane_nt;
+        load_page_table(a, it, first, count, lane, lane_pid, lane_nt);
+        const int nsteps = (count + 1) >> 1;
+        const float sc = a.scale_log2;
+        Step<D> fa, fb;
+        load_step<D>(fa, a, it.head, count, 0, lane_pid, lane_nt, n, c);
+        for (int s = 0; s < nsteps; s += 2) {
+            load_step<D>(fb, a, it.head, count, s + 1, lane_pid, lane_nt, n, c);
+            compute_step<D, 1, true>(fa, qf, o, m_ref, l_run, 1, sc, c);
+            if (s + 1 >= nsteps) break;
+            load_step<D>(fa, a, it.head, count, s + 2, lane_pid, lane_nt, n, c);
+            compute_step<D, 1, true>(fb, qf, o, m_ref, l_run, 1, sc, c);
+        }
     }
-    write_partials<D, 1>(a, it, 0, nrows, 1, o, m_ref, l_run, n, c);
+
+    // this wave's statistics into LDS: o rows [wave][16][D], then m[wave][16], l[wave][16]
+    float *ob = mrg, *mb = mrg + kWaves * 16 * D, *lb = mb + kWaves * 16;
+    float l = l_run[0];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j)
+        *reinterpret_cast<f32x4 *>(ob + (wave * 16 + n) * D + 16 * j + 4 * c) = o[0][j];
+    if (c == 0) {
+        mb[wave * 16 + n] = m_ref[0];
+        lb[wave * 16 + n] = l;
+    }
+    __syncthreads();
+
+    // merge: thread t takes row t / TPR and D/TPR consecutive dims
+    constexpr int TPR = kSharedThreads / 16;             // threads per row
+    constexpr int V = D / TPR;
+    const int row = tid / TPR, d0 = (tid % TPR) * V;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+        if (lb[w * 16 + row] > 0.f) M = fmaxf(M, mb[w * 16 + row]);
+    float L = 0.f, acc[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc[v] = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const float lw = lb[w * 16 + row];
+        const float wt = lw > 0.f ? fast_exp2(mb[w * 16 + row] - M) : 0.f;
+        L += wt * lw;
+#pragma unroll
+        for (int v = 0; v < V; ++v) acc[v] += wt * ob[(w * 16 + row) * D + d0 + v];
+    }
+    if (row < nrows) {
+        const int G = a.G;
+        const int64_t slot = (int64_t)(it.slot_base + row / G) * a.Hq + it.head * G + row % G;
+        float *po = a.part_o + slot * D + d0;
+#pragma unroll
+        for (int v = 0; v < V; ++v) po[v] = acc[v];
+        if (tid % TPR == 0) {
+            a.part_m[slot] = M;
+            a.part_l[slot] = L;
+        }
+    }
 }
 
 // ----------------------------------------------------------------- shared path
-// One workgroup, one item of up to 256 rows (nreq x G).  The eight waves
-// stream each 2-page step of KV once, cooperatively (128-bit loads, D/64 per
-// thread per step, four steps in flight in registers), stage it in a
-// double-buffered LDS tile, and each wave applies the tile to its own 32
-// rows.  One barrier per step.
+// One workgroup, one item of up to kSharedRows rows (nreq x G).  The waves
+// stream each 2-page step of KV once, cooperatively (128-bit loads, kStages
+// steps in flight in registers), stage it in a double-buffered LDS tile, and
+// each wave applies the tile to its own 32 rows.  One barrier per step.
 template <int D>
 struct Stage {
-    u32x4 x[D / 64];
+    static constexpr int kPieces = 8 * D / kSharedThreads;   // 16-byte pieces per thread per step
+    u32x4 x[kPieces];
 };
 
 template <int D>
@@ -318,7 +405,7 @@ __device__ __forceinline__ void issue_stage(Stage<D> &st, const DecodeArgs &a, i
     const int64_t p0 = __builtin_amdgcn_readlane(lane_pid, i0);
     const int64_t p1 = __builtin_amdgcn_readlane(lane_pid, i1);
 #pragma unroll
-    for (int k = 0; k < D / 64; ++k) {
+    for (int k = 0; k < Stage<D>::kPieces; ++k) {
         const int p = tid + k * kSharedThreads;     // 16-byte piece of the 4-block stage
         const int b = p / (2 * D);                  // 0 K page0, 1 K page1, 2 V page0, 3 V page1 (wave-uniform)
         const int64_t page = (b & 1) ? p1 : p0;
@@ -327,15 +414,50 @@ __device__ __forceinline__ void issue_stage(Stage<D> &st, const DecodeArgs &a, i
     }
 }
 
+// LDS tile of one step: K page 0, K page 1, V page 0, V page 1, each 16 x D
+// bf16.  K blocks keep the pool layout (a wave's fragment read is 1 KB
+// contiguous).  V blocks ([D][16], 32-byte rows) store the 8-byte column c of
+// row d at column c ^ ((d >> 2) & 3): the sixteen lanes that read one column of
+// rows 16j..16j+15 then hit sixteen different bank pairs instead of four.
 template <int D>
-__device__ __forceinline__ void write_stage(const Stage<D> &st, uint16_t *slot, int tid)
+__device__ __forceinline__ void write_stage(const Stage<D> &st, uint16_t *slot, int tid, int nt0, int nt1)
 {
 #pragma unroll
-    for (int k = 0; k < D / 64; ++k)
-        *reinterpret_cast<u32x4 *>(slot + (tid + k * kSharedThreads) * 8) = st.x[k];
+    for (int k = 0; k < Stage<D>::kPieces; ++k) {
+        const int p = tid + k * kSharedThreads;
+        if (p < 4 * D) {                                  // K blocks: as in the pool
+            *reinterpret_cast<u32x4 *>(slot + p * 8) = st.x[k];
+        } else {                                          // V blocks: swizzled 8-byte columns
+            const int q = p % (2 * D);                    // piece within the V block
+            const int d = q >> 1, h = q & 1;              // row, 16-byte half (tokens 8h..8h+7)
+            const int sw = (d >> 2) & 3;
+            u32x4 x = st.x[k];
+            const int nt = p < 6 * D ? nt0 : nt1;         // V page 0 or V page 1 (wave-uniform)
+            if (nt < kPage) {                             // zero tokens >= nt (tails may hold NaN)
+                const int lim = nt - 8 * h;
+                x.x &= (lim > 0 ? 0x0000FFFFu : 0u) | (lim > 1 ? 0xFFFF0000u : 0u);
+                x.y &= (lim > 2 ? 0x0000FFFFu : 0u) | (lim > 3 ? 0xFFFF0000u : 0u);
+                x.z &= (lim > 4 ? 0x0000FFFFu : 0u) | (lim > 5 ? 0xFFFF0000u : 0u);
+                x.w &= (lim > 6 ? 0x0000FFFFu : 0u) | (lim > 7 ? 0xFFFF0000u : 0u);
+            }
+            uint16_t *row = slot + (p - q) * 8 + d * kPage;
+            *reinterpret_cast<u32x2 *>(row + ((2 * h) ^ sw) * 4) = u32x2{x.x, x.y};
+            *reinterpret_cast<u32x2 *>(row + ((2 * h + 1) ^ sw) * 4) = u32x2{x.z, x.w};
+        }
+    }
 }
 
-// MFMA fragments of one step from an LDS tile laid out as the four page blocks.
+// Valid tokens of the two pages of step s (0 for a missing second page).
+__device__ __forceinline__ void step_tokens(int npages, int s, int lane_nt, int &nt0, int &nt1)
+{
+    const int nsteps = (npages + 1) >> 1;
+    const int ss = s < nsteps ? s : nsteps - 1;
+    const int i0 = 2 * ss;
+    nt0 = __builtin_amdgcn_readlane(lane_nt, i0);
+    nt1 = i0 + 1 < npages ? __builtin_amdgcn_readlane(lane_nt, i0 + 1) : 0;
+}
+
+// MFMA fragments of one step from the LDS tile.
 template <int D>
 __device__ __forceinline__ void lds_step(Step<D> &f, const uint16_t *slot, int npages, int s, int lane_nt,
                                          int n, int c)
@@ -350,10 +472,11 @@ __device__ __forceinline__ void lds_step(Step<D> &f, const uint16_t *slot, int n
         f.k0[i] = *reinterpret_cast<const u32x4 *>(slot + ((4 * i + c) * kPage + n) * 8);
         f.k1[i] = *reinterpret_cast<const u32x4 *>(slot + blk + ((4 * i + c) * kPage + n) * 8);
     }
+    const int col = (c ^ ((n >> 2) & 3)) * 4;            // rows 16j + n share (n >> 2) & 3
 #pragma unroll
     for (int j = 0; j < D / 16; ++j) {
-        const u32x2 x0 = *reinterpret_cast<const u32x2 *>(slot + 2 * blk + (16 * j + n) * kPage + 4 * c);
-        const u32x2 x1 = *reinterpret_cast<const u32x2 *>(slot + 3 * blk + (16 * j + n) * kPage + 4 * c);
+        const u32x2 x0 = *reinterpret_cast<const u32x2 *>(slot + 2 * blk + (16 * j + n) * kPage + col);
+        const u32x2 x1 = *reinterpret_cast<const u32x2 *>(slot + 3 * blk + (16 * j + n) * kPage + col);
         f.v[j] = u32x4{x0.x, x0.y, x1.x, x1.y};
     }
 }
@@ -375,75 +498,56 @@ __device__ __forceinline__ void shared_item(const DecodeArgs &a, const WorkItem 
         for (int j = 0; j < D / 16; ++j) o[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_ref[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
     int lane_pid, lane_nt;
-    load_page_table(a, it, lane, lane_pid, lane_nt);
+    load_page_table(a, it, 0, it.npages, lane, lane_pid, lane_nt);
 
     const int nsteps = (it.npages + 1) >> 1;
     const float sc = a.scale_log2;
     uint16_t *slot0 = lds, *slot1 = lds + 4 * kPage * D;
     const int h = it.head, np = it.npages;
     Step<D> f;
-    Stage<D> r0, r1, r2, r3;                        // stage q lives in r[q % 4] until written to LDS
-    issue_stage<D>(r0, a, h, np, 0, lane_pid, tid);
-    issue_stage<D>(r1, a, h, np, 1, lane_pid, tid);
-    issue_stage<D>(r2, a, h, np, 2, lane_pid, tid);
-    issue_stage<D>(r3, a, h, np, 3, lane_pid, tid);
-    write_stage<D>(r0, slot0, tid);
+    Stage<D> r[kStages];                            // stage q lives in r[q % kStages] until written to LDS
+#pragma unroll
+    for (int q = 0; q < kStages; ++q) issue_stage<D>(r[q], a, h, np, q, lane_pid, tid);
+    int t0, t1;
+    step_tokens(np, 0, lane_nt, t0, t1);
+    write_stage<D>(r[0], slot0, tid, t0, t1);
     __syncthreads();
-    issue_stage<D>(r0, a, h, np, 4, lane_pid, tid);
-    for (int s = 0; s < nsteps; s += 4) {
-        if (nblk) {
-            lds_step<D>(f, slot0, np, s, lane_nt, n, c);
-            compute_step<D, 2>(f, qf, o, m_ref, l_run, nblk, sc, c);
+    issue_stage<D>(r[0], a, h, np, kStages, lane_pid, tid);
+    for (int s = 0; s < nsteps; s += kStages) {
+#pragma unroll
+        for (int u = 0; u < kStages; ++u) {             // kStages is even: step s + u uses slot u % 2
+            if (s + u >= nsteps) break;
+            if (nblk) {
+                lds_step<D>(f, (u & 1) ? slot1 : slot0, np, s + u, lane_nt, n, c);
+                compute_step<D, 2, false>(f, qf, o, m_ref, l_run, nblk, sc, c);
+            }
+            step_tokens(np, s + u + 1, lane_nt, t0, t1);
+            write_stage<D>(r[(u + 1) % kStages], (u & 1) ? slot0 : slot1, tid, t0, t1);
+            issue_stage<D>(r[(u + 1) % kStages], a, h, np, s + u + 1 + kStages, lane_pid, tid);
+            __syncthreads();
         }
-        write_stage<D>(r1, slot1, tid);
-        issue_stage<D>(r1, a, h, np, s + 5, lane_pid, tid);
-        __syncthreads();
-        if (s + 1 >= nsteps) break;
-        if (nblk) {
-            lds_step<D>(f, slot1, np, s + 1, lane_nt, n, c);
-            compute_step<D, 2>(f, qf, o, m_ref, l_run, nblk, sc, c);
-        }
-        write_stage<D>(r2, slot0, tid);
-        issue_stage<D>(r2, a, h, np, s + 6, lane_pid, tid);
-        __syncthreads();
-        if (s + 2 >= nsteps) break;
-        if (nblk) {
-            lds_step<D>(f, slot0, np, s + 2, lane_nt, n, c);
-            compute_step<D, 2>(f, qf, o, m_ref, l_run, nblk, sc, c);
-        }
-        write_stage<D>(r3, slot1, tid);
-        issue_stage<D>(r3, a, h, np, s + 7, lane_pid, tid);
-        __syncthreads();
-        if (s + 3 >= nsteps) break;
-        if (nblk) {
-            lds_step<D>(f, slot1, np, s + 3, lane_nt, n, c);
-            compute_step<D, 2>(f, qf, o, m_ref, l_run, nblk, sc, c);
-        }
-        write_stage<D>(r0, slot0, tid);
-        issue_stage<D>(r0, a, h, np, s + 8, lane_pid, tid);
-        __syncthreads();
     }
     write_partials<D, 2>(a, it, row0, nrows, nblk, o, m_ref, l_run, n, c);
 }
 
-// Workgroups [0, n_shared) run one shared item each; the rest run eight
-// private items each (one per wave).
+// One workgroup per work item: shared items stage KV in LDS for their
+// row-waves; private items split their pages over the waves.
 template <int D>
 __global__ __launch_bounds__(kSharedThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_kernel(DecodeArgs a)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 4 * kPage * D];
+    constexpr int kTileBytes = 2 * 4 * kPage * D * 2;               // shared path: two LDS tiles
+    constexpr int kMergeBytes = (kWaves * 16 * D + 2 * kWaves * 16) * 4;   // private path: merge buffer
+    constexpr int kLdsBytes = kTileBytes > kMergeBytes ? kTileBytes : kMergeBytes;
+    __shared__ __attribute__((aligned(16))) float lds[kLdsBytes / 4];
     const int tid = threadIdx.x;
     const int lane = tid & (kWaveSize - 1);
     const int n = lane & 15, c = lane >> 4;
-    const int bid = blockIdx.x;
-    if (bid < a.n_shared) {
-        shared_item<D>(a, a.shared_items[bid], lds, tid, lane, n, c);
-        return;
-    }
-    const int wi = __builtin_amdgcn_readfirstlane((bid - a.n_shared) * (kSharedThreads / kWaveSize) + (tid >> 6));
-    if (wi >= a.n_items) return;
-    private_item<D>(a, a.items[wi], lane, n, c);
+    const WorkItem &it = a.items[blockIdx.x];
+    if (it.mode == kModeShared)
+        shared_item<D>(a, it, reinterpret_cast<uint16_t *>(lds), tid, lane, n, c);
+    else
+        private_item<D>(a, it, lds, tid, lane, n, c);
 }
 
 // One wave per (request, query head): out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i.
@@ -571,14 +675,12 @@ __global__ __launch_bounds__(256) void copy_kernel(u32x4 *dst, const u32x4 *src,
 
 int launch_decode(const DecodeArgs &a, int head_dim, void *stream)
 {
-    const int private_wg = (a.n_items + kSharedThreads / kWaveSize - 1) / (kSharedThreads / kWaveSize);
-    const int nwg = a.n_shared + private_wg;
-    if (nwg <= 0) return 0;
+    if (a.n_items <= 0) return 0;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (head_dim == 128)
-        hipLaunchKernelGGL(decode_kernel<128>, dim3(nwg), dim3(kSharedThreads), 0, s, a);
+        hipLaunchKernelGGL(decode_kernel<128>, dim3(a.n_items), dim3(kSharedThreads), 0, s, a);
     else
-        hipLaunchKernelGGL(decode_kernel<64>, dim3(nwg), dim3(kSharedThreads), 0, s, a);
+        hipLaunchKernelGGL(decode_kernel<64>, dim3(a.n_items), dim3(kSharedThreads), 0, s, a);
     return (int)hipGetLastError();
 }
 

@@ -109,14 +109,16 @@ typedef struct cap_plan_opts {
                                  every request streams its whole context), 1 share
                                  every non-empty node, 2 auto (same as -1) */
     int32_t split_pages;      /* 0 auto; else the most KV pages one work item streams
-                                 (values above 64 are treated as 64) */
-    int32_t shared_rows;      /* 0 = 32: request groups with more query rows than this
-                                 (requests x G) are served by shared workgroup items of
-                                 up to 256 rows; the others by one-wave private items of
-                                 up to 16 rows.  G > 16 always uses shared items */
+                                 (shared items hold at most 64, private at most 256) */
+    int32_t shared_rows;      /* 0 = 16: request groups with more query rows than this
+                                 (requests x G) are served by shared items (KV staged in
+                                 LDS for up to 128 rows); the others by private items (up
+                                 to 16 rows, pages split over the 4 waves).  G > 16
+                                 always uses shared items */
     int32_t num_cus;          /* 0 = 256 (MI355X); used by the cost model */
-    int32_t waves_per_cu;     /* 0 = 8; resident waves per CU in the cost model */
-    float rounds;             /* 0 = 2.0; target work-item rounds per resident slot */
+    float shared_cost;        /* 0 = 4.0; cost of a shared item's page relative to a
+                                 private item's page, used to size items */
+    float rounds;             /* 0 = 2.0; target work items per CU */
     float share_margin;       /* 0 = 1.0; share a node only if saved bytes exceed
                                  margin x added partial bytes */
     int32_t reserved[4];
@@ -124,8 +126,8 @@ typedef struct cap_plan_opts {
 
 /* Plan summary (host-side numbers; bytes are per decode step). */
 typedef struct cap_plan_stats {
-    int64_t num_items;            /* private work items (one wavefront each) */
-    int64_t num_shared_items;     /* shared work items (one 8-wave workgroup each) */
+    int64_t num_items;            /* work items (one 4-wave workgroup each) */
+    int64_t num_shared_items;     /* ... of which shared items */
     int64_t num_tasks;            /* (page run, request group) pairs; items = tasks x Hkv */
     int64_t num_groups;           /* request groups after share/fold decisions */
     int64_t partial_rows;         /* partial slots = partial_rows x Hq */
@@ -144,16 +146,19 @@ typedef struct cap_plan_stats {
 typedef struct cap_tree cap_tree;   /* opaque host handles */
 typedef struct cap_plan cap_plan;
 
-/* Work item as stored in the plan (exposed for inspection and tests).  A
- * private item is one wavefront and serves up to 16 query rows; a shared item
- * is one 8-wave workgroup and serves up to 256. */
+/* Work item as stored in the plan (exposed for inspection and tests).  Each
+ * is run by one 4-wave workgroup: a private item (mode 0) serves up to 16
+ * query rows and streams up to 256 pages; a shared item (mode 1) serves up to
+ * 128 rows and streams up to 64 pages. */
 typedef struct cap_work_item {
     int32_t stream_off;   /* first entry of its page run in the plan's page stream */
-    int32_t npages;       /* pages in the run (1..64) */
+    int32_t npages;       /* pages in the run */
     int32_t head;         /* KV head */
     int32_t row_off;      /* first entry of its request list in the plan's row table */
     int32_t nreq;         /* requests served; query rows = nreq x G */
     int32_t slot_base;    /* partial row of its first request */
+    int32_t mode;         /* 0 private, 1 shared */
+    int32_t reserved;
 } cap_work_item;
 
 /* Read-only host view of a plan (pointers valid until cap_plan_free).
@@ -162,7 +167,6 @@ typedef struct cap_work_item {
  *   (slot_base + i/G) * Hq + head*G + i%G.
  * Request r's partial rows: merge_rows[merge_off[r] .. merge_off[r+1]). */
 typedef struct cap_plan_view {
-    int32_t num_shared_items;  const cap_work_item *shared_items;
     int32_t num_items;         const cap_work_item *items;
     int32_t stream_len;        const int32_t *stream;
     int32_t rows_len;          const int32_t *rows;

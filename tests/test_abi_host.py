@@ -125,16 +125,17 @@ def check_coverage(tree, plan_handle):
     got = {(r, h): [] for r in range(R) for h in range(Hkv)}
     slot_writes = np.zeros(int(st["partial_rows"]) * Hq, np.int64)
     slot_rows_of = {r: set() for r in range(R)}
-    for items, max_rows in ((v["items"], 16), (v["shared_items"], 256)):
-        for so, npg, head, ro, nreq, sb in items:
-            assert 1 <= npg <= 64 and 0 <= head < Hkv and 1 <= nreq and nreq * G <= max_rows
-            ents = v["stream"][so:so + npg]
-            pages = [(int(e) >> 5, (int(e) & 31) + 1) for e in ents]
-            for qpos, r in enumerate(v["rows"][ro:ro + nreq]):
-                got[(int(r), int(head))].extend(pages)
-                for i in range(G):
-                    slot_writes[(sb + qpos) * Hq + head * G + i] += 1
-                slot_rows_of[int(r)].add(int(sb + qpos))
+    for so, npg, head, ro, nreq, sb, mode, _ in v["items"]:
+        max_rows, max_pages = (128, 64) if mode == 1 else (16, 256)
+        assert mode in (0, 1)
+        assert 1 <= npg <= max_pages and 0 <= head < Hkv and 1 <= nreq and nreq * G <= max_rows
+        ents = v["stream"][so:so + npg]
+        pages = [(int(e) >> 5, (int(e) & 31) + 1) for e in ents]
+        for qpos, r in enumerate(v["rows"][ro:ro + nreq]):
+            got[(int(r), int(head))].extend(pages)
+            for i in range(G):
+                slot_writes[(sb + qpos) * Hq + head * G + i] += 1
+            slot_rows_of[int(r)].add(int(sb + qpos))
     for (r, h), s in got.items():
         assert sorted(s) == want[r], f"request {r} head {h}"
     assert np.all(slot_writes == 1)
@@ -143,14 +144,14 @@ def check_coverage(tree, plan_handle):
         assert len(set(ml.tolist())) == len(ml)
         assert set(ml.tolist()) == slot_rows_of[r]
     assert st["num_items"] == len(v["items"])
-    assert st["num_shared_items"] == len(v["shared_items"])
-    if G > 16:
-        assert len(v["items"]) == 0
+    assert st["num_shared_items"] == int((v["items"][:, 6] == 1).sum()) if len(v["items"]) else True
+    if G > 16 and len(v["items"]):
+        assert np.all(v["items"][:, 6] == 1)
     return st
 
 
 @pytest.mark.parametrize("share_mode", [-1, 0, 1])
-@pytest.mark.parametrize("split_pages", [0, 1, 3, 64])
+@pytest.mark.parametrize("split_pages", [0, 1, 3, 64, 600])
 def test_planner_coverage_random_trees(share_mode, split_pages):
     for seed in range(8):
         rng = np.random.default_rng(seed)
