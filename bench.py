@@ -1,13 +1,14 @@
 #!/usr/bin/env python3
 """One-GPU benchmark of shared-prefix decode attention on MI355X.
 
-A step is one pass of the whole path -- decode kernel (partials) + merge
-kernel (bf16 output) -- over one synthetic batch whose inputs are resident
-in HBM.  Before every step (warm-up and timed) a 1 GiB read of another
+A step is one pass of the whole path over one synthetic batch whose inputs
+are resident in HBM: by default the decode kernel (partials) followed by the
+merge kernel (bf16 output); with --fused one cap_decode_step launch (decode
+kernel with the per-request merge done by the item that completes it).  Before every step (warm-up and timed) a 1 GiB read of another
 buffer evicts L2 and the 256 MB Infinity Cache, so KV is read from HBM, not
 from cache; a read leaves clean lines behind, so no write-back of the flush
 competes with the step.  Step time
-is the HIP-event time of the two kernels on the stream they run on; the
+is the HIP-event time of the step's kernels on the stream they run on; the
 planner and the uploads run once, before timing.
 
 Prints one JSON line.  Default workload: the 64-request shared-system-prompt
@@ -79,6 +80,11 @@ def main():
     ap.add_argument("--shared-rows", type=int, default=0,
                     help="groups with more query rows than this use shared workgroups (0: 32)")
     ap.add_argument("--rounds", type=float, default=0.0)
+    ap.add_argument("--order", type=int, default=0, help="work-item order (planner option)")
+    ap.add_argument("--shared-cost", type=float, default=0.0)
+    ap.add_argument("--fused", action="store_true",
+                    help="time the one-launch cap_decode_step instead of cap_decode_attention + "
+                         "cap_merge_partials")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--read-probe-mb", type=int, default=2048)
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -115,6 +121,10 @@ def main():
         opts["shared_rows"] = args.shared_rows
     if args.rounds:
         opts["rounds"] = args.rounds
+    if args.order:
+        opts["order"] = args.order
+    if args.shared_cost:
+        opts["shared_cost"] = args.shared_cost
     dec = TreeDecoder(w.tree, w.q, w.k_pool, w.v_pool, device=dev, **opts)
     plan = dec.stats
     stream = torch.cuda.current_stream(dev)
@@ -148,10 +158,15 @@ def main():
             evict()
         if evs is not None:
             evs[0].record(stream)
-        dec.decode()
-        if evs is not None:
-            evs[1].record(stream)
-        dec.merge()
+        if not args.fused:
+            dec.decode()
+            if evs is not None:
+                evs[1].record(stream)
+            dec.merge()
+        else:
+            dec.fused_step()
+            if evs is not None:
+                evs[1].record(stream)
         if evs is not None:
             evs[2].record(stream)
 
@@ -175,7 +190,9 @@ def main():
     uniq = st_tree["unique_kv_bytes"]
     value = uniq / (mean_ms * 1e-3) / 1e9
     dec_mean = statistics.fmean(dec_ms)
-    alg_bytes_decode = uniq + st_tree["q_bytes"]
+    fused = args.fused
+    # the fused launch also writes the bf16 output
+    alg_bytes_decode = uniq + st_tree["q_bytes"] + (st_tree["out_bytes"] if fused else 0)
     achieved = alg_bytes_decode / (dec_mean * 1e-3) / 1e9
     traffic = load_traffic(args.config) if not args.control else None
     result = {
@@ -205,7 +222,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
-            "kernel": f"decode_kernel<{w.tree.head_dim}>",
+            "kernel": f"decode_kernel<{w.tree.head_dim}, {'true' if fused else 'false'}>",
             "algorithmic_bytes_per_launch": alg_bytes_decode,
             "decode_us_mean": round(dec_mean * 1e3, 3),
         },
@@ -214,8 +231,9 @@ def main():
         "req_heads_per_s": round(st_tree["request_heads"] / (mean_ms * 1e-3), 1),
         "mfma_util": round(st_tree["useful_flop"] / (mean_ms * 1e-3) / 2.5e15, 5),
         "t_decode_us": {"mean": round(dec_mean * 1e3, 3), "median": round(statistics.median(dec_ms) * 1e3, 3)},
-        "t_merge_us": {"mean": round(statistics.fmean(mrg_ms) * 1e3, 3),
-                       "median": round(statistics.median(mrg_ms) * 1e3, 3)},
+        "step_form": "fused cap_decode_step" if fused else "cap_decode_attention + cap_merge_partials",
+        "t_merge_us": ({"mean": round(statistics.fmean(mrg_ms) * 1e3, 3),
+                        "median": round(statistics.median(mrg_ms) * 1e3, 3)} if not fused else None),
         "t_step_us": {"mean": round(mean_ms * 1e3, 3), "median": round(med_ms * 1e3, 3),
                       "min": round(srt[0] * 1e3, 3), "p90": round(p90_ms * 1e3, 3)},
         "value_median_step": round(uniq / (med_ms * 1e-3) / 1e9, 2),

@@ -25,7 +25,7 @@ EXPORTED = [
     "cap_abi_version", "cap_last_error", "cap_plan_opts_default", "cap_tree_device_bytes",
     "cap_tree_upload", "cap_tree_free", "cap_plan_step", "cap_plan_get_stats",
     "cap_plan_get_view", "cap_plan_upload", "cap_decode_attention", "cap_merge_partials",
-    "cap_plan_free", "cap_bench_fill", "cap_bench_read", "cap_bench_copy",
+    "cap_decode_step", "cap_plan_free", "cap_bench_fill", "cap_bench_read", "cap_bench_copy",
 ]
 
 
@@ -53,7 +53,8 @@ class PlanOpts(ctypes.Structure):
     _fields_ = [("share_mode", ctypes.c_int32), ("split_pages", ctypes.c_int32),
                 ("shared_rows", ctypes.c_int32), ("num_cus", ctypes.c_int32),
                 ("shared_cost", ctypes.c_float), ("rounds", ctypes.c_float),
-                ("share_margin", ctypes.c_float), ("reserved", ctypes.c_int32 * 4)]
+                ("share_margin", ctypes.c_float), ("order", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 3)]
 
 
 class PlanStats(ctypes.Structure):
@@ -106,6 +107,7 @@ def lib():
         L.cap_plan_upload.argtypes = [vp, vp, sz, vp]
         L.cap_decode_attention.argtypes = [vp, vp, vp, vp, vp, sz, vp]
         L.cap_merge_partials.argtypes = [vp, vp, sz, vp, vp]
+        L.cap_decode_step.argtypes = [vp, vp, vp, vp, vp, sz, vp, vp]
         L.cap_plan_free.argtypes = [vp]
         L.cap_plan_free.restype = None
         L.cap_bench_fill.argtypes = [vp, sz, ctypes.c_uint32, vp]
@@ -113,7 +115,7 @@ def lib():
         L.cap_bench_copy.argtypes = [vp, vp, sz, vp]
         for name in ("cap_tree_device_bytes", "cap_tree_upload", "cap_plan_step",
                      "cap_plan_get_stats", "cap_plan_get_view", "cap_plan_upload",
-                     "cap_decode_attention", "cap_merge_partials", "cap_bench_fill",
+                     "cap_decode_attention", "cap_merge_partials", "cap_decode_step", "cap_bench_fill",
                      "cap_bench_read", "cap_bench_copy"):
             getattr(L, name).restype = st
         _lib = L
@@ -232,6 +234,13 @@ def cap_decode_attention(plan: int, q: int, k_pool: int, v_pool: int, workspace:
 def cap_merge_partials(plan: int, workspace: int, ws_bytes: int, out: int, stream: int = 0) -> None:
     _check(lib().cap_merge_partials(ctypes.c_void_p(plan), ctypes.c_void_p(workspace), ws_bytes,
                                     ctypes.c_void_p(out), ctypes.c_void_p(stream or None)))
+
+
+def cap_decode_step(plan: int, q: int, k_pool: int, v_pool: int, workspace: int, ws_bytes: int,
+                    out: int, stream: int = 0) -> None:
+    _check(lib().cap_decode_step(ctypes.c_void_p(plan), ctypes.c_void_p(q), ctypes.c_void_p(k_pool),
+                                 ctypes.c_void_p(v_pool), ctypes.c_void_p(workspace), ws_bytes,
+                                 ctypes.c_void_p(out), ctypes.c_void_p(stream or None)))
 
 
 def cap_plan_free(plan: int) -> None:

@@ -80,7 +80,7 @@ struct cap_plan {
     std::vector<int32_t> rows;        // request ids
     std::vector<int32_t> merge_off, merge_rows;
     // device image
-    size_t off_items = 0, off_stream = 0, off_rows = 0, off_moff = 0, off_mrows = 0, dev_bytes = 0;
+    size_t off_items = 0, off_stream = 0, off_rows = 0, off_moff = 0, off_mrows = 0, off_cnt = 0, dev_bytes = 0;
     std::vector<unsigned char> host_image;
     void *dev = nullptr;
 };
@@ -336,6 +336,7 @@ void fill_defaults(cap_plan_opts &o)
     if (o.shared_cost == 0.f) o.shared_cost = 4.0f;
     if (o.rounds == 0.f) o.rounds = 2.0f;
     if (o.share_margin == 0.f) o.share_margin = 1.0f;
+    if (o.order == 0) o.order = 2;
 }
 
 }  // namespace
@@ -412,6 +413,7 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
     if (o.split_pages < 0 || o.num_cus < 0 || !(o.shared_cost > 0.f) || !(o.rounds > 0.f) ||
         !(o.share_margin > 0.f))
         return fail(CAP_ERR_INVALID_ARG, "negative planner option");
+    if (o.order < 1 || o.order > 3) return fail(CAP_ERR_INVALID_ARG, "order %d not in {0, 1, 2, 3}", o.order);
 
     cap_plan *p = new (std::nothrow) cap_plan();
     if (!p) return fail(CAP_ERR_INVALID_ARG, "out of host memory");
@@ -448,26 +450,35 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
             }
         }
     }
-    // costliest first within each kind (the hardware dispatches workgroups in
-    // order, so this is greedy longest-processing-time scheduling), and the two
-    // kinds interleaved evenly so that compute-heavy shared items and
-    // memory-heavy private items run side by side on the CUs; one item per
-    // task and KV head, the heads of a task back to back
-    std::stable_sort(tasks.begin(), tasks.end(),
-                     [](const Task &a, const Task &b) { return a.cost > b.cost; });
-    std::vector<const Task *> sh, pr;
-    for (const Task &tk : tasks) (tk.shared ? sh : pr).push_back(&tk);
-    p->items.reserve(tasks.size() * Hkv);
-    size_t i_sh = 0, i_pr = 0;
-    while (i_sh < sh.size() || i_pr < pr.size()) {
-        // pick the kind that is further behind its share of the sequence
-        const bool take_sh = i_pr >= pr.size() ||
-                             (i_sh < sh.size() && (double)i_sh * pr.size() <= (double)i_pr * sh.size());
-        const Task &tk = take_sh ? *sh[i_sh++] : *pr[i_pr++];
-        for (int h = 0; h < Hkv; ++h)
-            p->items.push_back(WorkItem{tk.so, tk.np, h, tk.ro, tk.nr, tk.sb,
-                                        tk.shared ? cap::kModeShared : cap::kModePrivate, 0});
+    // The hardware starts workgroups in item order as CUs free up, so a list
+    // sorted costliest first is greedy longest-processing-time scheduling.
+    // order 1 interleaves the two kinds evenly (each costliest first), 2 sorts
+    // both kinds together, 3 puts every shared item first.  One item per task
+    // and KV head, the heads of a task back to back.
+    std::stable_sort(tasks.begin(), tasks.end(), [&](const Task &a, const Task &b) {
+        if (o.order == 3 && a.shared != b.shared) return a.shared;
+        return a.cost > b.cost;
+    });
+    std::vector<const Task *> seq;
+    seq.reserve(tasks.size());
+    if (o.order == 1) {
+        std::vector<const Task *> sh, pr;
+        for (const Task &tk : tasks) (tk.shared ? sh : pr).push_back(&tk);
+        size_t i_sh = 0, i_pr = 0;
+        while (i_sh < sh.size() || i_pr < pr.size()) {
+            // take the kind that is further behind its share of the sequence
+            const bool take_sh = i_pr >= pr.size() ||
+                                 (i_sh < sh.size() && (double)i_sh * pr.size() <= (double)i_pr * sh.size());
+            seq.push_back(take_sh ? sh[i_sh++] : pr[i_pr++]);
+        }
+    } else {
+        for (const Task &tk : tasks) seq.push_back(&tk);
     }
+    p->items.reserve(tasks.size() * Hkv);
+    for (const Task *tk : seq)
+        for (int h = 0; h < Hkv; ++h)
+            p->items.push_back(WorkItem{tk->so, tk->np, h, tk->ro, tk->nr, tk->sb,
+                                        tk->shared ? cap::kModeShared : cap::kModePrivate, 0});
     p->merge_off.assign(tree->R + 1, 0);
     int32_t maxp = 0;
     for (int r = 0; r < tree->R; ++r) {
@@ -476,13 +487,15 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
         maxp = std::max<int32_t>(maxp, (int32_t)req_rows[r].size());
     }
 
-    // device image: items | stream | rows | merge_off | merge_rows
+    // device image: items | stream | rows | merge_off | merge_rows | counters
+    // (the fused step's arrival counters, one per request and KV head, zero)
     p->off_items = 0;
     p->off_stream = align_up(p->items.size() * sizeof(WorkItem));
     p->off_rows = p->off_stream + align_up(p->stream.size() * 4);
     p->off_moff = p->off_rows + align_up(p->rows.size() * 4);
     p->off_mrows = p->off_moff + align_up(p->merge_off.size() * 4);
-    p->dev_bytes = std::max<size_t>(p->off_mrows + align_up(p->merge_rows.size() * 4), kAlign);
+    p->off_cnt = p->off_mrows + align_up(p->merge_rows.size() * 4);
+    p->dev_bytes = std::max<size_t>(p->off_cnt + align_up((size_t)tree->R * Hkv * 4), kAlign);
     p->host_image.assign(p->dev_bytes, 0);
     std::memcpy(p->host_image.data() + p->off_items, p->items.data(), p->items.size() * sizeof(WorkItem));
     std::memcpy(p->host_image.data() + p->off_stream, p->stream.data(), p->stream.size() * 4);
@@ -566,15 +579,14 @@ static cap_status split_workspace(const cap_plan *p, const void *ws, size_t ws_b
     return CAP_OK;
 }
 
-cap_status cap_decode_attention(const cap_plan *plan, const void *q, const void *k_pool,
-                                const void *v_pool, void *workspace, size_t ws_bytes,
-                                cap_stream_t stream)
+static cap_status decode_args(const cap_plan *plan, const void *q, const void *k_pool, const void *v_pool,
+                              void *workspace, size_t ws_bytes, cap::DecodeArgs &a)
 {
     if (!plan || !q || !k_pool || !v_pool || !workspace) return fail(CAP_ERR_INVALID_ARG, "NULL argument");
     if (!plan->dev) return fail(CAP_ERR_STATE, "plan not uploaded (call cap_plan_upload first)");
     if (((uintptr_t)q | (uintptr_t)k_pool | (uintptr_t)v_pool) & 15)
         return fail(CAP_ERR_INVALID_ARG, "q, k_pool and v_pool must be 16-byte aligned");
-    cap::DecodeArgs a{};
+    a = cap::DecodeArgs{};
     cap_status st = split_workspace(plan, workspace, ws_bytes, &a.part_o, &a.part_m, &a.part_l);
     if (st != CAP_OK) return st;
     const char *d = static_cast<const char *>(plan->dev);
@@ -590,6 +602,39 @@ cap_status cap_decode_attention(const cap_plan *plan, const void *q, const void 
     a.Hkv = plan->tree->attn.num_kv_heads;
     a.G = plan->tree->G;
     a.scale_log2 = (float)((double)plan->tree->attn.sm_scale * 1.4426950408889634);
+    return CAP_OK;
+}
+
+cap_status cap_decode_attention(const cap_plan *plan, const void *q, const void *k_pool,
+                                const void *v_pool, void *workspace, size_t ws_bytes,
+                                cap_stream_t stream)
+{
+    cap::DecodeArgs a;
+    cap_status st = decode_args(plan, q, k_pool, v_pool, workspace, ws_bytes, a);
+    if (st != CAP_OK) return st;
+    const int e = cap::launch_decode(a, plan->tree->attn.head_dim, stream);
+    if (e != 0) return fail(CAP_ERR_HIP, "decode launch failed: %s", cap::hip_error_string(e));
+    return CAP_OK;
+}
+
+cap_status cap_decode_step(const cap_plan *plan, const void *q, const void *k_pool, const void *v_pool,
+                           void *workspace, size_t ws_bytes, void *out, cap_stream_t stream)
+{
+    if (!out) return fail(CAP_ERR_INVALID_ARG, "NULL argument");
+    if ((uintptr_t)out & 15) return fail(CAP_ERR_INVALID_ARG, "out must be 16-byte aligned");
+    cap::DecodeArgs a;
+    cap_status st = decode_args(plan, q, k_pool, v_pool, workspace, ws_bytes, a);
+    if (st != CAP_OK) return st;
+    const int64_t slots = plan->stats.partial_rows * (int64_t)a.Hq;
+    if (slots * plan->tree->attn.head_dim * 4 >= (int64_t)1 << 31)
+        return fail(CAP_ERR_UNSUPPORTED, "fused step: %lld partial slots exceed the 2 GiB partial-o limit "
+                    "(use cap_decode_attention + cap_merge_partials)", (long long)slots);
+    a.slots = (int32_t)slots;
+    char *d = static_cast<char *>(plan->dev);
+    a.counters = reinterpret_cast<int32_t *>(d + plan->off_cnt);
+    a.merge_off = reinterpret_cast<const int32_t *>(d + plan->off_moff);
+    a.merge_rows = reinterpret_cast<const int32_t *>(d + plan->off_mrows);
+    a.out = static_cast<uint16_t *>(out);
     const int e = cap::launch_decode(a, plan->tree->attn.head_dim, stream);
     if (e != 0) return fail(CAP_ERR_HIP, "decode launch failed: %s", cap::hip_error_string(e));
     return CAP_OK;

@@ -51,6 +51,12 @@ struct DecodeArgs {
     int32_t n_items;
     int32_t Hq, Hkv, G;
     float scale_log2;            // sm_scale * log2(e)
+    // fused step only (counters == nullptr: partials are left for merge_kernel)
+    int32_t *counters;           // [R][Hkv] arrival counts, zero between steps
+    const int32_t *merge_off;    // [R+1] partial rows of each request
+    const int32_t *merge_rows;
+    uint16_t *out;               // [R][Hq][D] bf16
+    int32_t slots;               // partial slots (fused: slots * D * 4 < 2^31)
 };
 
 struct MergeArgs {

@@ -153,18 +153,35 @@ __device__ __forceinline__ float row_max4(float v)
     return a;
 }
 
+// max of three floats as one v_max3_f32.  Written out because fmaxf on
+// values the compiler cannot prove canonical costs an extra NaN-quieting
+// v_max per operand; the operands here are never signalling NaNs.
+__device__ __forceinline__ float vmax3(float a, float b, float c)
+{
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // One 2-page step for up to RB 16-row blocks, in phases so the blocks'
-// independent work can overlap: all QK MFMAs, then masking and row maxima,
-// one (rare) rescale, the probabilities, then all PV MFMAs.  A missing second
-// page (nt1 = 0) is masked like any tail.  MASKV: zero V tails in registers
-// (the shared path zeroes them when it stages the tile in LDS instead).
+// independent work can overlap: all QK MFMAs, the exponent arguments
+// x = s * scale - m_ref against each row's current reference, one (rare)
+// rescale, the probabilities 2^x, then all PV MFMAs.  The common path needs
+// no cross-lane work: a lane only checks that none of its arguments exceeds
+// the rescale threshold; the exact row maxima are taken (over the four lanes
+// of a row) only when some row must move its reference -- the first step, or
+// a maximum that rose by more than the threshold.  Masking (tokens past nt,
+// a missing second page with nt1 = 0) runs only on tail steps.  MASKV: zero
+// V tails in registers (the shared path zeroes them when it stages the tile
+// in LDS instead).
 template <int D, int RB, bool MASKV>
 __device__ __forceinline__ void compute_step(Step<D> &f, const u32x4 (&qf)[RB][D / 32],
                                              f32x4 (&o)[RB][D / 16], float (&m_ref)[RB],
                                              float (&l_run)[RB], int nblk, float scale, int c)
 {
+    const bool tail = f.nt0 < kPage || f.nt1 < kPage;           // wave-uniform
     if constexpr (MASKV) {
-        if (f.nt0 < kPage || f.nt1 < kPage) mask_v<D>(f.v, f.nt0, f.nt1, c);
+        if (tail) mask_v<D>(f.v, f.nt0, f.nt1, c);
     }
     f32x4 s0[RB], s1[RB];
 #pragma unroll
@@ -180,47 +197,62 @@ __device__ __forceinline__ void compute_step(Step<D> &f, const u32x4 (&qf)[RB][D
         }
     }
     const int lim0 = f.nt0 - 4 * c, lim1 = f.nt1 - 4 * c;   // lane holds tokens 4c..4c+3
-    float x[RB][8], mx[RB];
-#pragma unroll
-    for (int b = 0; b < RB; ++b) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            x[b][j] = j < lim0 ? s0[b][j] : -INFINITY;
-            x[b][4 + j] = j < lim1 ? s1[b][j] : -INFINITY;
-        }
-        mx[b] = fmaxf(fmaxf(fmaxf(x[b][0], x[b][1]), fmaxf(x[b][2], x[b][3])),
-                      fmaxf(fmaxf(x[b][4], x[b][5]), fmaxf(x[b][6], x[b][7])));
-    }
+    float x[RB][8];
     bool need = false;
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
-        mx[b] = row_max4(mx[b]) * scale;                 // base-2 units (scale > 0)
-        need |= mx[b] > m_ref[b] + kRescaleThreshold;
+        const float mneg = -m_ref[b];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[b][j] = __builtin_fmaf(s0[b][j], scale, mneg);
+            x[b][4 + j] = __builtin_fmaf(s1[b][j], scale, mneg);
+        }
+        // checked before masking (an unmasked tail value can at worst send the
+        // step down the exact rescale path below, which masks)
+        const float lm = vmax3(vmax3(x[b][0], x[b][1], x[b][2]), vmax3(x[b][3], x[b][4], x[b][5]),
+                               vmax3(x[b][6], x[b][7], x[b][7]));
+        need |= lm > kRescaleThreshold;                  // also true while m_ref = -inf
+        if (tail) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                x[b][j] = j < lim0 ? x[b][j] : -INFINITY;
+                x[b][4 + j] = j < lim1 ? x[b][4 + j] : -INFINITY;
+            }
+        }
     }
     if (__builtin_amdgcn_ballot_w64(need)) {             // wave-uniform, rare after the first step
 #pragma unroll
         for (int b = 0; b < RB; ++b) {
-            const float m_new = mx[b] > m_ref[b] + kRescaleThreshold ? mx[b] : m_ref[b];
+            float y[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                y[j] = (!tail || j < lim0) ? s0[b][j] * scale : -INFINITY;
+                y[4 + j] = (!tail || j < lim1) ? s1[b][j] * scale : -INFINITY;
+            }
+            float mx = fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])),
+                             fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
+            mx = row_max4(mx);                           // base-2 units (scale > 0)
+            const float m_new = mx > m_ref[b] + kRescaleThreshold ? mx : m_ref[b];
             const float alpha = fast_exp2(m_ref[b] - m_new);   // 1 if unchanged, 0 from -inf
             m_ref[b] = m_new;
             l_run[b] *= alpha;
 #pragma unroll
             for (int j = 0; j < D / 16; ++j) o[b][j] *= alpha;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[b][j] = y[j] - m_new;
         }
     }
     u32x4 pw[RB];
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
-        const float mneg = -m_ref[b];
-        float psum = 0.f;
+        float p[8];
         bf16x8 pb;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const float p = fast_exp2(__builtin_fmaf(x[b][j], scale, mneg));
-            psum += p;
-            pb[j] = (__bf16)p;
+            p[j] = fast_exp2(x[b][j]);
+            pb[j] = (__bf16)p[j];
         }
-        l_run[b] += psum;
+        l_run[b] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         pw[b] = __builtin_bit_cast(u32x4, pb);
     }
 #pragma unroll
@@ -255,8 +287,46 @@ __device__ __forceinline__ void load_q(u32x4 (&qf)[RB][D / 32], const DecodeArgs
     }
 }
 
+// Partial stores and loads.  The fused step hands partials from one
+// workgroup to another inside the launch, possibly across XCDs (each with
+// its own L2), so there they go through buffer instructions with the sc1
+// cache policy -- the device-coherent form the compiler itself uses for
+// device-scope atomic stores and loads: written through the L2, read past
+// any stale copy -- instead of plain stores published by a whole-L2
+// write-back.  The two-launch path writes them with plain stores.
+constexpr int kCoherent = 16;                    // cache-policy bits: sc1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
+}
+
+template <int D, bool FUSED>
+__device__ __forceinline__ void store_partial_o(const DecodeArgs &a, int64_t slot, int d, f32x4 v)
+{
+    if constexpr (FUSED)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), buf_rsrc(a.part_o, a.slots * D * 4),
+                                               (int)(slot * D + d) * 4, 0, kCoherent);
+    else
+        *reinterpret_cast<f32x4 *>(a.part_o + slot * D + d) = v;
+}
+
+template <bool FUSED>
+__device__ __forceinline__ void store_partial_ml(const DecodeArgs &a, int64_t slot, float m, float l)
+{
+    if constexpr (FUSED) {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, m), buf_rsrc(a.part_m, a.slots * 4),
+                                              (int)slot * 4, 0, kCoherent);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, l), buf_rsrc(a.part_l, a.slots * 4),
+                                              (int)slot * 4, 0, kCoherent);
+    } else {
+        a.part_m[slot] = m;
+        a.part_l[slot] = l;
+    }
+}
+
 // Partials of rows row0 + 16b + n: slot = (slot_base + row / G) * Hq + head * G + row % G.
-template <int D, int RB>
+template <int D, int RB, bool FUSED>
 __device__ __forceinline__ void write_partials(const DecodeArgs &a, const WorkItem &it, int row0, int nrows,
                                                int nblk, const f32x4 (&o)[RB][D / 16],
                                                const float (&m_ref)[RB], const float (&l_run)[RB], int n,
@@ -272,13 +342,9 @@ __device__ __forceinline__ void write_partials(const DecodeArgs &a, const WorkIt
         const int row = row0 + 16 * b + n;
         if (row < nrows) {
             const int64_t slot = (int64_t)(it.slot_base + row / G) * a.Hq + it.head * G + row % G;
-            float *po = a.part_o + slot * D + 4 * c;
 #pragma unroll
-            for (int j = 0; j < D / 16; ++j) *reinterpret_cast<f32x4 *>(po + 16 * j) = o[b][j];
-            if (c == 0) {
-                a.part_m[slot] = m_ref[b];
-                a.part_l[slot] = l;
-            }
+            for (int j = 0; j < D / 16; ++j) store_partial_o<D, FUSED>(a, slot, 16 * j + 4 * c, o[b][j]);
+            if (c == 0) store_partial_ml<FUSED>(a, slot, m_ref[b], l);
         }
     }
 }
@@ -303,7 +369,7 @@ __device__ __forceinline__ void load_page_table(const DecodeArgs &a, const WorkI
 // pages straight from HBM into registers (one step in flight while the
 // previous computes) and keeps its own (m, l, o).  At the end the waves put
 // their statistics in LDS and the workgroup writes one merged partial.
-template <int D>
+template <int D, bool FUSED>
 __device__ __forceinline__ void private_item(const DecodeArgs &a, const WorkItem &it, float *mrg, int tid,
                                              int lane, int n, int c)
 {
@@ -372,13 +438,10 @@ __device__ __forceinline__ void private_item(const DecodeArgs &a, const WorkItem
     if (row < nrows) {
         const int G = a.G;
         const int64_t slot = (int64_t)(it.slot_base + row / G) * a.Hq + it.head * G + row % G;
-        float *po = a.part_o + slot * D + d0;
 #pragma unroll
-        for (int v = 0; v < V; ++v) po[v] = acc[v];
-        if (tid % TPR == 0) {
-            a.part_m[slot] = M;
-            a.part_l[slot] = L;
-        }
+        for (int v = 0; v < V; v += 4)
+            store_partial_o<D, FUSED>(a, slot, d0 + v, f32x4{acc[v], acc[v + 1], acc[v + 2], acc[v + 3]});
+        if (tid % TPR == 0) store_partial_ml<FUSED>(a, slot, M, L);
     }
 }
 
@@ -481,7 +544,7 @@ __device__ __forceinline__ void lds_step(Step<D> &f, const uint16_t *slot, int n
     }
 }
 
-template <int D>
+template <int D, bool FUSED>
 __device__ __forceinline__ void shared_item(const DecodeArgs &a, const WorkItem &it, uint16_t *lds, int tid,
                                             int lane, int n, int c)
 {
@@ -527,34 +590,10 @@ __device__ __forceinline__ void shared_item(const DecodeArgs &a, const WorkItem 
             __syncthreads();
         }
     }
-    write_partials<D, 2>(a, it, row0, nrows, nblk, o, m_ref, l_run, n, c);
+    write_partials<D, 2, FUSED>(a, it, row0, nrows, nblk, o, m_ref, l_run, n, c);
 }
 
-// One workgroup per work item: shared items stage KV in LDS for their
-// row-waves; private items split their pages over the waves.
-template <int D>
-__global__ __launch_bounds__(kSharedThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void decode_kernel(DecodeArgs a)
-{
-    constexpr int kTileBytes = 2 * 4 * kPage * D * 2;               // shared path: two LDS tiles
-    constexpr int kMergeBytes = (kWaves * 16 * D + 2 * kWaves * 16) * 4;   // private path: merge buffer
-    constexpr int kLdsBytes = kTileBytes > kMergeBytes ? kTileBytes : kMergeBytes;
-    __shared__ __attribute__((aligned(16))) float lds[kLdsBytes / 4];
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWaveSize - 1);
-    const int n = lane & 15, c = lane >> 4;
-    const WorkItem &it = a.items[blockIdx.x];
-    if (it.mode == kModeShared)
-        shared_item<D>(a, it, reinterpret_cast<uint16_t *>(lds), tid, lane, n, c);
-    else
-        private_item<D>(a, it, lds, tid, lane, n, c);
-}
-
-// One wave per (request, query head): out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i.
-// The (m, l) pairs of up to 64 partials are loaded one per lane, M and the
-// weights come from wave reductions, and the o rows (D floats each) are
-// accumulated with eight row loads in flight.  More than 64 partials are
-// taken in blocks of 64 with the running result rescaled between blocks.
+// ------------------------------------------------------------------ merge
 __device__ __forceinline__ float wave_max(float v)
 {
 #pragma unroll
@@ -562,74 +601,154 @@ __device__ __forceinline__ float wave_max(float v)
     return v;
 }
 
-__device__ __forceinline__ float wave_sum(float v)
+// Where a merge reads its partials and writes its output.
+struct MergeView {
+    const int32_t *merge_off;    // [R+1]
+    const int32_t *merge_rows;   // partial rows of each request
+    const float *part_o, *part_m, *part_l;
+    uint16_t *out;               // [R][Hq][D] bf16
+    int32_t Hq, slots;
+};
+
+// One wave merges the partials of (request r, query head qh) and writes the
+// bf16 output row:  out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i.
+// Lane = (pk, dc): dc picks 4 of the D output dims, pk one of PK = 256 / D
+// partial lanes.  Partials are taken 16 per block, 16 / PK per lane, all
+// their loads issued together; the block maximum comes from a reduction over
+// the pk lanes, the running result is rescaled when it rises, and the pk
+// lanes' sums are added at the end.  COHERENT: sc1 loads (fused step).
+template <int D, bool COHERENT>
+__device__ __forceinline__ void merge_row_wave(const MergeView &v, int r, int qh, int lane)
 {
+    constexpr int CH = D / 4, PK = kWaveSize / CH, NI = 16 / PK;
+    const int pk = lane / CH, dc = lane % CH;
+    const int beg = v.merge_off[r], end = v.merge_off[r + 1];
+    float M = -INFINITY, L = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int kb = beg; kb < end; kb += 16) {
+        int slot[NI];
+        bool ok[NI];
 #pragma unroll
-    for (int k = 32; k >= 1; k >>= 1) v += __shfl_xor(v, k);
-    return v;
+        for (int i = 0; i < NI; ++i) {
+            const int k = kb + pk + PK * i;
+            ok[i] = k < end;
+            slot[i] = v.merge_rows[ok[i] ? k : end - 1] * v.Hq + qh;
+        }
+        float m[NI], l[NI];
+        f32x4 x[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            if constexpr (COHERENT) {
+                l[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                    buf_rsrc(v.part_l, v.slots * 4), slot[i] * 4, 0, kCoherent));
+                m[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                    buf_rsrc(v.part_m, v.slots * 4), slot[i] * 4, 0, kCoherent));
+                x[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                    buf_rsrc(v.part_o, v.slots * D * 4), (slot[i] * D + 4 * dc) * 4, 0, kCoherent));
+            } else {
+                l[i] = v.part_l[slot[i]];
+                m[i] = v.part_m[slot[i]];
+                x[i] = *reinterpret_cast<const f32x4 *>(v.part_o + (int64_t)slot[i] * D + 4 * dc);
+            }
+        }
+        float mb = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            if (ok[i] && l[i] > 0.f) mb = fmaxf(mb, m[i]);
+#pragma unroll
+        for (int sft = CH; sft < kWaveSize; sft <<= 1) mb = fmaxf(mb, __shfl_xor(mb, sft));
+        const float M_new = fmaxf(M, mb);
+        const float rescale = M_new == -INFINITY ? 0.f : fast_exp2(M - M_new);   // 0 on the first block
+        acc *= rescale;
+        L *= rescale;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const float w = (ok[i] && l[i] > 0.f) ? fast_exp2(m[i] - M_new) : 0.f;
+            acc += w * x[i];
+            L += w * l[i];
+        }
+        M = M_new;
+    }
+#pragma unroll
+    for (int sft = CH; sft < kWaveSize; sft <<= 1) {
+        L += __shfl_xor(L, sft);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], sft);
+    }
+    if (pk == 0) {
+        const float inv = 1.0f / L;
+        const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)(acc[0] * inv)) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc[1] * inv)) << 16);
+        const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)(acc[2] * inv)) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc[3] * inv)) << 16);
+        *reinterpret_cast<u32x2 *>(v.out + ((int64_t)r * v.Hq + qh) * D + 4 * dc) = u32x2{lo, hi};
+    }
 }
 
+// Fused step, after an item has written its partials (sc1 stores): wait for
+// them to complete, then count the item in for each of its requests (one
+// counter per request and KV head).  The item that completes a request's
+// count merges that request's G query heads here, one wave per head, and
+// resets the counter for the next step.  lst: LDS, [0] = count, then the
+// completed request ids.
+template <int D>
+__device__ __forceinline__ void finish_item(const DecodeArgs &a, const WorkItem &it, int *lst, int tid)
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0): this wave's partial stores are done
+    __syncthreads();
+    if (tid < it.nreq) {
+        const int r = a.rows[it.row_off + tid];
+        const int need = a.merge_off[r + 1] - a.merge_off[r];
+        int *cp = a.counters + (int64_t)r * a.Hkv + it.head;
+        const int seen = __hip_atomic_fetch_add(cp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (seen == need - 1) {
+            __hip_atomic_store(cp, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            lst[1 + atomicAdd(&lst[0], 1)] = r;
+        }
+    }
+    __syncthreads();
+    const int nlast = lst[0];
+    if (nlast == 0) return;
+    const MergeView v{a.merge_off, a.merge_rows, a.part_o, a.part_m, a.part_l, a.out, a.Hq, a.slots};
+    const int G = a.G;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    for (int t = wave; t < nlast * G; t += kWaves)
+        merge_row_wave<D, true>(v, lst[1 + t / G], it.head * G + t % G, tid & (kWaveSize - 1));
+}
+
+// One workgroup per work item: shared items stage KV in LDS for their
+// row-waves; private items split their pages over the waves.  FUSED: the
+// item that completes a request also merges it (no merge_kernel launch).
+template <int D, bool FUSED>
+__global__ __launch_bounds__(kSharedThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_kernel(DecodeArgs a)
+{
+    constexpr int kTileBytes = 2 * 4 * kPage * D * 2;               // shared path: two LDS tiles
+    constexpr int kMergeBytes = (kWaves * 16 * D + 2 * kWaves * 16) * 4;   // private path: merge buffer
+    constexpr int kLdsBytes = kTileBytes > kMergeBytes ? kTileBytes : kMergeBytes;
+    __shared__ __attribute__((aligned(16))) float lds[kLdsBytes / 4];
+    __shared__ int lst[FUSED ? 1 + kSharedRows : 1];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWaveSize - 1);
+    const int n = lane & 15, c = lane >> 4;
+    const WorkItem &it = a.items[blockIdx.x];
+    if (FUSED && tid == 0) lst[0] = 0;         // read after the item's barriers
+    if (it.mode == kModeShared)
+        shared_item<D, FUSED>(a, it, reinterpret_cast<uint16_t *>(lds), tid, lane, n, c);
+    else
+        private_item<D, FUSED>(a, it, lds, tid, lane, n, c);
+    if constexpr (FUSED) finish_item<D>(a, it, lst, tid);
+}
+
+// Two-launch step: one wave per (request, query head).
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a)
 {
-    constexpr int V = D / 64;   // o values per lane
-    const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
     if (wid >= a.R * a.Hq) return;
-    const int r = wid / a.Hq, h = wid % a.Hq;
-    const int beg = a.merge_off[r], end = a.merge_off[r + 1];
-    float M = -INFINITY, L = 0.f;
-    float acc[V];
-#pragma unroll
-    for (int v = 0; v < V; ++v) acc[v] = 0.f;
-    for (int kb = beg; kb < end; kb += 64) {
-        const int cnt = min(64, end - kb);
-        int slot = 0;
-        float m = -INFINITY, l = 0.f;
-        if (lane < cnt) {
-            slot = a.merge_rows[kb + lane] * a.Hq + h;
-            l = a.part_l[slot];
-            m = l > 0.f ? a.part_m[slot] : -INFINITY;
-        }
-        const float M_new = fmaxf(M, wave_max(m));
-        const float w = (l > 0.f) ? fast_exp2(m - M_new) : 0.f;
-        const float rescale = fast_exp2(M - M_new);   // 0 on the first block
-        L = L * rescale + wave_sum(w * l);
-#pragma unroll
-        for (int v = 0; v < V; ++v) acc[v] *= rescale;
-        M = M_new;
-        for (int k0 = 0; k0 < cnt; k0 += 8) {
-            float x[8][V];
-            float wk[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int k = min(k0 + u, cnt - 1);
-                const int64_t sl = __builtin_amdgcn_readlane(slot, k);
-                const float wu = __builtin_bit_cast(
-                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
-                wk[u] = (k0 + u < cnt) ? wu : 0.f;
-                const float *po = a.part_o + sl * D + lane * V;
-                if (V == 2) {
-                    const f32x2 y = *reinterpret_cast<const f32x2 *>(po);
-                    x[u][0] = y[0];
-                    x[u][V - 1] = y[1];
-                } else {
-                    x[u][0] = po[0];
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-#pragma unroll
-                for (int v = 0; v < V; ++v) acc[v] += wk[u] * x[u][v];
-        }
-    }
-    const float inv = 1.0f / L;
-    uint16_t *ob = a.out + ((int64_t)r * a.Hq + h) * D + lane * V;
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-        const __bf16 y = (__bf16)(acc[v] * inv);
-        ob[v] = __builtin_bit_cast(uint16_t, y);
-    }
+    const MergeView v{a.merge_off, a.merge_rows, a.part_o, a.part_m, a.part_l, a.out, a.Hq, 0};
+    merge_row_wave<D, false>(v, wid / a.Hq, wid % a.Hq, threadIdx.x & (kWaveSize - 1));
 }
 
 __global__ __launch_bounds__(256) void fill_kernel(uint32_t *buf, size_t words, uint32_t value)
@@ -677,10 +796,18 @@ int launch_decode(const DecodeArgs &a, int head_dim, void *stream)
 {
     if (a.n_items <= 0) return 0;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (head_dim == 128)
-        hipLaunchKernelGGL(decode_kernel<128>, dim3(a.n_items), dim3(kSharedThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL(decode_kernel<64>, dim3(a.n_items), dim3(kSharedThreads), 0, s, a);
+    const bool fused = a.counters != nullptr;
+    if (head_dim == 128) {
+        if (fused)
+            hipLaunchKernelGGL((decode_kernel<128, true>), dim3(a.n_items), dim3(kSharedThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL((decode_kernel<128, false>), dim3(a.n_items), dim3(kSharedThreads), 0, s, a);
+    } else {
+        if (fused)
+            hipLaunchKernelGGL((decode_kernel<64, true>), dim3(a.n_items), dim3(kSharedThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL((decode_kernel<64, false>), dim3(a.n_items), dim3(kSharedThreads), 0, s, a);
+    }
     return (int)hipGetLastError();
 }
 

@@ -73,9 +73,16 @@ class TreeDecoder:
         cap.cap_merge_partials(self.plan_h, self.ws.data_ptr(), self.ws.numel() * 4,
                                self.out.data_ptr(), self.stream())
 
-    def step(self):
-        self.decode()
-        self.merge()
+    def fused_step(self):
+        cap.cap_decode_step(self.plan_h, self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(),
+                            self.ws.data_ptr(), self.ws.numel() * 4, self.out.data_ptr(), self.stream())
+
+    def step(self, fused: bool = True):
+        if fused:
+            self.fused_step()
+        else:
+            self.decode()
+            self.merge()
 
     def output_bits(self) -> np.ndarray:
         self.torch.cuda.current_stream(self.device).synchronize()

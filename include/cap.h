@@ -121,7 +121,12 @@ typedef struct cap_plan_opts {
     float rounds;             /* 0 = 2.0; target work items per CU */
     float share_margin;       /* 0 = 1.0; share a node only if saved bytes exceed
                                  margin x added partial bytes */
-    int32_t reserved[4];
+    int32_t order;            /* dispatch order of the work items (workgroups start in
+                                 item order as CUs free up): 0 = default (2); 1 = the
+                                 two item kinds interleaved evenly, each costliest
+                                 first; 2 = costliest first over both kinds; 3 = all
+                                 shared items first, then private ones costliest first */
+    int32_t reserved[3];
 } cap_plan_opts;
 
 /* Plan summary (host-side numbers; bytes are per decode step). */
@@ -205,7 +210,11 @@ cap_status cap_plan_get_view(const cap_plan *plan, cap_plan_view *view);
 
 /* Copy the plan into dev_buf (>= stats.plan_device_bytes, 256-byte aligned)
  * with one asynchronous host-to-device copy.  The plan keeps the host copy
- * alive; free the plan only after the stream has passed this copy.
+ * alive; free the plan only after the stream has passed this copy.  The
+ * buffer ends with the fused step's arrival counters (R x Hkv int32, zero
+ * after the upload and again after every completed cap_decode_step), so it
+ * must stay writable device memory, and one plan buffer serves one fused
+ * step at a time.
  * Errors: CAP_ERR_INVALID_ARG, CAP_ERR_WORKSPACE, CAP_ERR_STATE (tree has no
  * device page table), CAP_ERR_HIP. */
 cap_status cap_plan_upload(cap_plan *plan, void *dev_buf, size_t bytes, cap_stream_t stream);
@@ -228,6 +237,23 @@ cap_status cap_decode_attention(const cap_plan *plan, const void *q, const void 
  * Errors: as cap_decode_attention. */
 cap_status cap_merge_partials(const cap_plan *plan, const void *workspace, size_t ws_bytes,
                               void *out, cap_stream_t stream);
+/* The whole step in one launch: the decode kernel of cap_decode_attention,
+ * with the merge of cap_merge_partials done inside it.  Each work item, once
+ * its partials are written, counts itself in on a per-(request, KV head)
+ * counter in the plan buffer; the item that brings a request's count to its
+ * number of partials merges that request's G query heads with the same
+ * log-sum-exp combination (Capillary Kernels project page, second paragraph:
+ * partial results of one request are reduced into one output) and writes
+ * its rows of bf16 `out` [R][Hq][D] (16-byte aligned), then resets the
+ * counter.  workspace: as cap_decode_attention; its contents afterwards are
+ * unspecified.  Steps that share a plan buffer must not overlap (counters).
+ * Errors: as cap_decode_attention, CAP_ERR_INVALID_ARG for a NULL or
+ * misaligned `out`, CAP_ERR_UNSUPPORTED when the partial o region
+ * (stats.partial_rows x Hq x D x 4 bytes) reaches 2 GiB (32-bit buffer
+ * offsets; the two-call form has no such limit). */
+cap_status cap_decode_step(const cap_plan *plan, const void *q, const void *k_pool,
+                           const void *v_pool, void *workspace, size_t ws_bytes, void *out,
+                           cap_stream_t stream);
 void cap_plan_free(cap_plan *plan);
 
 #ifdef __cplusplus

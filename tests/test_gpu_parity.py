@@ -2,8 +2,10 @@
 
 Bar: |gpu - oracle| <= 4e-3 + 4e-3 * |oracle| for every output element, no
 NaN/Inf.  Pool tails and unused pool pages hold NaN and the partial workspace
-is NaN-poisoned before every run, so an unmasked read or an unwritten slot
-fails the test.
+and the output are NaN-poisoned before every run, so an unmasked read, an
+unwritten slot or an unwritten output row fails the test.  Both step forms
+are checked: the fused cap_decode_step (merge inside the decode launch) and
+cap_decode_attention followed by cap_merge_partials.
 """
 import numpy as np
 import pytest
@@ -24,16 +26,34 @@ def _torch():
     return torch
 
 
-def run_gpu(w, **opts):
+def run_gpu(w, fused=True, repeats=1, **opts):
+    """Run `repeats` steps on one plan (poisoned workspace and output before
+    each); every repeat must give the same bits.  Returns the last output."""
     _torch()
     from decode_attention_prefix_amd.decoder import TreeDecoder
     dec = TreeDecoder(w.tree, w.q, w.k_pool, w.v_pool, **opts)
     try:
-        dec.poison_workspace()
-        dec.step()
-        return dec.output(), dec.output_bits(), dec.stats
+        first = None
+        for _ in range(repeats):
+            dec.poison_workspace()
+            dec.out.fill_(-1)                     # 0xFFFF: a bf16 NaN
+            dec.step(fused=fused)
+            bits = dec.output_bits()
+            if first is None:
+                first = bits
+            else:
+                assert np.array_equal(bits, first), "repeated step changed the output"
+        return dec.output(), bits, dec.stats
     finally:
         dec.close()
+
+
+def run_both(w, ref, what, **opts):
+    """Fused and two-launch steps, each against the oracle."""
+    for fused in (True, False):
+        out, _, st = run_gpu(w, fused=fused, **opts)
+        check(out, ref, f"{what} fused={fused}")
+    return st
 
 
 def check(out, ref, what=""):
@@ -65,36 +85,35 @@ def test_config0_all_plan_variants():
     for mode in (-1, 0, 1):
         for split in (0, 1, 3, 100):
             for shared_rows in (0, 1, 1 << 30):
-                out, _, _ = run_gpu(w, share_mode=mode, split_pages=split, shared_rows=shared_rows)
-                check(out, ref, f"cfg0 mode={mode} split={split} shared_rows={shared_rows}")
+                run_both(w, ref, f"cfg0 mode={mode} split={split} shared_rows={shared_rows}",
+                         share_mode=mode, split_pages=split, shared_rows=shared_rows)
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4])
 def test_full_configs(cfg):
     w, ref = config_case(cfg)
     print(f"config {cfg}: {wl.tree_stats(w.tree)}", flush=True)
-    out, _, st = run_gpu(w)
-    e = check(out, ref, f"cfg{cfg} auto")
+    out, _, st = run_gpu(w, repeats=2)
+    e = check(out, ref, f"cfg{cfg} auto fused")
     print(f"config {cfg}: max abs err {e:.3e}; plan {st}", flush=True)
+    out2, _, _ = run_gpu(w, fused=False)
+    check(out2, ref, f"cfg{cfg} auto two-launch")
     if cfg == 4:
         ctl = wl.control_workload(w)
-        out_c, _, _ = run_gpu(ctl)
-        check(out_c, ref, "cfg4 control batch")
+        run_both(ctl, ref, "cfg4 control batch")
 
 
 @pytest.mark.parametrize("cfg,mode", [(1, 0), (1, 1), (2, 1), (3, 1)])
 def test_full_configs_forced_modes(cfg, mode):
     w, ref = config_case(cfg)
-    out, _, _ = run_gpu(w, share_mode=mode)
-    check(out, ref, f"cfg{cfg} mode={mode}")
+    run_both(w, ref, f"cfg{cfg} mode={mode}", share_mode=mode)
 
 
 @pytest.mark.parametrize("shared_rows", [1, 1 << 30])
 def test_shared_and_private_paths_full_config(shared_rows):
     """Every group on shared workgroups, or every group on private waves."""
     w, ref = config_case(3)
-    out, _, _ = run_gpu(w, shared_rows=shared_rows, split_pages=24)
-    check(out, ref, f"cfg3 shared_rows={shared_rows}")
+    run_both(w, ref, f"cfg3 shared_rows={shared_rows}", shared_rows=shared_rows, split_pages=24)
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -112,8 +131,7 @@ def test_random_small_trees(D, HqHkv):
         for opts in ({}, {"share_mode": 1, "split_pages": 1, "shared_rows": 1},
                      {"share_mode": 0, "shared_rows": 1 << 30},
                      {"split_pages": 3, "shared_rows": 1}, {"split_pages": 2}):
-            out, _, _ = run_gpu(w, **opts)
-            check(out, ref, f"seed={seed} D={D} Hq={Hq} Hkv={Hkv} {opts}")
+            run_both(w, ref, f"seed={seed} D={D} Hq={Hq} Hkv={Hkv} {opts}", **opts)
 
 
 def test_large_logits_and_single_token_requests():
@@ -124,12 +142,35 @@ def test_large_logits_and_single_token_requests():
     w = wl.make_workload(nt, par, paths, 16, 4, 128, rng, q_values=q)
     ref = oracle.decode(w.tree, w.q, w.k_pool, w.v_pool)
     for opts in ({}, {"share_mode": 1, "split_pages": 1}, {"shared_rows": 1}):
-        out, _, _ = run_gpu(w, **opts)
-        check(out, ref, f"stretched {opts}")
+        run_both(w, ref, f"stretched {opts}", **opts)
 
 
-def test_bitwise_deterministic():
+@pytest.mark.parametrize("fused", [True, False])
+def test_bitwise_deterministic(fused):
     w, _ = config_case(0)
-    _, b1, _ = run_gpu(w, split_pages=2)
-    _, b2, _ = run_gpu(w, split_pages=2)
+    _, b1, _ = run_gpu(w, fused=fused, split_pages=2)
+    _, b2, _ = run_gpu(w, fused=fused, split_pages=2, repeats=3)
     assert np.array_equal(b1, b2)
+
+
+def test_fused_counters_reset_across_plans_and_steps():
+    """Many fused steps on one plan, then a re-plan on the same buffers: the
+    arrival counters must be back at zero after every step."""
+    _torch()
+    from decode_attention_prefix_amd.decoder import TreeDecoder
+    rng = np.random.default_rng(5)
+    nt, par, paths = wl.make_random_tree(rng, num_requests=40, max_depth=3, max_len=200,
+                                         num_q_heads=8, num_kv_heads=2, head_dim=128,
+                                         internal_end_prob=0.2, empty_root=False, min_len=1)
+    w = wl.make_workload(nt, par, paths, 8, 2, 128, rng)
+    ref = oracle.decode(w.tree, w.q, w.k_pool, w.v_pool)
+    dec = TreeDecoder(w.tree, w.q, w.k_pool, w.v_pool, split_pages=2)
+    try:
+        for opts in ({"split_pages": 2}, {"split_pages": 1, "share_mode": 1}, {}):
+            dec.plan(**opts)
+            for _ in range(5):
+                dec.out.fill_(-1)
+                dec.step(fused=True)
+                check(dec.output(), ref, f"repeated fused steps {opts}")
+    finally:
+        dec.close()
