@@ -51,6 +51,7 @@ cap_status fail(cap_status st, const char *fmt, ...)
 }
 
 constexpr size_t kAlign = 256;
+constexpr int64_t kMaxPoolPages = (int64_t)1 << 26;   // page-stream entry: (page << 5) | (ntok - 1)
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 }  // namespace
@@ -76,7 +77,7 @@ struct cap_plan {
     const cap_tree *tree = nullptr;
     cap_plan_stats stats{};
     std::vector<WorkItem> items;          // one workgroup each
-    std::vector<int32_t> stream;      // (tree page index << 5) | (ntok - 1)
+    std::vector<int32_t> stream;      // (physical page << 5) | (ntok - 1)
     std::vector<int32_t> rows;        // request ids
     std::vector<int32_t> merge_off, merge_rows;
     // device image
@@ -119,9 +120,12 @@ cap_status build_tree(const cap_attn_desc *attn, const cap_tree_desc *d, cap_tre
     if (R <= 0) return fail(CAP_ERR_BAD_TREE, "num_requests must be > 0");
     if (!d->parent || !d->num_tokens || !d->page_offsets || !d->path_offsets || !d->path_nodes)
         return fail(CAP_ERR_INVALID_ARG, "a tree array pointer is NULL");
-    if (d->num_pool_pages <= 0 || d->num_pool_pages > std::numeric_limits<int32_t>::max())
+    if (d->num_pool_pages <= 0)
         return fail(CAP_ERR_BAD_TREE, "num_pool_pages %lld out of range",
                     (long long)d->num_pool_pages);
+    if (d->num_pool_pages > kMaxPoolPages)
+        return fail(CAP_ERR_UNSUPPORTED, "num_pool_pages %lld above the limit of %lld (page ids share an "
+                    "int32 with the token count)", (long long)d->num_pool_pages, (long long)kMaxPoolPages);
     if (d->page_offsets[0] != 0) return fail(CAP_ERR_BAD_TREE, "page_offsets[0] != 0");
     for (int i = 0; i < N; ++i) {
         const int p = d->parent[i];
@@ -234,7 +238,7 @@ struct Planner {
         for (int64_t p = 0; p < np; ++p) {
             const int64_t left = t.ntok[n] - p * cap::kPage;
             const int nt = (int)std::min<int64_t>(cap::kPage, left);
-            out.push_back((int32_t)(((t.page_off[n] + p) << 5) | (nt - 1)));
+            out.push_back((int32_t)(((int64_t)t.page_ids[t.page_off[n] + p] << 5) | (nt - 1)));
         }
     }
 
@@ -333,8 +337,8 @@ void fill_defaults(cap_plan_opts &o)
     if (o.share_mode == 2) o.share_mode = -1;
     if (o.shared_rows == 0) o.shared_rows = cap::kPrivateRows;
     if (o.num_cus == 0) o.num_cus = 256;
-    if (o.shared_cost == 0.f) o.shared_cost = 4.0f;
-    if (o.rounds == 0.f) o.rounds = 2.0f;
+    if (o.shared_cost == 0.f) o.shared_cost = 2.0f;
+    if (o.rounds == 0.f) o.rounds = 1.5f;
     if (o.share_margin == 0.f) o.share_margin = 1.0f;
     if (o.order == 0) o.order = 2;
 }
@@ -553,8 +557,6 @@ cap_status cap_plan_get_view(const cap_plan *plan, cap_plan_view *v)
 cap_status cap_plan_upload(cap_plan *plan, void *dev_buf, size_t bytes, cap_stream_t stream)
 {
     if (!plan || !dev_buf) return fail(CAP_ERR_INVALID_ARG, "NULL argument");
-    if (!plan->tree->dev_pages)
-        return fail(CAP_ERR_STATE, "the plan's tree has no device page table (uploaded with dev_buf = NULL)");
     if (bytes < plan->dev_bytes || (reinterpret_cast<uintptr_t>(dev_buf) & (kAlign - 1)))
         return fail(CAP_ERR_WORKSPACE, "plan buffer: %zu bytes given, %zu needed (256-byte aligned)",
                     bytes, plan->dev_bytes);
@@ -593,7 +595,6 @@ static cap_status decode_args(const cap_plan *plan, const void *q, const void *k
     a.items = reinterpret_cast<const WorkItem *>(d + plan->off_items);
     a.stream = reinterpret_cast<const int32_t *>(d + plan->off_stream);
     a.rows = reinterpret_cast<const int32_t *>(d + plan->off_rows);
-    a.tree_pages = plan->tree->dev_pages;
     a.q = static_cast<const uint16_t *>(q);
     a.k_pool = static_cast<const uint16_t *>(k_pool);
     a.v_pool = static_cast<const uint16_t *>(v_pool);

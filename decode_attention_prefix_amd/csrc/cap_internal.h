@@ -13,7 +13,6 @@ constexpr int kPage = 16;            // tokens per page
 constexpr int kWaveSize = 64;        // CDNA wavefront
 constexpr int kWaves = 4;            // waves per decode workgroup
 constexpr int kSharedThreads = kWaves * kWaveSize;
-constexpr int kStages = 2;           // shared path: KV steps in flight in registers
 constexpr int kPrivateRows = 16;     // query rows of a private (one-wave) item
 constexpr int kSharedRows = 32 * kWaves;  // query rows of a shared item: 32 per wave
 constexpr int kRowsPerItem = 32;     // the GQA group must divide this
@@ -39,8 +38,7 @@ static_assert(sizeof(WorkItem) == sizeof(cap_work_item), "work item layout");
 
 struct DecodeArgs {
     const WorkItem *items;         // one workgroup each
-    const int32_t *stream;       // page-stream entries: (tree page index << 5) | (ntok - 1)
-    const int32_t *tree_pages;   // tree page index -> physical page
+    const int32_t *stream;       // page-stream entries: (physical page << 5) | (ntok - 1)
     const int32_t *rows;         // request ids of each item's request list
     const uint16_t *q;           // [R][Hq][D] bf16
     const uint16_t *k_pool;      // [pages][Hkv][D/8][16][8] bf16

@@ -72,7 +72,7 @@ constexpr float kRescaleThreshold = 8.0f;
 template <int D>
 struct Step {
     u32x4 k0[D / 32], k1[D / 32];   // QK A operands, page 0 / page 1
-    u32x4 v[D / 16];                // PV A operands: .xy page 0, .zw page 1
+    u32x4 v[D / 16];                // PV A operands: lane (n, c) holds tokens 8(c&1)..+7 of page c>>1
     int nt0, nt1;                   // valid tokens in page 0 / page 1 (nt1 = 0: no page)
 };
 
@@ -105,31 +105,53 @@ __device__ __forceinline__ void load_step(Step<D> &f, const DecodeArgs &a, int h
         f.k0[i] = ld16(kb0 + ((4 * i + c) * kPage + n) * 8);
         f.k1[i] = ld16(kb1 + ((4 * i + c) * kPage + n) * 8);
     }
+    const uint16_t *vb = ((c >> 1) ? vb1 : vb0) + 8 * (c & 1);
 #pragma unroll
-    for (int j = 0; j < D / 16; ++j) {
-        const u32x2 x0 = ld8(vb0 + (16 * j + n) * kPage + 4 * c);
-        const u32x2 x1 = ld8(vb1 + (16 * j + n) * kPage + 4 * c);
-        f.v[j] = u32x4{x0.x, x0.y, x1.x, x1.y};
-    }
+    for (int j = 0; j < D / 16; ++j) f.v[j] = ld16(vb + (16 * j + n) * kPage);
 }
 
-// Zero the V elements of tokens >= nt (page 0: .xy, page 1: .zw) -- those
-// slots may hold NaN, and 0 * NaN would poison the MFMA sum.
+// Zero the V elements of tokens >= nt -- those slots may hold NaN, and
+// 0 * NaN would poison the MFMA sum.  Lane (n, c) holds tokens
+// 8(c & 1) .. 8(c & 1) + 7 of page c >> 1, two per dword.
 template <int D>
 __device__ __forceinline__ void mask_v(u32x4 (&v)[D / 16], int nt0, int nt1, int c)
 {
-    const int t = 4 * c;
-    const uint32_t a0 = (t + 0 < nt0 ? 0x0000FFFFu : 0u) | (t + 1 < nt0 ? 0xFFFF0000u : 0u);
-    const uint32_t a1 = (t + 2 < nt0 ? 0x0000FFFFu : 0u) | (t + 3 < nt0 ? 0xFFFF0000u : 0u);
-    const uint32_t b0 = (t + 0 < nt1 ? 0x0000FFFFu : 0u) | (t + 1 < nt1 ? 0xFFFF0000u : 0u);
-    const uint32_t b1 = (t + 2 < nt1 ? 0x0000FFFFu : 0u) | (t + 3 < nt1 ? 0xFFFF0000u : 0u);
+    const int lim = ((c >> 1) ? nt1 : nt0) - 8 * (c & 1);
+    uint32_t m[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        m[e] = (2 * e < lim ? 0x0000FFFFu : 0u) | (2 * e + 1 < lim ? 0xFFFF0000u : 0u);
 #pragma unroll
     for (int j = 0; j < D / 16; ++j) {
-        v[j].x &= a0;
-        v[j].y &= a1;
-        v[j].z &= b0;
-        v[j].w &= b1;
+        v[j].x &= m[0];
+        v[j].y &= m[1];
+        v[j].z &= m[2];
+        v[j].w &= m[3];
     }
+}
+
+// PV B operand from the packed probabilities.  The QK output leaves lane
+// (n, c) with tokens 4c..4c+3 of page 0 (.xy) and of page 1 (.zw) for row n;
+// the PV MFMA wants lane (n, c) to hold the 8 k-values 8c..8c+7, which this
+// kernel maps to tokens 8(c & 1)..+7 of page c >> 1 -- so each lane's V
+// operand is one 16-byte piece of a page row.  Moving the pieces is a 4 x 4
+// exchange of dword pairs across the four 16-lane rows: a lane-half swap
+// (rows 2,3 of x with rows 0,1 of y) and then a row swap (rows 1,3 of x with
+// rows 0,2 of y) take rows [A0 A1 A2 A3] / [B0 B1 B2 B3] to [A0 A2 B0 B2] /
+// [A1 A3 B1 B3].  One asm block, with the VALU-to-permlane wait states.
+__device__ __forceinline__ u32x4 p_operand(u32x4 pw)
+{
+    uint32_t a0 = pw.x, a1 = pw.y, b0 = pw.z, b1 = pw.w;
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_permlane32_swap_b32 %0, %2\n\t"
+        "v_permlane32_swap_b32 %1, %3\n\t"
+        "s_nop 1\n\t"
+        "v_permlane16_swap_b32 %0, %2\n\t"
+        "v_permlane16_swap_b32 %1, %3\n\t"
+        "s_nop 1"
+        : "+v"(a0), "+v"(a1), "+v"(b0), "+v"(b1));
+    return u32x4{a0, a1, b0, b1};
 }
 
 // max over the four lanes n, n+16, n+32, n+48 that hold one query row, with
@@ -163,27 +185,13 @@ __device__ __forceinline__ float vmax3(float a, float b, float c)
     return r;
 }
 
-// One 2-page step for up to RB 16-row blocks, in phases so the blocks'
-// independent work can overlap: all QK MFMAs, the exponent arguments
-// x = s * scale - m_ref against each row's current reference, one (rare)
-// rescale, the probabilities 2^x, then all PV MFMAs.  The common path needs
-// no cross-lane work: a lane only checks that none of its arguments exceeds
-// the rescale threshold; the exact row maxima are taken (over the four lanes
-// of a row) only when some row must move its reference -- the first step, or
-// a maximum that rose by more than the threshold.  Masking (tokens past nt,
-// a missing second page with nt1 = 0) runs only on tail steps.  MASKV: zero
-// V tails in registers (the shared path zeroes them when it stages the tile
-// in LDS instead).
-template <int D, int RB, bool MASKV>
-__device__ __forceinline__ void compute_step(Step<D> &f, const u32x4 (&qf)[RB][D / 32],
-                                             f32x4 (&o)[RB][D / 16], float (&m_ref)[RB],
-                                             float (&l_run)[RB], int nblk, float scale, int c)
+// S^T tiles of one 2-page step for up to RB 16-row blocks: lane (n, c) gets
+// the logits of tokens 4c..4c+3 of page 0 (s0) and page 1 (s1) for row n.
+template <int D, int RB>
+__device__ __forceinline__ void qk_step(const u32x4 (&k0)[D / 32], const u32x4 (&k1)[D / 32],
+                                        const u32x4 (&qf)[RB][D / 32], f32x4 (&s0)[RB], f32x4 (&s1)[RB],
+                                        int nblk)
 {
-    const bool tail = f.nt0 < kPage || f.nt1 < kPage;           // wave-uniform
-    if constexpr (MASKV) {
-        if (tail) mask_v<D>(f.v, f.nt0, f.nt1, c);
-    }
-    f32x4 s0[RB], s1[RB];
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
         s0[b] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -191,12 +199,33 @@ __device__ __forceinline__ void compute_step(Step<D> &f, const u32x4 (&qf)[RB][D
         if (RB == 1 || b < nblk) {
 #pragma unroll
             for (int i = 0; i < D / 32; ++i) {
-                s0[b] = mfma(f.k0[i], qf[b][i], s0[b]);
-                s1[b] = mfma(f.k1[i], qf[b][i], s1[b]);
+                s0[b] = mfma(k0[i], qf[b][i], s0[b]);
+                s1[b] = mfma(k1[i], qf[b][i], s1[b]);
             }
         }
     }
-    const int lim0 = f.nt0 - 4 * c, lim1 = f.nt1 - 4 * c;   // lane holds tokens 4c..4c+3
+}
+
+// The rest of a step, in phases so the blocks' independent work can overlap:
+// the exponent arguments x = s * scale - m_ref against each row's current
+// reference, one (rare) rescale, the probabilities 2^x, then all PV MFMAs.
+// The common path needs no cross-lane work: a lane only checks that none of
+// its arguments exceeds the rescale threshold; the exact row maxima are taken
+// (over the four lanes of a row) only when some row must move its reference
+// -- the first step, or a maximum that rose by more than the threshold.
+// Masking (tokens past nt, a missing second page with nt1 = 0) runs only on
+// tail steps.  MASKV: also zero the V tails in registers (pool tails may hold
+// anything, and 0 * NaN would poison the sums).
+template <int D, int RB, bool MASKV>
+__device__ __forceinline__ void softmax_pv(const f32x4 (&s0)[RB], const f32x4 (&s1)[RB], u32x4 (&v)[D / 16],
+                                           int nt0, int nt1, f32x4 (&o)[RB][D / 16], float (&m_ref)[RB],
+                                           float (&l_run)[RB], int nblk, float scale, int c)
+{
+    const bool tail = nt0 < kPage || nt1 < kPage;               // wave-uniform
+    if constexpr (MASKV) {
+        if (tail) mask_v<D>(v, nt0, nt1, c);
+    }
+    const int lim0 = nt0 - 4 * c, lim1 = nt1 - 4 * c;   // lane holds tokens 4c..4c+3
     float x[RB][8];
     bool need = false;
 #pragma unroll
@@ -258,10 +287,21 @@ __device__ __forceinline__ void compute_step(Step<D> &f, const u32x4 (&qf)[RB][D
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
         if (RB == 1 || b < nblk) {
+            const u32x4 pb = p_operand(pw[b]);
 #pragma unroll
-            for (int j = 0; j < D / 16; ++j) o[b][j] = mfma(f.v[j], pw[b], o[b][j]);
+            for (int j = 0; j < D / 16; ++j) o[b][j] = mfma(v[j], pb, o[b][j]);
         }
     }
+}
+
+template <int D, int RB, bool MASKV>
+__device__ __forceinline__ void compute_step(Step<D> &f, const u32x4 (&qf)[RB][D / 32],
+                                             f32x4 (&o)[RB][D / 16], float (&m_ref)[RB],
+                                             float (&l_run)[RB], int nblk, float scale, int c)
+{
+    f32x4 s0[RB], s1[RB];
+    qk_step<D, RB>(f.k0, f.k1, qf, s0, s1, nblk);
+    softmax_pv<D, RB, MASKV>(s0, s1, f.v, f.nt0, f.nt1, o, m_ref, l_run, nblk, scale, c);
 }
 
 // Q fragments (B operand of QK) for rows row0 + 16b + n of an item: lane
@@ -358,7 +398,7 @@ __device__ __forceinline__ void load_page_table(const DecodeArgs &a, const WorkI
     lane_nt = 0;
     if (lane < count) {
         const int e = a.stream[it.stream_off + first + lane];
-        lane_pid = a.tree_pages[e >> 5];
+        lane_pid = e >> 5;
         lane_nt = (e & 31) + 1;
     }
 }
@@ -447,148 +487,188 @@ __device__ __forceinline__ void private_item(const DecodeArgs &a, const WorkItem
 
 // ----------------------------------------------------------------- shared path
 // One workgroup, one item of up to kSharedRows rows (nreq x G).  The waves
-// stream each 2-page step of KV once, cooperatively (128-bit loads, kStages
-// steps in flight in registers), stage it in a double-buffered LDS tile, and
-// each wave applies the tile to its own 32 rows.  One barrier per step.
-template <int D>
-struct Stage {
-    static constexpr int kPieces = 8 * D / kSharedThreads;   // 16-byte pieces per thread per step
-    u32x4 x[kPieces];
-};
+// stream each 2-page step of KV once, cooperatively, straight from HBM into
+// a kSlots-deep LDS ring with gfx950's 16-byte global->LDS loads (no staging
+// registers, no LDS write instructions), kSlots - 1 steps ahead of the
+// compute; each wave applies the tile to its own 32 rows.  One barrier per
+// step, after which the slot of the previous step is refilled.
+//
+// Tile of one step: K page 0, K page 1, V page 0, V page 1, each 16 x D bf16
+// (kPage * D elements).  K blocks keep the pool layout ([D/8][16][8]: a
+// wave's fragment read is 1 KB contiguous).  V blocks ([D][16], two 16-byte
+// chunks per dim row) store chunk h of row d at chunk h ^ ((d >> 2) & 1): the
+// sixteen lanes that read chunk h of rows 16j..16j+15 then spread evenly over
+// the banks (two passes, no conflict).  A load lane picks its source chunk so
+// that the chunk lands where this layout wants it.
+constexpr int kSlots = 4;
 
 template <int D>
-__device__ __forceinline__ void issue_stage(Stage<D> &st, const DecodeArgs &a, int head, int npages, int s,
-                                            int lane_pid, int tid)
+struct SharedTile {
+    static constexpr int kBlock = kPage * D;                 // elements of one K or V page block
+    static constexpr int kStep = 4 * kBlock;                  // elements of one step (slot)
+    static constexpr int kPPB = kBlock * 2 / (kWaveSize * 16); // 1 KB pieces per block (one per wave for D=128)
+};
+
+// Global->LDS loads of step `step` into `slot`: piece k of each wave covers
+// block k * kWaves / kPPB ... (kPPB pieces per block, 4 blocks, kWaves waves).
+template <int D>
+__device__ __forceinline__ void issue_dma(const DecodeArgs &a, int head, int npages, int step, int lane_pid,
+                                          uint16_t *slot, int wave, int lane)
 {
-    const int64_t blk = (int64_t)kPage * D;
-    const int nsteps = (npages + 1) >> 1;
-    const int ss = s < nsteps ? s : nsteps - 1;
-    const int i0 = 2 * ss;
+    using T = SharedTile<D>;
+    const int i0 = 2 * step;
     const int i1 = i0 + 1 < npages ? i0 + 1 : i0;
     const int64_t p0 = __builtin_amdgcn_readlane(lane_pid, i0);
     const int64_t p1 = __builtin_amdgcn_readlane(lane_pid, i1);
 #pragma unroll
-    for (int k = 0; k < Stage<D>::kPieces; ++k) {
-        const int p = tid + k * kSharedThreads;     // 16-byte piece of the 4-block stage
-        const int b = p / (2 * D);                  // 0 K page0, 1 K page1, 2 V page0, 3 V page1 (wave-uniform)
+    for (int k = 0; k < T::kPPB; ++k) {
+        const int piece = wave + kWaves * k;                 // 0 .. 4 * kPPB - 1
+        const int b = piece / T::kPPB;                       // 0 K page0, 1 K page1, 2 V page0, 3 V page1
+        const int c = (piece % T::kPPB) * kWaveSize + lane;  // destination 16-byte chunk in the block
+        int src = c;
+        if (b & 2) {                                         // V: row d, chunk h lands at h ^ ((d >> 2) & 1)
+            const int d = c >> 1;
+            src = 2 * d + ((c & 1) ^ ((d >> 2) & 1));
+        }
         const int64_t page = (b & 1) ? p1 : p0;
         const uint16_t *pool = (b & 2) ? a.v_pool : a.k_pool;
-        st.x[k] = ld16(pool + (page * a.Hkv + head) * blk + (p % (2 * D)) * 8);
+        const uint16_t *g = pool + (page * a.Hkv + head) * T::kBlock + src * 8;
+        __builtin_amdgcn_global_load_lds(
+            (const void __attribute__((address_space(1))) *)g,
+            (void __attribute__((address_space(3))) *)(slot + b * T::kBlock + (piece % T::kPPB) * kWaveSize * 8),
+            16, 0, 0);
     }
 }
 
-// LDS tile of one step: K page 0, K page 1, V page 0, V page 1, each 16 x D
-// bf16.  K blocks keep the pool layout (a wave's fragment read is 1 KB
-// contiguous).  V blocks ([D][16], 32-byte rows) store the 8-byte column c of
-// row d at column c ^ ((d >> 2) & 3): the sixteen lanes that read one column of
-// rows 16j..16j+15 then hit sixteen different bank pairs instead of four.
-template <int D>
-__device__ __forceinline__ void write_stage(const Stage<D> &st, uint16_t *slot, int tid, int nt0, int nt1)
+// Wait until this wave's loads of all but the newest `keep` issued steps have
+// landed (and its LDS reads are done), then barrier: every wave's loads for
+// the oldest step are in LDS and every wave has finished the step before.
+// The asm barrier is also a compiler memory barrier; __syncthreads() would
+// drain every outstanding global->LDS load instead.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0()
 {
-#pragma unroll
-    for (int k = 0; k < Stage<D>::kPieces; ++k) {
-        const int p = tid + k * kSharedThreads;
-        if (p < 4 * D) {                                  // K blocks: as in the pool
-            *reinterpret_cast<u32x4 *>(slot + p * 8) = st.x[k];
-        } else {                                          // V blocks: swizzled 8-byte columns
-            const int q = p % (2 * D);                    // piece within the V block
-            const int d = q >> 1, h = q & 1;              // row, 16-byte half (tokens 8h..8h+7)
-            const int sw = (d >> 2) & 3;
-            u32x4 x = st.x[k];
-            const int nt = p < 6 * D ? nt0 : nt1;         // V page 0 or V page 1 (wave-uniform)
-            if (nt < kPage) {                             // zero tokens >= nt (tails may hold NaN)
-                const int lim = nt - 8 * h;
-                x.x &= (lim > 0 ? 0x0000FFFFu : 0u) | (lim > 1 ? 0xFFFF0000u : 0u);
-                x.y &= (lim > 2 ? 0x0000FFFFu : 0u) | (lim > 3 ? 0xFFFF0000u : 0u);
-                x.z &= (lim > 4 ? 0x0000FFFFu : 0u) | (lim > 5 ? 0xFFFF0000u : 0u);
-                x.w &= (lim > 6 ? 0x0000FFFFu : 0u) | (lim > 7 ? 0xFFFF0000u : 0u);
-            }
-            uint16_t *row = slot + (p - q) * 8 + d * kPage;
-            *reinterpret_cast<u32x2 *>(row + ((2 * h) ^ sw) * 4) = u32x2{x.x, x.y};
-            *reinterpret_cast<u32x2 *>(row + ((2 * h + 1) ^ sw) * 4) = u32x2{x.z, x.w};
-        }
-    }
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0070 | (N & 15) | ((N >> 4) << 14));   // vmcnt(N) expcnt(7) lgkmcnt(0)
 }
 
-// Valid tokens of the two pages of step s (0 for a missing second page).
-__device__ __forceinline__ void step_tokens(int npages, int s, int lane_nt, int &nt0, int &nt1)
+template <int PPB>
+__device__ __forceinline__ void ring_barrier(int keep)
 {
-    const int nsteps = (npages + 1) >> 1;
-    const int ss = s < nsteps ? s : nsteps - 1;
-    const int i0 = 2 * ss;
-    nt0 = __builtin_amdgcn_readlane(lane_nt, i0);
-    nt1 = i0 + 1 < npages ? __builtin_amdgcn_readlane(lane_nt, i0 + 1) : 0;
+    if (keep >= 3)
+        wait_vm_lgkm0<3 * PPB>();
+    else if (keep == 2)
+        wait_vm_lgkm0<2 * PPB>();
+    else if (keep == 1)
+        wait_vm_lgkm0<PPB>();
+    else
+        wait_vm_lgkm0<0>();
+    asm volatile("s_barrier" ::: "memory");
 }
 
-// MFMA fragments of one step from the LDS tile.
+// QK operands (K page blocks) of one step from the LDS tile.
 template <int D>
-__device__ __forceinline__ void lds_step(Step<D> &f, const uint16_t *slot, int npages, int s, int lane_nt,
-                                         int n, int c)
+__device__ __forceinline__ void lds_k(u32x4 (&k0)[D / 32], u32x4 (&k1)[D / 32], const uint16_t *slot, int n,
+                                      int c)
 {
-    const int blk = kPage * D;
-    const int i0 = 2 * s;
-    const bool has1 = i0 + 1 < npages;
-    f.nt0 = __builtin_amdgcn_readlane(lane_nt, i0);
-    f.nt1 = has1 ? __builtin_amdgcn_readlane(lane_nt, i0 + 1) : 0;
+    constexpr int blk = SharedTile<D>::kBlock;
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) {
-        f.k0[i] = *reinterpret_cast<const u32x4 *>(slot + ((4 * i + c) * kPage + n) * 8);
-        f.k1[i] = *reinterpret_cast<const u32x4 *>(slot + blk + ((4 * i + c) * kPage + n) * 8);
+        k0[i] = *reinterpret_cast<const u32x4 *>(slot + ((4 * i + c) * kPage + n) * 8);
+        k1[i] = *reinterpret_cast<const u32x4 *>(slot + blk + ((4 * i + c) * kPage + n) * 8);
     }
-    const int col = (c ^ ((n >> 2) & 3)) * 4;            // rows 16j + n share (n >> 2) & 3
+}
+
+// PV operands (V page blocks) of one step from the LDS tile: lane (n, c)
+// reads tokens 8(c & 1)..+7 of row 16j + n of page c >> 1, one 16-byte chunk.
+template <int D>
+__device__ __forceinline__ void lds_v(u32x4 (&v)[D / 16], const uint16_t *slot, int n, int c)
+{
+    constexpr int blk = SharedTile<D>::kBlock;
+    const uint16_t *vb = slot + (2 + (c >> 1)) * blk + 8 * ((c & 1) ^ ((n >> 2) & 1));
 #pragma unroll
-    for (int j = 0; j < D / 16; ++j) {
-        const u32x2 x0 = *reinterpret_cast<const u32x2 *>(slot + 2 * blk + (16 * j + n) * kPage + col);
-        const u32x2 x1 = *reinterpret_cast<const u32x2 *>(slot + 3 * blk + (16 * j + n) * kPage + col);
-        f.v[j] = u32x4{x0.x, x0.y, x1.x, x1.y};
-    }
+    for (int j = 0; j < D / 16; ++j) v[j] = *reinterpret_cast<const u32x4 *>(vb + (16 * j + n) * kPage);
+}
+
+// Ring bookkeeping shared by the computing and the idle waves: the prologue
+// loads steps 0..kSlots-1 (one per slot) and waits for step 0; before step
+// s + 1 is read, ring_next waits for it, and (from s = 1 on) refills the slot
+// of step s - 1, which every wave finished reading before this barrier, with
+// step s + kSlots - 1.
+template <int D>
+__device__ __forceinline__ void ring_start(const DecodeArgs &a, int h, int np, int nsteps, int lane_pid,
+                                           uint16_t *lds, int wave, int lane)
+{
+#pragma unroll
+    for (int q = 0; q < kSlots; ++q)
+        if (q < nsteps) issue_dma<D>(a, h, np, q, lane_pid, lds + q * SharedTile<D>::kStep, wave, lane);
+    ring_barrier<SharedTile<D>::kPPB>(min(kSlots, nsteps) - 1);
+}
+
+template <int D>
+__device__ __forceinline__ void ring_next(const DecodeArgs &a, int h, int np, int nsteps, int s, int lane_pid,
+                                          uint16_t *lds, int wave, int lane)
+{
+    // issued so far: steps 0 .. min(nsteps, max(kSlots, s + kSlots - 1)) - 1; wait for step s + 1
+    const int issued = min(nsteps, max(kSlots, s + kSlots - 1));
+    ring_barrier<SharedTile<D>::kPPB>(issued - (s + 2));
+    const int nxt = s + kSlots - 1;
+    if (s >= 1 && nxt < nsteps)
+        issue_dma<D>(a, h, np, nxt, lane_pid, lds + (nxt % kSlots) * SharedTile<D>::kStep, wave, lane);
 }
 
 template <int D, bool FUSED>
 __device__ __forceinline__ void shared_item(const DecodeArgs &a, const WorkItem &it, uint16_t *lds, int tid,
                                             int lane, int n, int c)
 {
-    const int wave = tid >> 6;
+    using T = SharedTile<D>;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nrows = it.nreq * a.G;
     const int row0 = 32 * wave;
     const int nblk = nrows > row0 ? min(2, (nrows - row0 + 15) >> 4) : 0;
+    int lane_pid, lane_nt;
+    load_page_table(a, it, 0, it.npages, lane, lane_pid, lane_nt);
     u32x4 qf[2][D / 32];
-    load_q<D, 2>(qf, a, it, row0, nrows, n, c);
+    load_q<D, 2>(qf, a, it, row0, nrows, n, c);         // before the ring loads: loads land in order
+    const int nsteps = (it.npages + 1) >> 1;
+    const int h = it.head, np = it.npages;
+    ring_start<D>(a, h, np, nsteps, lane_pid, lds, wave, lane);
+
     f32x4 o[2][D / 16];
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int j = 0; j < D / 16; ++j) o[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_ref[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-    int lane_pid, lane_nt;
-    load_page_table(a, it, 0, it.npages, lane, lane_pid, lane_nt);
-
-    const int nsteps = (it.npages + 1) >> 1;
     const float sc = a.scale_log2;
-    uint16_t *slot0 = lds, *slot1 = lds + 4 * kPage * D;
-    const int h = it.head, np = it.npages;
-    Step<D> f;
-    Stage<D> r[kStages];                            // stage q lives in r[q % kStages] until written to LDS
-#pragma unroll
-    for (int q = 0; q < kStages; ++q) issue_stage<D>(r[q], a, h, np, q, lane_pid, tid);
-    int t0, t1;
-    step_tokens(np, 0, lane_nt, t0, t1);
-    write_stage<D>(r[0], slot0, tid, t0, t1);
-    __syncthreads();
-    issue_stage<D>(r[0], a, h, np, kStages, lane_pid, tid);
-    for (int s = 0; s < nsteps; s += kStages) {
-#pragma unroll
-        for (int u = 0; u < kStages; ++u) {             // kStages is even: step s + u uses slot u % 2
-            if (s + u >= nsteps) break;
-            if (nblk) {
-                lds_step<D>(f, (u & 1) ? slot1 : slot0, np, s + u, lane_nt, n, c);
-                compute_step<D, 2, false>(f, qf, o, m_ref, l_run, nblk, sc, c);
+    // A wave with rows computes both of its 16-row blocks (rows past nrows
+    // have zero Q and are not written): wave 0 always has two, and the waves
+    // wait for each other every step.  Software-pipelined: the QK MFMAs of
+    // step s + 1 are issued before the softmax of step s, so the matrix cores
+    // work while the vector ALUs do the softmax.  A wave without rows only
+    // keeps the ring going.
+    if (nblk > 0) {
+        u32x4 k0[D / 32], k1[D / 32], v[D / 16];
+        f32x4 sa0[2], sa1[2], sb0[2], sb1[2];
+        lds_k<D>(k0, k1, lds, n, c);
+        qk_step<D, 2>(k0, k1, qf, sa0, sa1, 2);
+        auto half = [&](int s, f32x4 (&c0)[2], f32x4 (&c1)[2], f32x4 (&n0)[2], f32x4 (&n1)[2]) {
+            if (s + 1 < nsteps) {
+                ring_next<D>(a, h, np, nsteps, s, lane_pid, lds, wave, lane);
+                lds_k<D>(k0, k1, lds + ((s + 1) % kSlots) * T::kStep, n, c);
+                qk_step<D, 2>(k0, k1, qf, n0, n1, 2);
             }
-            step_tokens(np, s + u + 1, lane_nt, t0, t1);
-            write_stage<D>(r[(u + 1) % kStages], (u & 1) ? slot0 : slot1, tid, t0, t1);
-            issue_stage<D>(r[(u + 1) % kStages], a, h, np, s + u + 1 + kStages, lane_pid, tid);
-            __syncthreads();
+            const int nt0 = __builtin_amdgcn_readlane(lane_nt, 2 * s);
+            const int nt1 = 2 * s + 1 < np ? __builtin_amdgcn_readlane(lane_nt, 2 * s + 1) : 0;
+            lds_v<D>(v, lds + (s % kSlots) * T::kStep, n, c);
+            softmax_pv<D, 2, true>(c0, c1, v, nt0, nt1, o, m_ref, l_run, 2, sc, c);
+        };
+        for (int s = 0; s < nsteps; s += 2) {
+            half(s, sa0, sa1, sb0, sb1);
+            if (s + 1 < nsteps) half(s + 1, sb0, sb1, sa0, sa1);
         }
+    } else {
+        for (int s = 0; s + 1 < nsteps; ++s) ring_next<D>(a, h, np, nsteps, s, lane_pid, lds, wave, lane);
     }
     write_partials<D, 2, FUSED>(a, it, row0, nrows, nblk, o, m_ref, l_run, n, c);
 }
@@ -724,7 +804,7 @@ template <int D, bool FUSED>
 __global__ __launch_bounds__(kSharedThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_kernel(DecodeArgs a)
 {
-    constexpr int kTileBytes = 2 * 4 * kPage * D * 2;               // shared path: two LDS tiles
+    constexpr int kTileBytes = kSlots * SharedTile<D>::kStep * 2;  // shared path: the LDS ring
     constexpr int kMergeBytes = (kWaves * 16 * D + 2 * kWaves * 16) * 4;   // private path: merge buffer
     constexpr int kLdsBytes = kTileBytes > kMergeBytes ? kTileBytes : kMergeBytes;
     __shared__ __attribute__((aligned(16))) float lds[kLdsBytes / 4];

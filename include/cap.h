@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define CAP_ABI_VERSION 1
+#define CAP_ABI_VERSION 2
 
 typedef enum cap_status {
     CAP_OK = 0,
@@ -85,6 +85,8 @@ typedef struct cap_attn_desc {
  *                     pages page_ids[page_offsets[i] .. page_offsets[i+1]).
  *  page_ids[..]       physical page indices into the K/V pools, each in
  *                     [0, num_pool_pages), no page owned twice.
+ *  num_pool_pages     pages in the pools, at most 2^26 (CAP_ERR_UNSUPPORTED
+ *                     above: a plan packs page id and token count in 32 bits).
  *  path_offsets[R+1]  CSR into path_nodes; request r's path runs from a root
  *                     down to the node where its context ends; consecutive
  *                     entries are parent and child.  Every request must have
@@ -116,9 +118,9 @@ typedef struct cap_plan_opts {
                                  to 16 rows, pages split over the 4 waves).  G > 16
                                  always uses shared items */
     int32_t num_cus;          /* 0 = 256 (MI355X); used by the cost model */
-    float shared_cost;        /* 0 = 4.0; cost of a shared item's page relative to a
+    float shared_cost;        /* 0 = 2.0; cost of a shared item's page relative to a
                                  private item's page, used to size items */
-    float rounds;             /* 0 = 2.0; target work items per CU */
+    float rounds;             /* 0 = 1.5; target work items per CU (two run at once) */
     float share_margin;       /* 0 = 1.0; share a node only if saved bytes exceed
                                  margin x added partial bytes */
     int32_t order;            /* dispatch order of the work items (workgroups start in
@@ -167,7 +169,8 @@ typedef struct cap_work_item {
 } cap_work_item;
 
 /* Read-only host view of a plan (pointers valid until cap_plan_free).
- * Page-stream entry e: tree page index = e >> 5, valid tokens = (e & 31) + 1.
+ * Page-stream entry e: physical pool page = e >> 5 (resolved from the tree's
+ * page table when the plan is built), valid tokens = (e & 31) + 1.
  * Partial slot of item row i (request position i/G, query head head*G + i%G):
  *   (slot_base + i/G) * Hq + head*G + i%G.
  * Request r's partial rows: merge_rows[merge_off[r] .. merge_off[r+1]). */
@@ -186,12 +189,14 @@ void cap_plan_opts_default(cap_plan_opts *opts);
 cap_status cap_tree_device_bytes(const cap_attn_desc *attn, const cap_tree_desc *tree,
                                  size_t *bytes);
 
-/* Validate the tree, derive node->requests lists and context lengths, and copy
- * the page table into dev_buf (>= cap_tree_device_bytes, 16-byte aligned) with
- * one asynchronous host-to-device copy on `stream`.  dev_buf may be NULL: the
- * tree is then validated and can be planned, but not used for decoding.
- * The host arrays may be freed on return.  On success *out owns a handle the
- * caller releases with cap_tree_free (after the stream has passed the copy).
+/* Validate the tree and derive node->requests lists and context lengths.
+ * Plans built from the tree carry the physical page ids they stream, so the
+ * kernels never read the tree's page table; dev_buf is optional (may be NULL)
+ * and, when given (>= cap_tree_device_bytes, 16-byte aligned), receives a
+ * device copy of page_ids with one asynchronous copy on `stream` for callers
+ * that want the table on the GPU.  The host arrays may be freed on return.
+ * On success *out owns a handle the caller releases with cap_tree_free
+ * (after the stream has passed the copy, if one was made).
  * Errors: CAP_ERR_INVALID_ARG (NULL desc/out), CAP_ERR_UNSUPPORTED (shape),
  * CAP_ERR_BAD_TREE (parents, page counts, page ids, paths, empty requests),
  * CAP_ERR_WORKSPACE (dev_bytes too small), CAP_ERR_HIP (copy failed). */
@@ -215,8 +220,7 @@ cap_status cap_plan_get_view(const cap_plan *plan, cap_plan_view *view);
  * after the upload and again after every completed cap_decode_step), so it
  * must stay writable device memory, and one plan buffer serves one fused
  * step at a time.
- * Errors: CAP_ERR_INVALID_ARG, CAP_ERR_WORKSPACE, CAP_ERR_STATE (tree has no
- * device page table), CAP_ERR_HIP. */
+ * Errors: CAP_ERR_INVALID_ARG, CAP_ERR_WORKSPACE, CAP_ERR_HIP. */
 cap_status cap_plan_upload(cap_plan *plan, void *dev_buf, size_t bytes, cap_stream_t stream);
 
 /* Launch the decode kernel: every work item streams its KV pages once for

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), f"libcap.so does not export {n}"
     assert set(cap.EXPORTED) == names
-    assert cap.cap_abi_version() == 1
+    assert cap.cap_abi_version() == 2
 
 
 def small_tree(**over):
@@ -90,19 +90,30 @@ def test_planner_rejects_bad_options():
         cap.cap_tree_free(h)
 
 
-def test_plan_upload_needs_device_tree():
+def test_decode_needs_uploaded_plan():
     h = cap.cap_tree_upload(small_tree())
     p = cap.cap_plan_step(h)
     try:
-        with pytest.raises(cap.CapError) as e:
-            cap.cap_plan_upload(p, 1 << 20, 1 << 20)
-        assert e.value.status == 6
-        with pytest.raises(cap.CapError) as e:
-            cap.cap_decode_attention(p, 256, 256, 256, 256, 1 << 20)
-        assert e.value.status == 6
+        for call in (lambda: cap.cap_decode_attention(p, 256, 256, 256, 256, 1 << 20),
+                     lambda: cap.cap_decode_step(p, 256, 256, 256, 256, 1 << 20, 256),
+                     lambda: cap.cap_merge_partials(p, 256, 1 << 20, 256)):
+            with pytest.raises(cap.CapError) as e:
+                call()
+            assert e.value.status == 6
+        with pytest.raises(cap.CapError) as e:          # too small a plan buffer
+            cap.cap_plan_upload(p, 256, 16)
+        assert e.value.status == 3
     finally:
         cap.cap_plan_free(p)
         cap.cap_tree_free(h)
+
+
+def test_pool_page_limit():
+    t = small_tree()
+    t.num_pool_pages = (1 << 26) + 1
+    with pytest.raises(cap.CapError) as e:
+        cap.cap_tree_upload(t)
+    assert e.value.status == 4
 
 
 def check_coverage(tree, plan_handle):
@@ -120,7 +131,7 @@ def check_coverage(tree, plan_handle):
         for n in tree.path(r):
             for p in range(int(tree.page_offsets[n]), int(tree.page_offsets[n + 1])):
                 nt = min(16, int(tree.num_tokens[n]) - 16 * (p - int(tree.page_offsets[n])))
-                s.append((p, nt))
+                s.append((int(tree.page_ids[p]), nt))      # plans carry physical page ids
         want[r] = sorted(s)
     got = {(r, h): [] for r in range(R) for h in range(Hkv)}
     slot_writes = np.zeros(int(st["partial_rows"]) * Hq, np.int64)
