@@ -4,12 +4,15 @@
 A step is one pass of the whole path over one synthetic batch whose inputs
 are resident in HBM: by default the decode kernel (partials) followed by the
 merge kernel (bf16 output); with --fused one cap_decode_step launch (decode
-kernel with the per-request merge done by the item that completes it).  Before every step (warm-up and timed) a 1 GiB read of another
-buffer evicts L2 and the 256 MB Infinity Cache, so KV is read from HBM, not
-from cache; a read leaves clean lines behind, so no write-back of the flush
-competes with the step.  Step time
-is the HIP-event time of the step's kernels on the stream they run on; the
-planner and the uploads run once, before timing.
+kernel with the per-request merge done by the item that completes it).
+Before every step (warm-up and timed) a 1 GiB read of another buffer evicts
+L2 and the 256 MB Infinity Cache, so KV is read from HBM, not from cache; a
+read leaves clean lines behind, so no write-back of the flush competes with
+the step.  Step time is the HIP-event time around the step's kernels on the
+stream they run on (no event between them); the decode kernel's own launch
+time, for the roofline, comes from a separate timed loop of that kernel
+alone under the same eviction.  The planner and the uploads run once,
+before timing.
 
 Prints one JSON line.  Default workload: the 64-request shared-system-prompt
 tree (4096-token root, suffixes U[256,1024], 32 q / 8 KV heads, D=128).
@@ -37,9 +40,10 @@ def kernel_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def load_traffic(cfg: int):
+def load_traffic(cfg: int, kernel: str):
     """HBM bytes per decode launch from a committed rocprofv3 --pmc summary,
-    if it was taken on the current kernel source; else None."""
+    if it was taken on the current kernel source and the same kernel; else
+    None."""
     path = TRAFFIC_FILE.format(cfg=cfg)
     if not os.path.exists(path):
         return None
@@ -48,7 +52,7 @@ def load_traffic(cfg: int):
         if ":" in line:
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256_16") != kernel_hash():
+    if kv.get("kernel_source_sha256_16") != kernel_hash() or kv.get("kernel") != kernel:
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -154,38 +158,65 @@ def main():
     del probe
 
     def one_step(evs=None):
+        # events only around the whole step: an event recorded between the two
+        # kernels would itself add a few microseconds of queue overhead
         if args.flush_mb > 0:
             evict()
         if evs is not None:
             evs[0].record(stream)
-        if not args.fused:
-            dec.decode()
-            if evs is not None:
-                evs[1].record(stream)
-            dec.merge()
-        else:
+        if args.fused:
             dec.fused_step()
-            if evs is not None:
-                evs[1].record(stream)
+        else:
+            dec.decode()
+            dec.merge()
         if evs is not None:
-            evs[2].record(stream)
+            evs[1].record(stream)
 
     for _ in range(args.warmup):
         one_step()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
     for k in range(args.steps):
         one_step(events[k])
     torch.cuda.synchronize(dev)
     wall_s = time.perf_counter() - t0
-    dec_ms = [e[0].elapsed_time(e[1]) for e in events]
-    mrg_ms = [e[1].elapsed_time(e[2]) for e in events]
-    step_ms = [a + b for a, b in zip(dec_ms, mrg_ms)]
+    step_ms = [e[0].elapsed_time(e[1]) for e in events]
     mean_ms = statistics.fmean(step_ms)
     med_ms = statistics.median(step_ms)
     srt = sorted(step_ms)
     p90_ms = srt[min(len(srt) - 1, int(round(0.9 * (len(srt) - 1))))]
+
+    # the dominant kernel alone, same inputs and cache state, for the roofline:
+    # HIP events on the stream it runs on, around each launch
+    def kernel_only(evs):
+        if args.flush_mb > 0:
+            evict()
+        evs[0].record(stream)
+        if args.fused:
+            dec.fused_step()
+        else:
+            dec.decode()
+        evs[1].record(stream)
+
+    kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        kernel_only(kev[k])
+    torch.cuda.synchronize(dev)
+    dec_ms = [e[0].elapsed_time(e[1]) for e in kev]
+    if args.fused:
+        mrg_ms = None
+    else:
+        mev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for k in range(args.steps):
+            if args.flush_mb > 0:
+                evict()
+            dec.decode()
+            mev[k][0].record(stream)
+            dec.merge()
+            mev[k][1].record(stream)
+        torch.cuda.synchronize(dev)
+        mrg_ms = [e[0].elapsed_time(e[1]) for e in mev]
 
     uniq = st_tree["unique_kv_bytes"]
     value = uniq / (mean_ms * 1e-3) / 1e9
@@ -194,7 +225,8 @@ def main():
     # the fused launch also writes the bf16 output
     alg_bytes_decode = uniq + st_tree["q_bytes"] + (st_tree["out_bytes"] if fused else 0)
     achieved = alg_bytes_decode / (dec_mean * 1e-3) / 1e9
-    traffic = load_traffic(args.config) if not args.control else None
+    kernel_name = f"decode_kernel<{w.tree.head_dim}, {'true' if fused else 'false'}>"
+    traffic = load_traffic(args.config, kernel_name) if not args.control else None
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -222,7 +254,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
-            "kernel": f"decode_kernel<{w.tree.head_dim}, {'true' if fused else 'false'}>",
+            "kernel": kernel_name,
             "algorithmic_bytes_per_launch": alg_bytes_decode,
             "decode_us_mean": round(dec_mean * 1e3, 3),
         },
@@ -233,7 +265,7 @@ def main():
         "t_decode_us": {"mean": round(dec_mean * 1e3, 3), "median": round(statistics.median(dec_ms) * 1e3, 3)},
         "step_form": "fused cap_decode_step" if fused else "cap_decode_attention + cap_merge_partials",
         "t_merge_us": ({"mean": round(statistics.fmean(mrg_ms) * 1e3, 3),
-                        "median": round(statistics.median(mrg_ms) * 1e3, 3)} if not fused else None),
+                        "median": round(statistics.median(mrg_ms) * 1e3, 3)} if mrg_ms else None),
         "t_step_us": {"mean": round(mean_ms * 1e3, 3), "median": round(med_ms * 1e3, 3),
                       "min": round(srt[0] * 1e3, 3), "p90": round(p90_ms * 1e3, 3)},
         "value_median_step": round(uniq / (med_ms * 1e-3) / 1e9, 2),

@@ -1,0 +1,124 @@
+"""Turn rocprofv3 output of bench.py runs into the short text summaries kept
+under profiles/ (kernel-trace statistics and HBM traffic per decode launch).
+
+Usage (after the three rocprofv3 runs named in each summary's header):
+
+    python -m decode_attention_prefix_amd.prof_summary --config 1 \
+        --kt <dir with kt_kernel_stats.csv> --fetch <dir> --write <dir> [--out profiles]
+
+Traffic: FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the decode kernel,
+each scaled by what the same counter reads for bench.py's copy kernel over a
+buffer of known size (--copy-probe-mb in the counter runs): the copy kernel
+reads and writes exactly that many bytes, so scale = bytes / counter reading.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import os
+import statistics
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KERNEL_SRC = os.path.join(ROOT, "decode_attention_prefix_amd", "csrc", "cap_kernels.hip")
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _short(name: str) -> str:
+    for key in ("decode_kernel", "merge_kernel", "read_kernel", "fill_kernel", "copy_kernel"):
+        if key in name:
+            tail = name[name.index(key):]
+            return tail.split("(")[0]
+    return name.split("(")[0][:60]
+
+
+def kernel_stats(kt_dir: str) -> list[tuple[str, int, float, float, float]]:
+    rows = []
+    with open(os.path.join(kt_dir, "kt_kernel_stats.csv")) as f:
+        for r in csv.DictReader(f):
+            rows.append((_short(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                         float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+    return rows
+
+
+def counter_means(pmc_dir: str, counter: str) -> dict[str, float]:
+    vals: dict[str, list[float]] = defaultdict(list)
+    with open(os.path.join(pmc_dir, "pmc_counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                vals[_short(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return {k: statistics.fmean(v) for k, v in vals.items()}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--config", type=int, required=True)
+    ap.add_argument("--workload", default="", help="one-line workload description")
+    ap.add_argument("--kt", required=True)
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--copy-mb", type=int, default=512)
+    ap.add_argument("--alg-bytes", type=float, required=True,
+                    help="algorithmic bytes per decode launch (unique K+V + Q [+ out])")
+    ap.add_argument("--kernel", default="decode_kernel<128, false>")
+    ap.add_argument("--bench-args", default="--no-cpu-baseline")
+    ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
+    a = ap.parse_args(argv)
+    h = kernel_hash()
+    cfg = a.config
+
+    kt = kernel_stats(a.kt)
+    lines = [f"rocprofv3 kernel-trace summary: bench.py --config {cfg} ({a.workload})",
+             f"command: cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o kt -- "
+             f"python3 <repo>/bench.py --config {cfg} {a.bench_args}",
+             f"kernel_source_sha256_16: {h}", "",
+             f"{'kernel':40s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
+    for name, calls, avg, mn, mx in kt:
+        lines.append(f"{name:40s} {calls:6d} {avg:9.3f} {mn:9.3f} {mx:9.3f}")
+    lines += ["", "(read_kernel and fill_kernel are the bench's cache-eviction read and buffer setup)"]
+    with open(os.path.join(a.out, f"decode_kernel_cfg{cfg}_kernel_trace.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    fetch = counter_means(a.fetch, "FETCH_SIZE")
+    write = counter_means(a.write, "WRITE_SIZE")
+    copy_kib = a.copy_mb * 1024.0
+    fs = copy_kib / fetch["copy_kernel"]
+    ws = copy_kib / write["copy_kernel"]
+    dk = [k for k in fetch if k.startswith("decode_kernel")][0]
+    fb = fetch[dk] * fs * 1024.0
+    wb = write[dk] * ws * 1024.0
+    mk = [k for k in fetch if k.startswith("merge_kernel")]
+    lines = [f"HBM traffic of one {a.kernel} launch, bench.py --config {cfg} ({a.workload})",
+             "commands (each its own run):",
+             f"  cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out> -o pmc -- python3 "
+             f"<repo>/bench.py --config {cfg} --no-cpu-baseline --steps 3 --warmup 1 --copy-probe-mb {a.copy_mb}",
+             f"  cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out> -o pmc -- python3 "
+             f"<repo>/bench.py --config {cfg} --no-cpu-baseline --steps 3 --warmup 1 --copy-probe-mb {a.copy_mb}",
+             f"kernel_source_sha256_16: {h}",
+             f"kernel: {a.kernel}",
+             f"copy_kernel_{a.copy_mb}MiB_fetch_kib: {fetch['copy_kernel']:.1f}",
+             f"copy_kernel_{a.copy_mb}MiB_write_kib: {write['copy_kernel']:.1f}",
+             f"fetch_scale: {fs:.5f}",
+             f"write_scale: {ws:.5f}",
+             f"decode_fetch_kib_per_dispatch: {fetch[dk]:.1f}",
+             f"decode_write_kib_per_dispatch: {write[dk]:.1f}"]
+    if mk:
+        lines += [f"merge_fetch_kib_per_dispatch: {fetch[mk[0]]:.1f}",
+                  f"merge_write_kib_per_dispatch: {write[mk[0]]:.1f}"]
+    lines += [f"decode_fetch_bytes: {fb:.0f}",
+              f"decode_write_bytes: {wb:.0f}",
+              f"hbm_bytes_per_launch: {fb + wb:.0f}",
+              f"algorithmic_bytes_per_launch: {a.alg_bytes:.0f}",
+              f"fetch_over_algorithmic: {fb / a.alg_bytes:.4f}"]
+    with open(os.path.join(a.out, f"decode_kernel_cfg{cfg}_traffic.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+if __name__ == "__main__":
+    main()
