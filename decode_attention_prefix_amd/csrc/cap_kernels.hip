@@ -1,33 +1,34 @@
 // cap_kernels.hip -- gfx950 (CDNA4) kernels of libcap.
 //
-// decode_kernel: one wavefront per work item.  A work item is a run of KV
-// pages of one KV head together with every query row (requests x GQA heads,
-// up to 32) that reads those pages, so the pages are streamed from HBM once
-// for the whole row group -- the point of the Capillary Kernels project page
+// decode_kernel: one 4-wave workgroup per work item.  A work item is a run of
+// KV pages of one KV head together with the query rows (requests x GQA
+// heads) that read those pages, so the pages come from HBM once for the
+// whole row group -- the point of the Capillary Kernels project page
 // (abstract, first paragraph): shared prefixes should not be fetched once per
-// request.  Both contractions run on the matrix cores with
+// request.  Private items (<= 16 rows) stream pages straight into VGPRs,
+// their 4 waves splitting the pages; shared items (<= 128 rows) stream each
+// step into an LDS ring with global->LDS loads and every wave applies it to
+// its own 32 rows.  Both contractions run on the matrix cores with
 // v_mfma_f32_16x16x32_bf16:
 //
 //   S^T[16 tokens x 16 rows] = K_page[16 x D] . Q^T[D x 16]     (D/32 MFMAs per page)
 //   O^T[16 dims  x 16 rows] += V^T[16 dims x 32 tokens] . P^T   (D/16 MFMAs per 2 pages)
 //
-// The page layouts are chosen so that every MFMA operand is one contiguous
-// 16- or 8-byte global load per lane, straight into VGPRs, with no LDS round
-// trip and no transpose: K pages are [D/8][16][8] (a lane's 8 dims of one
-// token are 16 contiguous bytes, and the 16 tokens of one dim chunk form a
-// contiguous 256-byte line), V pages are [D][16] (a lane's 4 tokens of one
-// dim are 8 contiguous bytes).  The QK output layout (lane n + 16c holds
-// tokens 4c..4c+3 of row n) is exactly the B-operand layout the PV MFMA
-// wants for P, so the probabilities never leave the lane.
+// K pages are [D/8][16][8] (a lane's 8 dims of one token are 16 contiguous
+// bytes; the 16 tokens of one dim chunk are a contiguous 256-byte line), V
+// pages are [D][16] (tokens contiguous per dim).  The PV k-order maps lane
+// group c to tokens 8(c & 1)..+7 of page c >> 1, so a lane's V operand is
+// one 16-byte piece of a page row; the probabilities, which the QK MFMA
+// leaves as tokens 4c..4c+3 of both pages, are moved to that order with two
+// lane swaps per register pair.
 //
-// Softmax is online in base 2 (scale folded with log2 e, exp via v_exp_f32).
-// The running maximum of a row is shared by the four lanes that hold the
-// row (two xor shuffles per 2-page step); the running sum stays per lane and
-// is reduced once at the end.  Each item writes (m, l, o) for its rows into
-// write-once partial slots; merge_kernel combines the partials of each
-// (request, head) with log-sum-exp rescaling (the partial-result combination
-// of the project page's second paragraph, done through global memory/L2
-// because CDNA4 has no cross-CU shared memory).
+// Softmax is online in base 2 (scale folded with log2 e, exp via v_exp_f32)
+// with a lazily moved per-row reference maximum.  Each item writes (m, l, o)
+// for its rows into write-once partial slots; merge_kernel (or, in the fused
+// step, the item that completes a request) combines the partials of each
+// (request, head) with log-sum-exp rescaling -- the partial-result
+// combination of the project page's second paragraph, through global
+// memory/L2 because CDNA4 has no cross-CU shared memory.
 #include <hip/hip_runtime.h>
 
 #include "cap_internal.h"
