@@ -54,7 +54,7 @@ class PlanOpts(ctypes.Structure):
                 ("shared_rows", ctypes.c_int32), ("num_cus", ctypes.c_int32),
                 ("shared_cost", ctypes.c_float), ("rounds", ctypes.c_float),
                 ("share_margin", ctypes.c_float), ("order", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 3)]
+                ("private_rounds", ctypes.c_float), ("reserved", ctypes.c_int32 * 2)]
 
 
 class PlanStats(ctypes.Structure):

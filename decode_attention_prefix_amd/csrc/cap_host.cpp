@@ -219,7 +219,8 @@ struct Planner {
     int D, Hkv, G;
     int64_t head_tok_bytes;        // K+V bytes per token per KV head
     int64_t partial_row_bytes;     // partial bytes per query row (o, m, l)
-    double unit = 0;               // target cost of one work item (cost units)
+    double unit = 0;               // target cost of one shared work item (cost units)
+    double unit_private = 0;       // ... of one private work item
     int max_pages = 0;             // largest page run of any item
     std::vector<Group> groups;
 
@@ -229,7 +230,7 @@ struct Planner {
         Hkv = t.attn.num_kv_heads;
         G = t.G;
         head_tok_bytes = 4LL * D;
-        partial_row_bytes = 4LL * D + 8;
+        partial_row_bytes = 2LL * D + 8;
     }
 
     void node_entries(int n, std::vector<int32_t> &out) const
@@ -267,7 +268,8 @@ struct Planner {
         if (o.split_pages > 0) {
             k = std::max<int64_t>(k, (pages + o.split_pages - 1) / o.split_pages);
         } else if (unit > 0) {
-            k = std::max<int64_t>(k, (int64_t)std::ceil(pages * page_cost(shared) / unit));
+            const double u = shared ? unit : unit_private;
+            k = std::max<int64_t>(k, (int64_t)std::ceil(pages * page_cost(shared) / u));
         }
         return std::max<int64_t>(1, std::min<int64_t>(k, pages));
     }
@@ -328,6 +330,7 @@ struct Planner {
                 W += (double)g.entries.size() * rg * Hkv * page_cost(is_shared(nreq));
             }
             unit = std::max(4.0, W / ((double)o.num_cus * o.rounds));
+            unit_private = std::max(4.0, W / ((double)o.num_cus * o.private_rounds));
         }
     }
 };
@@ -338,9 +341,10 @@ void fill_defaults(cap_plan_opts &o)
     if (o.shared_rows == 0) o.shared_rows = cap::kPrivateRows;
     if (o.num_cus == 0) o.num_cus = 256;
     if (o.shared_cost == 0.f) o.shared_cost = 2.0f;
-    if (o.rounds == 0.f) o.rounds = 1.5f;
+    if (o.rounds == 0.f) o.rounds = 2.0f;
     if (o.share_margin == 0.f) o.share_margin = 1.0f;
     if (o.order == 0) o.order = 2;
+    if (o.private_rounds == 0.f) o.private_rounds = 1.5f;
 }
 
 }  // namespace
@@ -415,9 +419,9 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
     if (o.shared_rows < 0)
         return fail(CAP_ERR_INVALID_ARG, "shared_rows %d is negative", o.shared_rows);
     if (o.split_pages < 0 || o.num_cus < 0 || !(o.shared_cost > 0.f) || !(o.rounds > 0.f) ||
-        !(o.share_margin > 0.f))
+        !(o.share_margin > 0.f) || !(o.private_rounds > 0.f))
         return fail(CAP_ERR_INVALID_ARG, "negative planner option");
-    if (o.order < 1 || o.order > 3) return fail(CAP_ERR_INVALID_ARG, "order %d not in {0, 1, 2, 3}", o.order);
+    if (o.order < 1 || o.order > 4) return fail(CAP_ERR_INVALID_ARG, "order %d not in {0, .., 4}", o.order);
 
     cap_plan *p = new (std::nothrow) cap_plan();
     if (!p) return fail(CAP_ERR_INVALID_ARG, "out of host memory");
@@ -465,14 +469,22 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
     });
     std::vector<const Task *> seq;
     seq.reserve(tasks.size());
-    if (o.order == 1) {
+    if (o.order == 1 || o.order == 4) {
         std::vector<const Task *> sh, pr;
         for (const Task &tk : tasks) (tk.shared ? sh : pr).push_back(&tk);
         size_t i_sh = 0, i_pr = 0;
+        if (o.order == 4) {
+            // first wave: one shared and one private workgroup on every CU (the
+            // hardware gives each CU of an XCD one workgroup before any second)
+            const size_t per = std::max<size_t>(1, (size_t)o.num_cus / std::max(1, Hkv));
+            for (; i_sh < std::min(per, sh.size()); ++i_sh) seq.push_back(sh[i_sh]);
+            for (; i_pr < std::min(per, pr.size()); ++i_pr) seq.push_back(pr[i_pr]);
+        }
+        const size_t sh0 = i_sh, pr0 = i_pr;
         while (i_sh < sh.size() || i_pr < pr.size()) {
-            // take the kind that is further behind its share of the sequence
-            const bool take_sh = i_pr >= pr.size() ||
-                                 (i_sh < sh.size() && (double)i_sh * pr.size() <= (double)i_pr * sh.size());
+            // take the kind that is further behind its share of the rest
+            const double a = (double)(i_sh - sh0) * (pr.size() - pr0), b = (double)(i_pr - pr0) * (sh.size() - sh0);
+            const bool take_sh = i_pr >= pr.size() || (i_sh < sh.size() && a <= b);
             seq.push_back(take_sh ? sh[i_sh++] : pr[i_pr++]);
         }
     } else {
@@ -515,7 +527,7 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
     s.num_groups = (int64_t)pl.groups.size();
     s.partial_rows = slot_rows;
     const size_t slots = (size_t)slot_rows * Hq;
-    s.workspace_bytes = (int64_t)(align_up(slots * D * 4) + 2 * align_up(slots * 4));
+    s.workspace_bytes = (int64_t)(align_up(slots * D * 2) + 2 * align_up(slots * 4));
     s.plan_device_bytes = (int64_t)p->dev_bytes;
     s.tree_device_bytes = (int64_t)align_up(std::max<size_t>(tree->page_ids.size(), 1) * 4);
     const int64_t page_bytes = 2LL * cap::kPage * D * 2;   // K+V of one page, one head
@@ -524,7 +536,7 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
     s.kv_bytes_streamed = streamed;
     s.kv_bytes_unique = tree->unique_tokens * 4LL * D * Hkv;
     s.kv_bytes_unshared = tree->sum_ctx * 4LL * D * Hkv;
-    s.partial_bytes = (int64_t)slots * (4LL * D + 8);
+    s.partial_bytes = (int64_t)slots * (2LL * D + 8);
     s.max_partials_per_request = maxp;
     s.max_pages_per_item = pl.max_pages;
     s.plan_host_us = std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count();
@@ -567,17 +579,18 @@ cap_status cap_plan_upload(cap_plan *plan, void *dev_buf, size_t bytes, cap_stre
     return CAP_OK;
 }
 
-static cap_status split_workspace(const cap_plan *p, const void *ws, size_t ws_bytes, float **o,
+static cap_status split_workspace(const cap_plan *p, const void *ws, size_t ws_bytes, uint16_t **o,
                                   float **m, float **l)
 {
     if ((size_t)p->stats.workspace_bytes > ws_bytes || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)))
         return fail(CAP_ERR_WORKSPACE, "workspace: %zu bytes given, %lld needed (256-byte aligned)",
                     ws_bytes, (long long)p->stats.workspace_bytes);
     const size_t slots = (size_t)p->stats.partial_rows * p->tree->attn.num_q_heads;
+    const size_t o_bytes = align_up(slots * p->tree->attn.head_dim * 2);
     char *b = (char *)ws;
-    *o = (float *)b;
-    *m = (float *)(b + align_up(slots * p->tree->attn.head_dim * 4));
-    *l = (float *)(b + align_up(slots * p->tree->attn.head_dim * 4) + align_up(slots * 4));
+    *o = (uint16_t *)b;
+    *m = (float *)(b + o_bytes);
+    *l = (float *)(b + o_bytes + align_up(slots * 4));
     return CAP_OK;
 }
 
@@ -627,7 +640,7 @@ cap_status cap_decode_step(const cap_plan *plan, const void *q, const void *k_po
     cap_status st = decode_args(plan, q, k_pool, v_pool, workspace, ws_bytes, a);
     if (st != CAP_OK) return st;
     const int64_t slots = plan->stats.partial_rows * (int64_t)a.Hq;
-    if (slots * plan->tree->attn.head_dim * 4 >= (int64_t)1 << 31)
+    if (slots * plan->tree->attn.head_dim * 2 >= (int64_t)1 << 31)
         return fail(CAP_ERR_UNSUPPORTED, "fused step: %lld partial slots exceed the 2 GiB partial-o limit "
                     "(use cap_decode_attention + cap_merge_partials)", (long long)slots);
     a.slots = (int32_t)slots;
@@ -648,7 +661,8 @@ cap_status cap_merge_partials(const cap_plan *plan, const void *workspace, size_
     if (!plan->dev) return fail(CAP_ERR_STATE, "plan not uploaded (call cap_plan_upload first)");
     if ((uintptr_t)out & 15) return fail(CAP_ERR_INVALID_ARG, "out must be 16-byte aligned");
     cap::MergeArgs a{};
-    float *o, *m, *l;
+    uint16_t *o;
+    float *m, *l;
     cap_status st = split_workspace(plan, workspace, ws_bytes, &o, &m, &l);
     if (st != CAP_OK) return st;
     const char *d = static_cast<const char *>(plan->dev);

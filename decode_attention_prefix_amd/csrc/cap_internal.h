@@ -43,7 +43,7 @@ struct DecodeArgs {
     const uint16_t *q;           // [R][Hq][D] bf16
     const uint16_t *k_pool;      // [pages][Hkv][D/8][16][8] bf16
     const uint16_t *v_pool;      // [pages][Hkv][D][16] bf16
-    float *part_o;               // [slots][D]
+    uint16_t *part_o;            // [slots][D] fp16: o / l (the normalised partial output)
     float *part_m;               // [slots]
     float *part_l;               // [slots]
     int32_t n_items;
@@ -54,13 +54,13 @@ struct DecodeArgs {
     const int32_t *merge_off;    // [R+1] partial rows of each request
     const int32_t *merge_rows;
     uint16_t *out;               // [R][Hq][D] bf16
-    int32_t slots;               // partial slots (fused: slots * D * 4 < 2^31)
+    int32_t slots;               // partial slots (fused: slots * D * 2 < 2^31)
 };
 
 struct MergeArgs {
     const int32_t *merge_off;    // [R+1]
     const int32_t *merge_rows;   // partial rows per request
-    const float *part_o;
+    const uint16_t *part_o;      // fp16 o / l
     const float *part_m;
     const float *part_l;
     uint16_t *out;               // [R][Hq][D] bf16

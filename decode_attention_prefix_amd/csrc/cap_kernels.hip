@@ -295,6 +295,79 @@ __device__ __forceinline__ void softmax_pv(const f32x4 (&s0)[RB], const f32x4 (&
     }
 }
 
+// The shared path's step, split so that the QK MFMAs of the next step can
+// sit in one basic block with this step's softmax arithmetic (the matrix
+// cores then run while the vector ALUs work).  softmax_prepare holds the
+// branches: tail masking of the raw logits and of V, and the (rare) move of
+// a row's reference maximum, decided on the raw logits: a lane's largest
+// logit times the scale may exceed the reference by at most the threshold.
+template <int D>
+__device__ __forceinline__ void softmax_prepare(f32x4 (&s0)[2], f32x4 (&s1)[2], u32x4 (&v)[D / 16], int nt0,
+                                                int nt1, f32x4 (&o)[2][D / 16], float (&m_ref)[2],
+                                                float (&l_run)[2], float scale, int c)
+{
+    if (nt0 < kPage || nt1 < kPage) {                    // wave-uniform: only a node's last step
+        mask_v<D>(v, nt0, nt1, c);
+        const int lim0 = nt0 - 4 * c, lim1 = nt1 - 4 * c;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                s0[b][j] = j < lim0 ? s0[b][j] : -INFINITY;
+                s1[b][j] = j < lim1 ? s1[b][j] : -INFINITY;
+            }
+    }
+    float lm[2];
+    bool need = false;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        lm[b] = vmax3(vmax3(s0[b][0], s0[b][1], s0[b][2]), vmax3(s0[b][3], s1[b][0], s1[b][1]),
+                      vmax3(s1[b][2], s1[b][3], s1[b][3]));
+        need |= __builtin_fmaf(lm[b], scale, -m_ref[b]) > kRescaleThreshold;   // true while m_ref = -inf
+    }
+    if (__builtin_amdgcn_ballot_w64(need)) {             // wave-uniform, rare after the first step
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const float mx = row_max4(lm[b]) * scale;    // base-2 units (scale > 0)
+            const float m_new = mx > m_ref[b] + kRescaleThreshold ? mx : m_ref[b];
+            const float alpha = fast_exp2(m_ref[b] - m_new);   // 1 if unchanged, 0 from -inf
+            m_ref[b] = m_new;
+            l_run[b] *= alpha;
+#pragma unroll
+            for (int j = 0; j < D / 16; ++j) o[b][j] *= alpha;
+        }
+    }
+}
+
+// Straight-line rest of a shared step: probabilities 2^(s * scale - m_ref),
+// row sums, bf16 packing and exchange, PV MFMAs.
+template <int D>
+__device__ __forceinline__ void softmax_finish(const f32x4 (&s0)[2], const f32x4 (&s1)[2], const u32x4 (&v)[D / 16],
+                                               f32x4 (&o)[2][D / 16], const float (&m_ref)[2],
+                                               float (&l_run)[2], float scale)
+{
+    u32x4 pb[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const float mneg = -m_ref[b];
+        float p[8];
+        bf16x8 pk;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            p[j] = fast_exp2(__builtin_fmaf(s0[b][j], scale, mneg));
+            p[4 + j] = fast_exp2(__builtin_fmaf(s1[b][j], scale, mneg));
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pk[j] = (__bf16)p[j];
+        l_run[b] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        pb[b] = p_operand(__builtin_bit_cast(u32x4, pk));
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) o[b][j] = mfma(v[j], pb[b], o[b][j]);
+}
+
 template <int D, int RB, bool MASKV>
 __device__ __forceinline__ void compute_step(Step<D> &f, const u32x4 (&qf)[RB][D / 32],
                                              f32x4 (&o)[RB][D / 16], float (&m_ref)[RB],
@@ -342,14 +415,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, int by
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
 }
 
+// Four dims d..d+3 of a partial's normalised output o / l, as fp16 (the
+// value is a convex combination of V rows, so |o / l| <= max |v| and fp16
+// keeps ~3 significant digits: far inside the output tolerance, at half the
+// bytes of fp32).
 template <int D, bool FUSED>
 __device__ __forceinline__ void store_partial_o(const DecodeArgs &a, int64_t slot, int d, f32x4 v)
 {
+    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+    const f16x4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+    const u32x2 bits = __builtin_bit_cast(u32x2, h);
     if constexpr (FUSED)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), buf_rsrc(a.part_o, a.slots * D * 4),
-                                               (int)(slot * D + d) * 4, 0, kCoherent);
+        __builtin_amdgcn_raw_buffer_store_b64(bits, buf_rsrc(a.part_o, a.slots * D * 2),
+                                              (int)(slot * D + d) * 2, 0, kCoherent);
     else
-        *reinterpret_cast<f32x4 *>(a.part_o + slot * D + d) = v;
+        *reinterpret_cast<u32x2 *>(a.part_o + slot * D + d) = bits;
 }
 
 template <bool FUSED>
@@ -380,11 +460,12 @@ __device__ __forceinline__ void write_partials(const DecodeArgs &a, const WorkIt
         float l = l_run[b];
         l += __shfl_xor(l, 16);
         l += __shfl_xor(l, 32);
+        const float inv = l > 0.f ? 1.0f / l : 0.f;
         const int row = row0 + 16 * b + n;
         if (row < nrows) {
             const int64_t slot = (int64_t)(it.slot_base + row / G) * a.Hq + it.head * G + row % G;
 #pragma unroll
-            for (int j = 0; j < D / 16; ++j) store_partial_o<D, FUSED>(a, slot, 16 * j + 4 * c, o[b][j]);
+            for (int j = 0; j < D / 16; ++j) store_partial_o<D, FUSED>(a, slot, 16 * j + 4 * c, o[b][j] * inv);
             if (c == 0) store_partial_ml<FUSED>(a, slot, m_ref[b], l);
         }
     }
@@ -479,9 +560,11 @@ __device__ __forceinline__ void private_item(const DecodeArgs &a, const WorkItem
     if (row < nrows) {
         const int G = a.G;
         const int64_t slot = (int64_t)(it.slot_base + row / G) * a.Hq + it.head * G + row % G;
+        const float inv = L > 0.f ? 1.0f / L : 0.f;
 #pragma unroll
         for (int v = 0; v < V; v += 4)
-            store_partial_o<D, FUSED>(a, slot, d0 + v, f32x4{acc[v], acc[v + 1], acc[v + 2], acc[v + 3]});
+            store_partial_o<D, FUSED>(a, slot, d0 + v,
+                                      f32x4{acc[v], acc[v + 1], acc[v + 2], acc[v + 3]} * inv);
         if (tid % TPR == 0) store_partial_ml<FUSED>(a, slot, M, L);
     }
 }
@@ -653,16 +736,32 @@ __device__ __forceinline__ void shared_item(const DecodeArgs &a, const WorkItem 
         f32x4 sa0[2], sa1[2], sb0[2], sb1[2];
         lds_k<D>(k0, k1, lds, n, c);
         qk_step<D, 2>(k0, k1, qf, sa0, sa1, 2);
+        // Per step: wait for the ring, read K of step s + 1 and V of step s,
+        // settle masking and the reference maximum of step s (branches), then
+        // one straight block: the QK MFMAs of step s + 1 (on the last step
+        // they read a stale slot; the result is unused) and the softmax and
+        // PV of step s.
         auto half = [&](int s, f32x4 (&c0)[2], f32x4 (&c1)[2], f32x4 (&n0)[2], f32x4 (&n1)[2]) {
-            if (s + 1 < nsteps) {
-                ring_next<D>(a, h, np, nsteps, s, lane_pid, lds, wave, lane);
-                lds_k<D>(k0, k1, lds + ((s + 1) % kSlots) * T::kStep, n, c);
-                qk_step<D, 2>(k0, k1, qf, n0, n1, 2);
-            }
+            if (s + 1 < nsteps) ring_next<D>(a, h, np, nsteps, s, lane_pid, lds, wave, lane);
+            lds_k<D>(k0, k1, lds + ((s + 1) % kSlots) * T::kStep, n, c);
             const int nt0 = __builtin_amdgcn_readlane(lane_nt, 2 * s);
             const int nt1 = 2 * s + 1 < np ? __builtin_amdgcn_readlane(lane_nt, 2 * s + 1) : 0;
             lds_v<D>(v, lds + (s % kSlots) * T::kStep, n, c);
-            softmax_pv<D, 2, true>(c0, c1, v, nt0, nt1, o, m_ref, l_run, 2, sc, c);
+            softmax_prepare<D>(c0, c1, v, nt0, nt1, o, m_ref, l_run, sc, c);
+            qk_step<D, 2>(k0, k1, qf, n0, n1, 2);
+            softmax_finish<D>(c0, c1, v, o, m_ref, l_run, sc);
+            // scheduling hint for this block: each QK MFMA followed by two
+            // vector ops of the softmax, then each PV MFMA by one
+#pragma unroll
+            for (int i = 0; i < D / 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < D / 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);
+            }
         };
         for (int s = 0; s < nsteps; s += 2) {
             half(s, sa0, sa1, sb0, sb1);
@@ -686,13 +785,15 @@ __device__ __forceinline__ float wave_max(float v)
 struct MergeView {
     const int32_t *merge_off;    // [R+1]
     const int32_t *merge_rows;   // partial rows of each request
-    const float *part_o, *part_m, *part_l;
+    const uint16_t *part_o;      // fp16 o / l
+    const float *part_m, *part_l;
     uint16_t *out;               // [R][Hq][D] bf16
     int32_t Hq, slots;
 };
 
 // One wave merges the partials of (request r, query head qh) and writes the
-// bf16 output row:  out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i.
+// bf16 output row:  out = sum_i 2^(m_i - M) l_i (o_i / l_i) / sum_i 2^(m_i - M) l_i,
+// the partials holding the normalised o_i / l_i.
 // Lane = (pk, dc): dc picks 4 of the D output dims, pk one of PK = 256 / D
 // partial lanes.  Partials are taken 16 per block, 16 / PK per lane, all
 // their loads issued together; the block maximum comes from a reduction over
@@ -719,18 +820,22 @@ __device__ __forceinline__ void merge_row_wave(const MergeView &v, int r, int qh
         f32x4 x[NI];
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
+            u32x2 bits;
             if constexpr (COHERENT) {
                 l[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                     buf_rsrc(v.part_l, v.slots * 4), slot[i] * 4, 0, kCoherent));
                 m[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                     buf_rsrc(v.part_m, v.slots * 4), slot[i] * 4, 0, kCoherent));
-                x[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                    buf_rsrc(v.part_o, v.slots * D * 4), (slot[i] * D + 4 * dc) * 4, 0, kCoherent));
+                bits = __builtin_amdgcn_raw_buffer_load_b64(buf_rsrc(v.part_o, v.slots * D * 2),
+                                                            (slot[i] * D + 4 * dc) * 2, 0, kCoherent);
             } else {
                 l[i] = v.part_l[slot[i]];
                 m[i] = v.part_m[slot[i]];
-                x[i] = *reinterpret_cast<const f32x4 *>(v.part_o + (int64_t)slot[i] * D + 4 * dc);
+                bits = *reinterpret_cast<const u32x2 *>(v.part_o + (int64_t)slot[i] * D + 4 * dc);
             }
+            typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+            const f16x4 hx = __builtin_bit_cast(f16x4, bits);
+            x[i] = f32x4{(float)hx[0], (float)hx[1], (float)hx[2], (float)hx[3]};
         }
         float mb = -INFINITY;
 #pragma unroll
@@ -744,9 +849,9 @@ __device__ __forceinline__ void merge_row_wave(const MergeView &v, int r, int qh
         L *= rescale;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const float w = (ok[i] && l[i] > 0.f) ? fast_exp2(m[i] - M_new) : 0.f;
-            acc += w * x[i];
-            L += w * l[i];
+            const float wl = (ok[i] && l[i] > 0.f) ? fast_exp2(m[i] - M_new) * l[i] : 0.f;
+            acc += wl * x[i];
+            L += wl;
         }
         M = M_new;
     }

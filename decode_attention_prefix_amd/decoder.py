@@ -62,8 +62,9 @@ class TreeDecoder:
         return self.stats
 
     def poison_workspace(self):
-        """Fill the partial workspace with NaN (tests: unwritten slots show up)."""
-        self.ws.fill_(float("nan"))
+        """Fill the partial workspace with all-ones bytes, a NaN in fp32 and in
+        fp16 alike (tests: unwritten slots show up)."""
+        self.ws.view(self.torch.int32).fill_(-1)
 
     def decode(self):
         cap.cap_decode_attention(self.plan_h, self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(),

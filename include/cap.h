@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define CAP_ABI_VERSION 2
+#define CAP_ABI_VERSION 3
 
 typedef enum cap_status {
     CAP_OK = 0,
@@ -120,15 +120,20 @@ typedef struct cap_plan_opts {
     int32_t num_cus;          /* 0 = 256 (MI355X); used by the cost model */
     float shared_cost;        /* 0 = 2.0; cost of a shared item's page relative to a
                                  private item's page, used to size items */
-    float rounds;             /* 0 = 1.5; target work items per CU (two run at once) */
+    float rounds;             /* 0 = 2.0; target work items per CU (two run at once) */
     float share_margin;       /* 0 = 1.0; share a node only if saved bytes exceed
                                  margin x added partial bytes */
     int32_t order;            /* dispatch order of the work items (workgroups start in
                                  item order as CUs free up): 0 = default (2); 1 = the
                                  two item kinds interleaved evenly, each costliest
                                  first; 2 = costliest first over both kinds; 3 = all
-                                 shared items first, then private ones costliest first */
-    int32_t reserved[3];
+                                 shared items first, then private ones costliest first;
+                                 4 = one shared and one private workgroup per CU first
+                                 (num_cus of each kind), then as 1 */
+    float private_rounds;     /* 0 = 1.5; like `rounds`, but sizes the private items only
+                                 (splitting a private run adds one request's partial
+                                 rows, splitting a shared one adds a whole group's) */
+    int32_t reserved[2];
 } cap_plan_opts;
 
 /* Plan summary (host-side numbers; bytes are per decode step). */
@@ -224,10 +229,12 @@ cap_status cap_plan_get_view(const cap_plan *plan, cap_plan_view *view);
 cap_status cap_plan_upload(cap_plan *plan, void *dev_buf, size_t bytes, cap_stream_t stream);
 
 /* Launch the decode kernel: every work item streams its KV pages once for
- * all its query rows and writes (m, l, o) partials -- m the running maximum
- * of the base-2-scaled logits, l the sum of exponentials, o the unnormalised
- * weighted sum of V, fp32 -- into `workspace`
- * (>= stats.workspace_bytes, 256-byte aligned).  q, k_pool, v_pool: device
+ * all its query rows and writes (m, l, o/l) partials into `workspace`
+ * (>= stats.workspace_bytes, 256-byte aligned): m the reference maximum of
+ * the base-2-scaled logits (fp32), l the sum of 2^(logit - m) (fp32), o/l the
+ * normalised weighted sum of V (fp16, |o/l| <= max |v|).  Layout: o/l
+ * [slots][D] fp16, then m [slots], then l [slots], each region starting on a
+ * 256-byte boundary; slot = partial row x Hq + query head.  q, k_pool, v_pool: device
  * pointers in the layouts above, 16-byte aligned.  Errors:
  * CAP_ERR_INVALID_ARG, CAP_ERR_WORKSPACE, CAP_ERR_STATE (plan not uploaded),
  * CAP_ERR_HIP. */
