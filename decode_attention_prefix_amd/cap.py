@@ -54,7 +54,8 @@ class PlanOpts(ctypes.Structure):
                 ("shared_rows", ctypes.c_int32), ("num_cus", ctypes.c_int32),
                 ("shared_cost", ctypes.c_float), ("rounds", ctypes.c_float),
                 ("share_margin", ctypes.c_float), ("order", ctypes.c_int32),
-                ("private_rounds", ctypes.c_float), ("reserved", ctypes.c_int32 * 2)]
+                ("private_rounds", ctypes.c_float), ("tail_factor", ctypes.c_float),
+                ("tail_min_pages", ctypes.c_int32)]
 
 
 class PlanStats(ctypes.Structure):

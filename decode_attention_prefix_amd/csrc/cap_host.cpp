@@ -345,6 +345,8 @@ void fill_defaults(cap_plan_opts &o)
     if (o.share_margin == 0.f) o.share_margin = 1.0f;
     if (o.order == 0) o.order = 2;
     if (o.private_rounds == 0.f) o.private_rounds = 1.5f;
+    if (o.tail_factor == 0.f) o.tail_factor = 1.0f;
+    if (o.tail_min_pages == 0) o.tail_min_pages = 16;
 }
 
 }  // namespace
@@ -419,7 +421,7 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
     if (o.shared_rows < 0)
         return fail(CAP_ERR_INVALID_ARG, "shared_rows %d is negative", o.shared_rows);
     if (o.split_pages < 0 || o.num_cus < 0 || !(o.shared_cost > 0.f) || !(o.rounds > 0.f) ||
-        !(o.share_margin > 0.f) || !(o.private_rounds > 0.f))
+        !(o.share_margin > 0.f) || !(o.private_rounds > 0.f) || o.tail_factor < 0.f || o.tail_min_pages < 1)
         return fail(CAP_ERR_INVALID_ARG, "negative planner option");
     if (o.order < 1 || o.order > 4) return fail(CAP_ERR_INVALID_ARG, "order %d not in {0, .., 4}", o.order);
 
@@ -430,11 +432,10 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
     Planner pl(*tree, o);
     pl.build_groups();
 
-    // tasks: (page run, request subgroup); balanced splits of both
+    // tasks: (page run, request subgroup); balanced splits of both.  Partial
+    // slots are assigned once the dispatch sequence is fixed.
     struct Task { int32_t so, np, ro, nr, sb; bool shared; double cost; };
     std::vector<Task> tasks;
-    std::vector<std::vector<int32_t>> req_rows(tree->R);
-    int32_t slot_rows = 0;
     for (const Group &g : pl.groups) {
         const int64_t npg = (int64_t)g.entries.size();
         const int nreq = (int)g.reqs.size();
@@ -449,26 +450,23 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
             const int64_t pb = npg * ci / k, pe = npg * (ci + 1) / k;
             for (int ri = 0; ri < rg; ++ri) {
                 const int rb = (int)((int64_t)nreq * ri / rg), re = (int)((int64_t)nreq * (ri + 1) / rg);
-                Task tk{(int32_t)(so0 + pb), (int32_t)(pe - pb), ro0 + rb, re - rb, slot_rows, shared,
-                        (double)(pe - pb) * pl.page_cost(shared)};
-                for (int q = rb; q < re; ++q) req_rows[g.reqs[q]].push_back(slot_rows + (q - rb));
-                slot_rows += re - rb;
-                tasks.push_back(tk);
-                pl.max_pages = std::max<int>(pl.max_pages, (int)(pe - pb));
+                tasks.push_back(Task{(int32_t)(so0 + pb), (int32_t)(pe - pb), ro0 + rb, re - rb, -1, shared,
+                                     (double)(pe - pb) * pl.page_cost(shared)});
             }
         }
     }
     // The hardware starts workgroups in item order as CUs free up, so a list
     // sorted costliest first is greedy longest-processing-time scheduling.
     // order 1 interleaves the two kinds evenly (each costliest first), 2 sorts
-    // both kinds together, 3 puts every shared item first.  One item per task
-    // and KV head, the heads of a task back to back.
+    // both kinds together, 3 puts every shared item first, 4 starts with one
+    // shared and one private workgroup per CU.  One item per task and KV head,
+    // the heads of a task back to back.
     std::stable_sort(tasks.begin(), tasks.end(), [&](const Task &a, const Task &b) {
         if (o.order == 3 && a.shared != b.shared) return a.shared;
         return a.cost > b.cost;
     });
-    std::vector<const Task *> seq;
-    seq.reserve(tasks.size());
+    std::vector<Task> seq;
+    seq.reserve(tasks.size() * 2);
     if (o.order == 1 || o.order == 4) {
         std::vector<const Task *> sh, pr;
         for (const Task &tk : tasks) (tk.shared ? sh : pr).push_back(&tk);
@@ -477,24 +475,64 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
             // first wave: one shared and one private workgroup on every CU (the
             // hardware gives each CU of an XCD one workgroup before any second)
             const size_t per = std::max<size_t>(1, (size_t)o.num_cus / std::max(1, Hkv));
-            for (; i_sh < std::min(per, sh.size()); ++i_sh) seq.push_back(sh[i_sh]);
-            for (; i_pr < std::min(per, pr.size()); ++i_pr) seq.push_back(pr[i_pr]);
+            for (; i_sh < std::min(per, sh.size()); ++i_sh) seq.push_back(*sh[i_sh]);
+            for (; i_pr < std::min(per, pr.size()); ++i_pr) seq.push_back(*pr[i_pr]);
         }
         const size_t sh0 = i_sh, pr0 = i_pr;
         while (i_sh < sh.size() || i_pr < pr.size()) {
             // take the kind that is further behind its share of the rest
             const double a = (double)(i_sh - sh0) * (pr.size() - pr0), b = (double)(i_pr - pr0) * (sh.size() - sh0);
             const bool take_sh = i_pr >= pr.size() || (i_sh < sh.size() && a <= b);
-            seq.push_back(take_sh ? sh[i_sh++] : pr[i_pr++]);
+            seq.push_back(take_sh ? *sh[i_sh++] : *pr[i_pr++]);
+        }
+    } else if (o.tail_factor < 1e30f) {
+        // Costliest first with a shrinking cap on private items (guided
+        // self-scheduling): an item may cost at most the remaining work per
+        // workgroup slot / tail_factor, so the last items to start are short
+        // and the slots finish together.  Only private runs are cut (a cut
+        // adds one request group's partial rows; cutting a shared run would add
+        // a whole group's).
+        auto less = [](const Task &a, const Task &b) { return a.cost < b.cost; };
+        std::vector<Task> heap(tasks.begin(), tasks.end());
+        std::make_heap(heap.begin(), heap.end(), less);
+        double remaining = 0;
+        for (const Task &tk : tasks) remaining += tk.cost;
+        const double slots = 2.0 * o.num_cus / std::max(1, Hkv);   // task slots: Hkv items each
+        while (!heap.empty()) {
+            std::pop_heap(heap.begin(), heap.end(), less);
+            Task tk = heap.back();
+            heap.pop_back();
+            const double cap_cost = remaining / (slots * o.tail_factor);
+            const int32_t cap_pages = std::max<int32_t>(o.tail_min_pages, (int32_t)(cap_cost / pl.page_cost(false)));
+            if (!tk.shared && tk.np > cap_pages + o.tail_min_pages) {
+                Task rest = tk;
+                tk.np = cap_pages;
+                tk.cost = tk.np * pl.page_cost(false);
+                rest.so += cap_pages;
+                rest.np -= cap_pages;
+                rest.cost = rest.np * pl.page_cost(false);
+                heap.push_back(rest);
+                std::push_heap(heap.begin(), heap.end(), less);
+            }
+            remaining -= tk.cost;
+            seq.push_back(tk);
         }
     } else {
-        for (const Task &tk : tasks) seq.push_back(&tk);
+        seq.assign(tasks.begin(), tasks.end());
     }
-    p->items.reserve(tasks.size() * Hkv);
-    for (const Task *tk : seq)
+    std::vector<std::vector<int32_t>> req_rows(tree->R);
+    int32_t slot_rows = 0;
+    for (Task &tk : seq) {
+        tk.sb = slot_rows;
+        for (int q = 0; q < tk.nr; ++q) req_rows[p->rows[tk.ro + q]].push_back(slot_rows + q);
+        slot_rows += tk.nr;
+        pl.max_pages = std::max<int>(pl.max_pages, tk.np);
+    }
+    p->items.reserve(seq.size() * Hkv);
+    for (const Task &tk : seq)
         for (int h = 0; h < Hkv; ++h)
-            p->items.push_back(WorkItem{tk->so, tk->np, h, tk->ro, tk->nr, tk->sb,
-                                        tk->shared ? cap::kModeShared : cap::kModePrivate, 0});
+            p->items.push_back(WorkItem{tk.so, tk.np, h, tk.ro, tk.nr, tk.sb,
+                                        tk.shared ? cap::kModeShared : cap::kModePrivate, 0});
     p->merge_off.assign(tree->R + 1, 0);
     int32_t maxp = 0;
     for (int r = 0; r < tree->R; ++r) {
@@ -523,7 +561,7 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
     s.num_items = (int64_t)p->items.size();
     s.num_shared_items = 0;
     for (const WorkItem &w : p->items) s.num_shared_items += w.mode == cap::kModeShared;
-    s.num_tasks = (int64_t)tasks.size();
+    s.num_tasks = (int64_t)seq.size();
     s.num_groups = (int64_t)pl.groups.size();
     s.partial_rows = slot_rows;
     const size_t slots = (size_t)slot_rows * Hq;
@@ -532,7 +570,7 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
     s.tree_device_bytes = (int64_t)align_up(std::max<size_t>(tree->page_ids.size(), 1) * 4);
     const int64_t page_bytes = 2LL * cap::kPage * D * 2;   // K+V of one page, one head
     int64_t streamed = 0;
-    for (const Task &tk : tasks) streamed += (int64_t)tk.np * page_bytes * Hkv;
+    for (const Task &tk : seq) streamed += (int64_t)tk.np * page_bytes * Hkv;
     s.kv_bytes_streamed = streamed;
     s.kv_bytes_unique = tree->unique_tokens * 4LL * D * Hkv;
     s.kv_bytes_unshared = tree->sum_ctx * 4LL * D * Hkv;

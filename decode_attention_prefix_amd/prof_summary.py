@@ -60,15 +60,17 @@ def main(argv=None):
     ap.add_argument("--config", type=int, required=True)
     ap.add_argument("--workload", default="", help="one-line workload description")
     ap.add_argument("--kt", required=True)
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
+    ap.add_argument("--fetch", default=None, help="omit to write the kernel-trace summary only")
+    ap.add_argument("--write", default=None)
     ap.add_argument("--copy-mb", type=int, default=512)
-    ap.add_argument("--alg-bytes", type=float, required=True,
+    ap.add_argument("--alg-bytes", type=float, default=0.0,
                     help="algorithmic bytes per decode launch (unique K+V + Q [+ out])")
     ap.add_argument("--kernel", default="decode_kernel<128, false>")
     ap.add_argument("--bench-args", default="--no-cpu-baseline")
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     a = ap.parse_args(argv)
+    if a.fetch and a.write and a.alg_bytes <= 0:
+        ap.error("--alg-bytes is needed with --fetch/--write")
     h = kernel_hash()
     cfg = a.config
 
@@ -83,6 +85,9 @@ def main(argv=None):
     lines += ["", "(read_kernel and fill_kernel are the bench's cache-eviction read and buffer setup)"]
     with open(os.path.join(a.out, f"decode_kernel_cfg{cfg}_kernel_trace.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    if not (a.fetch and a.write):
+        return
 
     fetch = counter_means(a.fetch, "FETCH_SIZE")
     write = counter_means(a.write, "WRITE_SIZE")

@@ -133,7 +133,12 @@ typedef struct cap_plan_opts {
     float private_rounds;     /* 0 = 1.5; like `rounds`, but sizes the private items only
                                  (splitting a private run adds one request's partial
                                  rows, splitting a shared one adds a whole group's) */
-    int32_t reserved[2];
+    float tail_factor;        /* 0 = 1.0; with order 2, cut private items so that none
+                                 costs more than the work still to be dispatched per
+                                 workgroup slot / tail_factor (the last items to start
+                                 are short, so the slots finish together); a huge value
+                                 (>= 1e30) turns the cuts off */
+    int32_t tail_min_pages;   /* 0 = 16; smallest private piece such a cut leaves */
 } cap_plan_opts;
 
 /* Plan summary (host-side numbers; bytes are per decode step). */

@@ -174,9 +174,11 @@ def test_planner_coverage_random_trees(share_mode, split_pages):
         t = wl.tree_from_lengths(nt, par, paths, Hq, Hkv, 64, page_perm_rng=rng)
         h = cap.cap_tree_upload(t)
         try:
-            for shared_rows in (0, 1, 8, 1 << 30):
+            for shared_rows, extra in ((0, {}), (1, {"order": 1}), (8, {"order": 4}), (1 << 30, {}),
+                                       (0, {"tail_factor": 2.0, "tail_min_pages": 1}),
+                                       (8, {"tail_factor": 4.0, "tail_min_pages": 2, "order": 2})):
                 p = cap.cap_plan_step(h, share_mode=share_mode, split_pages=split_pages,
-                                      shared_rows=shared_rows)
+                                      shared_rows=shared_rows, **extra)
                 try:
                     check_coverage(t, p)
                 finally:
@@ -192,8 +194,9 @@ def test_planner_coverage_configs(cfg):
     t = wl.tree_from_lengths(nt, par, paths, Hq, Hkv, D, page_perm_rng=rng)
     h = cap.cap_tree_upload(t)
     try:
-        for mode in (-1, 0, 1):
-            p = cap.cap_plan_step(h, share_mode=mode)
+        for mode, extra in ((-1, {}), (0, {}), (1, {}), (-1, {"tail_factor": 2.0}), (-1, {"order": 4}),
+                            (-1, {"order": 3, "private_rounds": 6.0})):
+            p = cap.cap_plan_step(h, share_mode=mode, **extra)
             try:
                 st = check_coverage(t, p)
                 stats = wl.tree_stats(t)
