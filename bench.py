@@ -86,6 +86,8 @@ def main():
     ap.add_argument("--rounds", type=float, default=0.0)
     ap.add_argument("--order", type=int, default=0, help="work-item order (planner option)")
     ap.add_argument("--shared-cost", type=float, default=0.0)
+    ap.add_argument("--dispatch", type=int, default=0, choices=[0, 1],
+                    help="0 one workgroup per item (default), 1 work queues (planner option item_dispatch)")
     ap.add_argument("--fused", action="store_true",
                     help="time the one-launch cap_decode_step instead of cap_decode_attention + "
                          "cap_merge_partials")
@@ -129,6 +131,8 @@ def main():
         opts["order"] = args.order
     if args.shared_cost:
         opts["shared_cost"] = args.shared_cost
+    if args.dispatch:
+        opts["item_dispatch"] = args.dispatch
     dec = TreeDecoder(w.tree, w.q, w.k_pool, w.v_pool, device=dev, **opts)
     plan = dec.stats
     stream = torch.cuda.current_stream(dev)

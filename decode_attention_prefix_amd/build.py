@@ -20,6 +20,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O2", "-std=c++17", "-fPIC", "-shared", "-Wall",
          # packed fp32 VALU ops are kept out of every kernel
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # atomics stay per lane: the wave-aggregating rewrite would wait for the
+         # decode kernel's work-queue ticket right where it is issued
+         "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
          "-I", os.path.join(ROOT, "include")]
 
 

@@ -55,7 +55,7 @@ class PlanOpts(ctypes.Structure):
                 ("shared_cost", ctypes.c_float), ("rounds", ctypes.c_float),
                 ("share_margin", ctypes.c_float), ("order", ctypes.c_int32),
                 ("private_rounds", ctypes.c_float), ("tail_factor", ctypes.c_float),
-                ("tail_min_pages", ctypes.c_int32)]
+                ("tail_min_pages", ctypes.c_int32), ("item_dispatch", ctypes.c_int32)]
 
 
 class PlanStats(ctypes.Structure):

@@ -81,7 +81,9 @@ struct cap_plan {
     std::vector<int32_t> rows;        // request ids
     std::vector<int32_t> merge_off, merge_rows;
     // device image
-    size_t off_items = 0, off_stream = 0, off_rows = 0, off_moff = 0, off_mrows = 0, off_cnt = 0, dev_bytes = 0;
+    size_t off_items = 0, off_stream = 0, off_rows = 0, off_moff = 0, off_mrows = 0, off_cnt = 0, off_queue = 0,
+           dev_bytes = 0;
+    bool work_queue = false;          // item_dispatch 1
     std::vector<unsigned char> host_image;
     void *dev = nullptr;
 };
@@ -423,18 +425,21 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
     if (o.split_pages < 0 || o.num_cus < 0 || !(o.shared_cost > 0.f) || !(o.rounds > 0.f) ||
         !(o.share_margin > 0.f) || !(o.private_rounds > 0.f) || o.tail_factor < 0.f || o.tail_min_pages < 1)
         return fail(CAP_ERR_INVALID_ARG, "negative planner option");
+    if (o.item_dispatch < 0 || o.item_dispatch > 1)
+        return fail(CAP_ERR_INVALID_ARG, "item_dispatch %d not in {0, 1}", o.item_dispatch);
     if (o.order < 1 || o.order > 4) return fail(CAP_ERR_INVALID_ARG, "order %d not in {0, .., 4}", o.order);
 
     cap_plan *p = new (std::nothrow) cap_plan();
     if (!p) return fail(CAP_ERR_INVALID_ARG, "out of host memory");
     p->tree = tree;
+    p->work_queue = o.item_dispatch == 1;
     const int Hkv = tree->attn.num_kv_heads, Hq = tree->attn.num_q_heads, D = tree->attn.head_dim;
     Planner pl(*tree, o);
     pl.build_groups();
 
     // tasks: (page run, request subgroup); balanced splits of both.  Partial
     // slots are assigned once the dispatch sequence is fixed.
-    struct Task { int32_t so, np, ro, nr, sb; bool shared; double cost; };
+    struct Task { int32_t so, np, ro, nr, sb; bool shared; double cost; int32_t idx; };
     std::vector<Task> tasks;
     for (const Group &g : pl.groups) {
         const int64_t npg = (int64_t)g.entries.size();
@@ -451,7 +456,7 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
             for (int ri = 0; ri < rg; ++ri) {
                 const int rb = (int)((int64_t)nreq * ri / rg), re = (int)((int64_t)nreq * (ri + 1) / rg);
                 tasks.push_back(Task{(int32_t)(so0 + pb), (int32_t)(pe - pb), ro0 + rb, re - rb, -1, shared,
-                                     (double)(pe - pb) * pl.page_cost(shared)});
+                                     (double)(pe - pb) * pl.page_cost(shared), (int32_t)tasks.size()});
             }
         }
     }
@@ -491,8 +496,13 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
         // workgroup slot / tail_factor, so the last items to start are short
         // and the slots finish together.  Only private runs are cut (a cut
         // adds one request group's partial rows; cutting a shared run would add
-        // a whole group's).
-        auto less = [](const Task &a, const Task &b) { return a.cost < b.cost; };
+        // a whole group's).  Ties keep creation order, which puts the request
+        // subgroups of one page run next to each other: with the heads of a
+        // task back to back, their items for one KV head start Hkv apart, on
+        // the same XCD when Hkv = 8, and the later ones read the run from its L2.
+        auto less = [](const Task &a, const Task &b) {
+            return a.cost < b.cost || (a.cost == b.cost && a.idx > b.idx);
+        };
         std::vector<Task> heap(tasks.begin(), tasks.end());
         std::make_heap(heap.begin(), heap.end(), less);
         double remaining = 0;
@@ -541,15 +551,17 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
         maxp = std::max<int32_t>(maxp, (int32_t)req_rows[r].size());
     }
 
-    // device image: items | stream | rows | merge_off | merge_rows | counters
-    // (the fused step's arrival counters, one per request and KV head, zero)
+    // device image: items | stream | rows | merge_off | merge_rows | counters |
+    // queue (the fused step's arrival counters, one per request and KV head,
+    // and the work queue's two counters, all zero)
     p->off_items = 0;
     p->off_stream = align_up(p->items.size() * sizeof(WorkItem));
     p->off_rows = p->off_stream + align_up(p->stream.size() * 4);
     p->off_moff = p->off_rows + align_up(p->rows.size() * 4);
     p->off_mrows = p->off_moff + align_up(p->merge_off.size() * 4);
     p->off_cnt = p->off_mrows + align_up(p->merge_rows.size() * 4);
-    p->dev_bytes = std::max<size_t>(p->off_cnt + align_up((size_t)tree->R * Hkv * 4), kAlign);
+    p->off_queue = p->off_cnt + align_up((size_t)tree->R * Hkv * 4);
+    p->dev_bytes = p->off_queue + align_up(cap::kQueueInts * 4);
     p->host_image.assign(p->dev_bytes, 0);
     std::memcpy(p->host_image.data() + p->off_items, p->items.data(), p->items.size() * sizeof(WorkItem));
     std::memcpy(p->host_image.data() + p->off_stream, p->stream.data(), p->stream.size() * 4);
@@ -654,6 +666,7 @@ static cap_status decode_args(const cap_plan *plan, const void *q, const void *k
     a.Hkv = plan->tree->attn.num_kv_heads;
     a.G = plan->tree->G;
     a.scale_log2 = (float)((double)plan->tree->attn.sm_scale * 1.4426950408889634);
+    if (plan->work_queue) a.queue = reinterpret_cast<int32_t *>(static_cast<char *>(plan->dev) + plan->off_queue);
     return CAP_OK;
 }
 

@@ -36,6 +36,10 @@ struct WorkItem {
 };
 static_assert(sizeof(WorkItem) == sizeof(cap_work_item), "work item layout");
 
+constexpr int kQueues = 8;            // one per XCD (workgroup b runs on XCD b mod 8)
+constexpr int kQueueStride = 64;      // ints: one 256-byte line per counter
+constexpr int kQueueInts = (kQueues + 1) * kQueueStride;
+
 struct DecodeArgs {
     const WorkItem *items;         // one workgroup each
     const int32_t *stream;       // page-stream entries: (physical page << 5) | (ntok - 1)
@@ -49,6 +53,10 @@ struct DecodeArgs {
     int32_t n_items;
     int32_t Hq, Hkv, G;
     float scale_log2;            // sm_scale * log2(e)
+    // work queues (nullptr: one workgroup per item): kQueues counters of items
+    // handed out, then the count of finished workgroups, each kQueueStride
+    // ints apart; zero between launches
+    int32_t *queue;
     // fused step only (counters == nullptr: partials are left for merge_kernel)
     int32_t *counters;           // [R][Hkv] arrival counts, zero between steps
     const int32_t *merge_off;    // [R+1] partial rows of each request

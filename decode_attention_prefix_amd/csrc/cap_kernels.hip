@@ -31,6 +31,8 @@
 // memory/L2 because CDNA4 has no cross-CU shared memory.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "cap_internal.h"
 
 namespace cap {
@@ -491,11 +493,22 @@ __device__ __forceinline__ void load_page_table(const DecodeArgs &a, const WorkI
 // pages straight from HBM into registers (one step in flight while the
 // previous computes) and keeps its own (m, l, o).  At the end the waves put
 // their statistics in LDS and the workgroup writes one merged partial.
+// Work queues: Q = min(kQueues, gridDim.x) of them; workgroup b draws from
+// queue b mod Q, which holds items gridDim.x + Q t + (b mod Q), t = 0, 1, ...
+__device__ __forceinline__ int num_queues() { return min(kQueues, (int)gridDim.x); }
+
+// Next item of this workgroup from its ticket; without a queue, none.
+__device__ __forceinline__ int next_item_of(const DecodeArgs &a, int ticket)
+{
+    const int nq = num_queues();
+    return a.queue ? (int)gridDim.x + nq * ticket + (int)blockIdx.x % nq : a.n_items;
+}
+
 template <int D, bool FUSED>
 __device__ __forceinline__ void private_item(const DecodeArgs &a, const WorkItem &it, float *mrg, int tid,
-                                             int lane, int n, int c)
+                                             int lane, int n, int c, int *publish, int ticket)
 {
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nrows = it.nreq * a.G;
     const int nsteps_all = (it.npages + 1) >> 1;
     const int s_begin = nsteps_all * wave / kWaves, s_end = nsteps_all * (wave + 1) / kWaves;
@@ -536,6 +549,7 @@ __device__ __forceinline__ void private_item(const DecodeArgs &a, const WorkItem
         mb[wave * 16 + n] = m_ref[0];
         lb[wave * 16 + n] = l;
     }
+    if (tid == 0) *publish = next_item_of(a, ticket);   // the ticket has long returned
     __syncthreads();
 
     // merge: thread t takes row t / TPR and D/TPR consecutive dims
@@ -703,7 +717,7 @@ __device__ __forceinline__ void ring_next(const DecodeArgs &a, int h, int np, in
 
 template <int D, bool FUSED>
 __device__ __forceinline__ void shared_item(const DecodeArgs &a, const WorkItem &it, uint16_t *lds, int tid,
-                                            int lane, int n, int c)
+                                            int lane, int n, int c, int *publish, int ticket)
 {
     using T = SharedTile<D>;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -770,6 +784,7 @@ __device__ __forceinline__ void shared_item(const DecodeArgs &a, const WorkItem 
     } else {
         for (int s = 0; s + 1 < nsteps; ++s) ring_next<D>(a, h, np, nsteps, s, lane_pid, lds, wave, lane);
     }
+    if (tid == 0) *publish = next_item_of(a, ticket);   // the ticket has long returned
     write_partials<D, 2, FUSED>(a, it, row0, nrows, nblk, o, m_ref, l_run, n, c);
 }
 
@@ -903,9 +918,20 @@ __device__ __forceinline__ void finish_item(const DecodeArgs &a, const WorkItem 
         merge_row_wave<D, true>(v, lst[1 + t / G], it.head * G + t % G, tid & (kWaveSize - 1));
 }
 
-// One workgroup per work item: shared items stage KV in LDS for their
-// row-waves; private items split their pages over the waves.  FUSED: the
-// item that completes a request also merges it (no merge_kernel launch).
+// Shared items stage KV in LDS for their row-waves; private items split
+// their pages over the waves.  FUSED: the item that completes a request also
+// merges it (no merge_kernel launch).
+//
+// Items in item order: workgroup b starts with item b; with work queues
+// (a.queue) the grid is two workgroups per CU and each then takes its next
+// item from queue b mod 8 (next_item_of), with a ticket from that queue's
+// counter, taken when it starts an item (the ticket's latency hides behind
+// the item's own loads).  Eight queues, one per XCD, keep the hardware's
+// XCD placement of items and spread the counter traffic.  Each workgroup's
+// last ticket is past the end; the workgroup that finishes last returns
+// every counter to zero for the next launch.  Without a queue (one
+// workgroup per item) the hardware starts workgroups in order, each bound to
+// one shader engine, so a free slot can wait for a busy engine.
 template <int D, bool FUSED>
 __global__ __launch_bounds__(kSharedThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_kernel(DecodeArgs a)
@@ -913,18 +939,52 @@ void decode_kernel(DecodeArgs a)
     constexpr int kTileBytes = kSlots * SharedTile<D>::kStep * 2;  // shared path: the LDS ring
     constexpr int kMergeBytes = (kWaves * 16 * D + 2 * kWaves * 16) * 4;   // private path: merge buffer
     constexpr int kLdsBytes = kTileBytes > kMergeBytes ? kTileBytes : kMergeBytes;
-    __shared__ __attribute__((aligned(16))) float lds[kLdsBytes / 4];
-    __shared__ int lst[FUSED ? 1 + kSharedRows : 1];
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWaveSize - 1);
-    const int n = lane & 15, c = lane >> 4;
-    const WorkItem &it = a.items[blockIdx.x];
-    if (FUSED && tid == 0) lst[0] = 0;         // read after the item's barriers
-    if (it.mode == kModeShared)
-        shared_item<D, FUSED>(a, it, reinterpret_cast<uint16_t *>(lds), tid, lane, n, c);
-    else
-        private_item<D, FUSED>(a, it, lds, tid, lane, n, c);
-    if constexpr (FUSED) finish_item<D>(a, it, lst, tid);
+    constexpr int kLstInts = FUSED ? 1 + kSharedRows : 0;
+    // One LDS object for everything: with several, the compiler's tracking of
+    // global->LDS loads makes every ring read wait for all of them.  Layout:
+    // ring / merge buffer, then the fused step's completion list, then the
+    // next item by iteration parity.
+    __shared__ __attribute__((aligned(16))) float lds[kLdsBytes / 4 + kLstInts + 2];
+    int *const lst = reinterpret_cast<int *>(lds + kLdsBytes / 4);
+    int *const next_item = lst + kLstInts;
+    int cur = blockIdx.x;
+    for (int par = 0; cur < a.n_items; par ^= 1) {
+        // the lane index is re-derived each item (opaque to the compiler), so
+        // nothing lane-dependent is hoisted out of the loop to hold registers
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & (kWaveSize - 1);
+        const int n = lane & 15, c = lane >> 4;
+        // thread 0's ticket; read only where the next item is published, which
+        // is where the compiler waits for it (no value on the other paths, so
+        // no copy at the branch join forces an early wait)
+        int ticket;
+        if (a.queue && tid == 0)
+            ticket = __hip_atomic_fetch_add(a.queue + (blockIdx.x % num_queues()) * kQueueStride, 1,
+                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const WorkItem &it = a.items[cur];
+        if (FUSED && tid == 0) lst[0] = 0;     // read after the item's barriers
+        if (it.mode == kModeShared)
+            shared_item<D, FUSED>(a, it, reinterpret_cast<uint16_t *>(lds), tid, lane, n, c, &next_item[par], ticket);
+        else
+            private_item<D, FUSED>(a, it, lds, tid, lane, n, c, &next_item[par], ticket);
+        if constexpr (FUSED) finish_item<D>(a, it, lst, tid);
+        // every wave is done with this item's LDS (and next_item is written);
+        // partial stores may still be in flight
+        __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0)
+        asm volatile("s_barrier" ::: "memory");
+        cur = __builtin_amdgcn_readfirstlane(next_item[par]);
+    }
+    if (a.queue && threadIdx.x == 0) {
+        // every ticket of this workgroup has returned (the last one ended the loop)
+        int *const done_ctr = a.queue + kQueues * kQueueStride;
+        const int done = __hip_atomic_fetch_add(done_ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (done == (int)gridDim.x - 1) {
+            for (int x = 0; x < kQueues; ++x)
+                __hip_atomic_store(a.queue + x * kQueueStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(done_ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 }
 
 // Two-launch step: one wave per (request, query head).
@@ -978,21 +1038,49 @@ __global__ __launch_bounds__(256) void copy_kernel(u32x4 *dst, const u32x4 *src,
 
 }  // namespace
 
+// CU count of the current device, cached per device.
+static int device_cus(int *cus)
+{
+    static int cache[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    if (dev >= 0 && dev < 64 && cache[dev] > 0) {
+        *cus = cache[dev];
+        return 0;
+    }
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return (int)e;
+    *cus = n > 0 ? n : 1;
+    if (dev >= 0 && dev < 64) cache[dev] = *cus;
+    return 0;
+}
+
 int launch_decode(const DecodeArgs &a, int head_dim, void *stream)
 {
     if (a.n_items <= 0) return 0;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const bool fused = a.counters != nullptr;
+    int grid = a.n_items;
+    if (a.queue) {
+        // two resident workgroups per CU (LDS and the two-waves-per-SIMD bound)
+        int cus = 0;
+        const int e = device_cus(&cus);
+        if (e != 0) return e;
+        grid = std::min(a.n_items, 2 * cus);
+    }
+    const dim3 g((unsigned)grid), b(kSharedThreads);
     if (head_dim == 128) {
         if (fused)
-            hipLaunchKernelGGL((decode_kernel<128, true>), dim3(a.n_items), dim3(kSharedThreads), 0, s, a);
+            hipLaunchKernelGGL((decode_kernel<128, true>), g, b, 0, s, a);
         else
-            hipLaunchKernelGGL((decode_kernel<128, false>), dim3(a.n_items), dim3(kSharedThreads), 0, s, a);
+            hipLaunchKernelGGL((decode_kernel<128, false>), g, b, 0, s, a);
     } else {
         if (fused)
-            hipLaunchKernelGGL((decode_kernel<64, true>), dim3(a.n_items), dim3(kSharedThreads), 0, s, a);
+            hipLaunchKernelGGL((decode_kernel<64, true>), g, b, 0, s, a);
         else
-            hipLaunchKernelGGL((decode_kernel<64, false>), dim3(a.n_items), dim3(kSharedThreads), 0, s, a);
+            hipLaunchKernelGGL((decode_kernel<64, false>), g, b, 0, s, a);
     }
     return (int)hipGetLastError();
 }

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define CAP_ABI_VERSION 3
+#define CAP_ABI_VERSION 4
 
 typedef enum cap_status {
     CAP_OK = 0,
@@ -139,6 +139,15 @@ typedef struct cap_plan_opts {
                                  are short, so the slots finish together); a huge value
                                  (>= 1e30) turns the cuts off */
     int32_t tail_min_pages;   /* 0 = 16; smallest private piece such a cut leaves */
+    int32_t item_dispatch;    /* 0 = one workgroup per item, started by the hardware
+                                 in item order (each bound to one shader engine, so a
+                                 free slot can wait for a busy engine); 1 = work
+                                 queues: two resident workgroups per CU take items as
+                                 they finish, workgroup b from queue b mod 8 (items
+                                 congruent to it mod 8, in item order), through
+                                 counters in the plan buffer.  Both read the same
+                                 bytes; with the memory system saturated neither is
+                                 faster on the measured trees, 0 by a little */
 } cap_plan_opts;
 
 /* Plan summary (host-side numbers; bytes are per decode step). */
@@ -226,10 +235,11 @@ cap_status cap_plan_get_view(const cap_plan *plan, cap_plan_view *view);
 /* Copy the plan into dev_buf (>= stats.plan_device_bytes, 256-byte aligned)
  * with one asynchronous host-to-device copy.  The plan keeps the host copy
  * alive; free the plan only after the stream has passed this copy.  The
- * buffer ends with the fused step's arrival counters (R x Hkv int32, zero
- * after the upload and again after every completed cap_decode_step), so it
- * must stay writable device memory, and one plan buffer serves one fused
- * step at a time.
+ * buffer ends with counters that the decode kernel updates (the fused
+ * step's arrival counters, R x Hkv int32, and the work queues' counters;
+ * all zero after the upload and again after every completed launch), so it
+ * must stay writable device memory, and launches that use one plan buffer
+ * must not overlap (on one stream they never do).
  * Errors: CAP_ERR_INVALID_ARG, CAP_ERR_WORKSPACE, CAP_ERR_HIP. */
 cap_status cap_plan_upload(cap_plan *plan, void *dev_buf, size_t bytes, cap_stream_t stream);
 
@@ -265,7 +275,7 @@ cap_status cap_merge_partials(const cap_plan *plan, const void *workspace, size_
  * unspecified.  Steps that share a plan buffer must not overlap (counters).
  * Errors: as cap_decode_attention, CAP_ERR_INVALID_ARG for a NULL or
  * misaligned `out`, CAP_ERR_UNSUPPORTED when the partial o region
- * (stats.partial_rows x Hq x D x 4 bytes) reaches 2 GiB (32-bit buffer
+ * (stats.partial_rows x Hq x D x 2 bytes) reaches 2 GiB (32-bit buffer
  * offsets; the two-call form has no such limit). */
 cap_status cap_decode_step(const cap_plan *plan, const void *q, const void *k_pool,
                            const void *v_pool, void *workspace, size_t ws_bytes, void *out,

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), f"libcap.so does not export {n}"
     assert set(cap.EXPORTED) == names
-    assert cap.cap_abi_version() == 3
+    assert cap.cap_abi_version() == 4
 
 
 def small_tree(**over):
@@ -82,7 +82,7 @@ def test_planner_rejects_bad_options():
     h = cap.cap_tree_upload(small_tree())
     try:
         for kw in ({"share_mode": 5}, {"shared_rows": -3}, {"split_pages": -1}, {"rounds": -1.0},
-                   {"share_margin": -1.0}):
+                   {"share_margin": -1.0}, {"item_dispatch": 2}, {"order": 5}):
             with pytest.raises(cap.CapError) as e:
                 cap.cap_plan_step(h, **kw)
             assert e.value.status == 1

@@ -80,13 +80,14 @@ def config_case(cfg):
     return _ORACLE_CACHE[cfg]
 
 
-def test_config0_all_plan_variants():
+@pytest.mark.parametrize("dispatch", [0, 1])
+def test_config0_all_plan_variants(dispatch):
     w, ref = config_case(0)
     for mode in (-1, 0, 1):
         for split in (0, 1, 3, 100):
             for shared_rows in (0, 1, 1 << 30):
-                run_both(w, ref, f"cfg0 mode={mode} split={split} shared_rows={shared_rows}",
-                         share_mode=mode, split_pages=split, shared_rows=shared_rows)
+                run_both(w, ref, f"cfg0 mode={mode} split={split} shared_rows={shared_rows} dispatch={dispatch}",
+                         share_mode=mode, split_pages=split, shared_rows=shared_rows, item_dispatch=dispatch)
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4])
@@ -96,8 +97,10 @@ def test_full_configs(cfg):
     out, _, st = run_gpu(w, repeats=2)
     e = check(out, ref, f"cfg{cfg} auto fused")
     print(f"config {cfg}: max abs err {e:.3e}; plan {st}", flush=True)
-    out2, _, _ = run_gpu(w, fused=False)
+    out2, _, _ = run_gpu(w, fused=False, repeats=2)
     check(out2, ref, f"cfg{cfg} auto two-launch")
+    out3, _, _ = run_gpu(w, fused=False, item_dispatch=1, repeats=2)
+    check(out3, ref, f"cfg{cfg} two-launch, work queues")
     if cfg == 4:
         ctl = wl.control_workload(w)
         run_both(ctl, ref, "cfg4 control batch")
@@ -130,7 +133,8 @@ def test_random_small_trees(D, HqHkv):
         ref = oracle.decode(w.tree, w.q, w.k_pool, w.v_pool)
         for opts in ({}, {"share_mode": 1, "split_pages": 1, "shared_rows": 1},
                      {"share_mode": 0, "shared_rows": 1 << 30},
-                     {"split_pages": 3, "shared_rows": 1}, {"split_pages": 2}):
+                     {"split_pages": 3, "shared_rows": 1}, {"split_pages": 2},
+                     {"split_pages": 1, "item_dispatch": 1}):
             run_both(w, ref, f"seed={seed} D={D} Hq={Hq} Hkv={Hkv} {opts}", **opts)
 
 
@@ -153,10 +157,12 @@ def test_bitwise_deterministic(fused):
     assert np.array_equal(b1, b2)
 
 
-def test_fused_counters_reset_across_plans_and_steps():
-    """Many fused steps on one plan, then a re-plan on the same buffers: the
-    arrival counters must be back at zero after every step."""
-    _torch()
+def test_counters_reset_across_plans_and_steps():
+    """Many steps on one plan, then a re-plan on the same buffers: the fused
+    step's arrival counters and the work queue's counters must be back at
+    zero after every launch, i.e. the plan buffer is byte-identical to what
+    the upload wrote."""
+    torch = _torch()
     from decode_attention_prefix_amd.decoder import TreeDecoder
     rng = np.random.default_rng(5)
     nt, par, paths = wl.make_random_tree(rng, num_requests=40, max_depth=3, max_len=200,
@@ -166,11 +172,17 @@ def test_fused_counters_reset_across_plans_and_steps():
     ref = oracle.decode(w.tree, w.q, w.k_pool, w.v_pool)
     dec = TreeDecoder(w.tree, w.q, w.k_pool, w.v_pool, split_pages=2)
     try:
-        for opts in ({"split_pages": 2}, {"split_pages": 1, "share_mode": 1}, {}):
+        for opts in ({"split_pages": 2}, {"split_pages": 1, "share_mode": 1}, {}, {"item_dispatch": 1}):
             dec.plan(**opts)
-            for _ in range(5):
+            torch.cuda.synchronize()
+            n = int(dec.stats["plan_device_bytes"])
+            image = dec.plan_buf[:n].cpu().numpy().copy()
+            for i in range(6):
+                fused = i % 3 != 2
                 dec.out.fill_(-1)
-                dec.step(fused=True)
-                check(dec.output(), ref, f"repeated fused steps {opts}")
+                dec.step(fused=fused)
+                check(dec.output(), ref, f"repeated steps {opts} fused={fused}")
+                after = dec.plan_buf[:n].cpu().numpy()
+                assert np.array_equal(after, image), f"plan buffer changed by a step {opts} fused={fused}"
     finally:
         dec.close()
