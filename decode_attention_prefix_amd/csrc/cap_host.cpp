@@ -554,8 +554,39 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
     // device image: items | stream | rows | merge_off | merge_rows | counters |
     // queue (the fused step's arrival counters, one per request and KV head,
     // and the work queue's two counters, all zero)
+    // device items: each item plus its requests' first id when they are
+    // consecutive and the stream entries of its first pages, split over the
+    // waves as the decode kernel splits a private item's steps
+    std::vector<cap::DevItem> dev_items(p->items.size());
+    for (size_t i = 0; i < p->items.size(); ++i) {
+        const WorkItem &w = p->items[i];
+        cap::DevItem &d = dev_items[i];
+        d = cap::DevItem{};
+        d.stream_off = w.stream_off;
+        d.npages = w.npages;
+        d.head = w.head;
+        d.row_off = w.row_off;
+        d.nreq = w.nreq;
+        d.slot_base = w.slot_base;
+        d.mode = w.mode;
+        bool consecutive = true;
+        for (int q = 1; q < w.nreq; ++q) consecutive &= p->rows[w.row_off + q] == p->rows[w.row_off] + q;
+        d.req0 = consecutive ? p->rows[w.row_off] : -1;
+        const int32_t *e = p->stream.data() + w.stream_off;
+        if (w.mode == cap::kModeShared) {
+            for (int j = 0; j < cap::kInlineEntries && j < w.npages; ++j) d.ent[j] = e[j];
+        } else {
+            const int nsteps = (w.npages + 1) >> 1;
+            for (int wv = 0; wv < cap::kWaves; ++wv) {
+                const int first = 2 * (nsteps * wv / cap::kWaves);
+                const int count = std::min(w.npages, 2 * (nsteps * (wv + 1) / cap::kWaves)) - first;
+                for (int j = 0; j < cap::kInlinePerWave && j < count; ++j)
+                    d.ent[cap::kInlinePerWave * wv + j] = e[first + j];
+            }
+        }
+    }
     p->off_items = 0;
-    p->off_stream = align_up(p->items.size() * sizeof(WorkItem));
+    p->off_stream = align_up(dev_items.size() * sizeof(cap::DevItem));
     p->off_rows = p->off_stream + align_up(p->stream.size() * 4);
     p->off_moff = p->off_rows + align_up(p->rows.size() * 4);
     p->off_mrows = p->off_moff + align_up(p->merge_off.size() * 4);
@@ -563,7 +594,7 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
     p->off_queue = p->off_cnt + align_up((size_t)tree->R * Hkv * 4);
     p->dev_bytes = p->off_queue + align_up(cap::kQueueInts * 4);
     p->host_image.assign(p->dev_bytes, 0);
-    std::memcpy(p->host_image.data() + p->off_items, p->items.data(), p->items.size() * sizeof(WorkItem));
+    std::memcpy(p->host_image.data() + p->off_items, dev_items.data(), dev_items.size() * sizeof(cap::DevItem));
     std::memcpy(p->host_image.data() + p->off_stream, p->stream.data(), p->stream.size() * 4);
     std::memcpy(p->host_image.data() + p->off_rows, p->rows.data(), p->rows.size() * 4);
     std::memcpy(p->host_image.data() + p->off_moff, p->merge_off.data(), p->merge_off.size() * 4);
@@ -655,7 +686,7 @@ static cap_status decode_args(const cap_plan *plan, const void *q, const void *k
     cap_status st = split_workspace(plan, workspace, ws_bytes, &a.part_o, &a.part_m, &a.part_l);
     if (st != CAP_OK) return st;
     const char *d = static_cast<const char *>(plan->dev);
-    a.items = reinterpret_cast<const WorkItem *>(d + plan->off_items);
+    a.items = reinterpret_cast<const cap::DevItem *>(d + plan->off_items);
     a.stream = reinterpret_cast<const int32_t *>(d + plan->off_stream);
     a.rows = reinterpret_cast<const int32_t *>(d + plan->off_rows);
     a.q = static_cast<const uint16_t *>(q);

@@ -36,12 +36,33 @@ struct WorkItem {
 };
 static_assert(sizeof(WorkItem) == sizeof(cap_work_item), "work item layout");
 
+// Device form of a work item: the fields above plus what lets a workgroup
+// issue its first K/V and Q loads right after reading the item, without
+// first reading the page stream and the row table (each a dependent trip to
+// memory).
+constexpr int kInlineEntries = 16;
+constexpr int kInlinePerWave = kInlineEntries / kWaves;   // private items: per wave
+struct DevItem {
+    int32_t stream_off;
+    int32_t npages;
+    int32_t head;
+    int32_t row_off;
+    int32_t nreq;
+    int32_t slot_base;
+    int32_t mode;
+    int32_t req0;               // first request id when the item's requests are consecutive ids, else -1
+    // page-stream entries of the first pages: private items, pages
+    // 0 .. kInlinePerWave - 1 of wave w's sub-stream at [kInlinePerWave * w ..];
+    // shared items, pages 0 .. kInlineEntries - 1 (0 past the end)
+    int32_t ent[kInlineEntries];
+};
+
 constexpr int kQueues = 8;            // one per XCD (workgroup b runs on XCD b mod 8)
 constexpr int kQueueStride = 64;      // ints: one 256-byte line per counter
 constexpr int kQueueInts = (kQueues + 1) * kQueueStride;
 
 struct DecodeArgs {
-    const WorkItem *items;         // one workgroup each
+    const DevItem *items;          // one workgroup each
     const int32_t *stream;       // page-stream entries: (physical page << 5) | (ntok - 1)
     const int32_t *rows;         // request ids of each item's request list
     const uint16_t *q;           // [R][Hq][D] bf16

@@ -49,11 +49,6 @@ __device__ __forceinline__ u32x4 ld16(const uint16_t *p)
     return *reinterpret_cast<const u32x4 *>(p);
 }
 
-__device__ __forceinline__ u32x2 ld8(const uint16_t *p)
-{
-    return *reinterpret_cast<const u32x2 *>(p);
-}
-
 __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -71,6 +66,35 @@ __device__ __forceinline__ float fast_exp2(float x)
 // bf16, and (m_ref, l, o) is still a valid partial for any reference.
 constexpr float kRescaleThreshold = 8.0f;
 
+// One work item, read once when the workgroup starts it: the fields as
+// uniform values, the inline page entries one per lane (lane i < 16: entry i).
+// Later reads of the item in memory would be vector loads with a wait on every
+// outstanding load (the compiler treats the ring's global->LDS loads as
+// possible writes to it), so nothing reads the item twice.
+struct ItemRegs {
+    int stream_off, npages, head, row_off, nreq, slot_base, mode, req0;
+    int lane_ent;
+};
+
+__device__ __forceinline__ ItemRegs read_item(const DevItem *items, int idx, int lane)
+{
+    const DevItem &d = items[idx];
+    ItemRegs r;
+    r.stream_off = d.stream_off;
+    r.npages = d.npages;
+    r.head = d.head;
+    r.row_off = d.row_off;
+    r.nreq = d.nreq;
+    r.slot_base = d.slot_base;
+    r.mode = d.mode;
+    r.req0 = d.req0;
+    r.lane_ent = lane < kInlineEntries ? d.ent[lane] : 0;
+    // a use on every path: the wait for the record lands here, before any
+    // other load of the item is issued, and no later read of an entry waits
+    asm volatile("" ::"v"(r.lane_ent));
+    return r;
+}
+
 // KV fragments of one 2-page step, already in MFMA operand layout.
 template <int D>
 struct Step {
@@ -79,26 +103,37 @@ struct Step {
     int nt0, nt1;                   // valid tokens in page 0 / page 1 (nt1 = 0: no page)
 };
 
-// Issue the loads of one 2-page step.  The page table of the item is held in
-// lanes (lane i: physical page and valid tokens of page i), so a step's page
-// ids come from v_readlane without a scalar-memory round trip.  Every call
-// issues the same number of loads whatever the step (a missing second page
-// re-reads the first; steps past the end re-read the last), so the wait
-// counts of the software pipeline stay exact.
+// Issue the loads of step s (two pages) of a private wave's sub-stream of
+// `count` pages.  Page ids: the sub-stream's first kInlinePerWave pages come
+// from the item itself (no wait on the page stream for the first two steps),
+// later ones from the wave's page table held in lanes (lane i: raw stream
+// entry of page i) via v_readlane.  Every call issues the same number of
+// loads whatever the step (a missing second page re-reads the first; steps
+// past the end re-read the last), so the wait counts of the software
+// pipeline stay exact.
 template <int D>
-__device__ __forceinline__ void load_step(Step<D> &f, const DecodeArgs &a, int head, int npages,
-                                          int s, int lane_pid, int lane_nt, int n, int c)
+__device__ __forceinline__ void load_step(Step<D> &f, const DecodeArgs &a, const ItemRegs &it, int wave, int count,
+                                          int s, int lane_e, int n, int c)
 {
     const int64_t blk = (int64_t)kPage * D;             // elements per (page, head)
-    const int nsteps = (npages + 1) >> 1;
+    const int head = it.head;
+    const int nsteps = (count + 1) >> 1;
     const int ss = s < nsteps ? s : nsteps - 1;
     const int i0 = 2 * ss;
-    const bool has1 = i0 + 1 < npages;
+    const bool has1 = i0 + 1 < count;
     const int i1 = has1 ? i0 + 1 : i0;
-    const int64_t p0 = __builtin_amdgcn_readlane(lane_pid, i0);
-    const int64_t p1 = __builtin_amdgcn_readlane(lane_pid, i1);
-    f.nt0 = __builtin_amdgcn_readlane(lane_nt, i0);
-    f.nt1 = has1 ? __builtin_amdgcn_readlane(lane_nt, i1) : 0;
+    int e0, e1;
+    if (i1 < kInlinePerWave) {
+        e0 = __builtin_amdgcn_readlane(it.lane_ent, kInlinePerWave * wave + i0);
+        e1 = __builtin_amdgcn_readlane(it.lane_ent, kInlinePerWave * wave + i1);
+    } else {
+        e0 = __builtin_amdgcn_readlane(lane_e, i0);
+        e1 = __builtin_amdgcn_readlane(lane_e, i1);
+    }
+    const int64_t p0 = e0 >> 5;
+    const int64_t p1 = e1 >> 5;
+    f.nt0 = (e0 & 31) + 1;
+    f.nt1 = has1 ? (e1 & 31) + 1 : 0;
     const uint16_t *kb0 = a.k_pool + (p0 * a.Hkv + head) * blk;
     const uint16_t *vb0 = a.v_pool + (p0 * a.Hkv + head) * blk;
     const uint16_t *kb1 = a.k_pool + (p1 * a.Hkv + head) * blk;
@@ -383,7 +418,7 @@ __device__ __forceinline__ void compute_step(Step<D> &f, const u32x4 (&qf)[RB][D
 // Q fragments (B operand of QK) for rows row0 + 16b + n of an item: lane
 // (n, c) holds dims 8(4i+c)..+7.  Rows past nrows are zero.
 template <int D, int RB>
-__device__ __forceinline__ void load_q(u32x4 (&qf)[RB][D / 32], const DecodeArgs &a, const WorkItem &it,
+__device__ __forceinline__ void load_q(u32x4 (&qf)[RB][D / 32], const DecodeArgs &a, const ItemRegs &it,
                                        int row0, int nrows, int n, int c)
 {
     const int G = a.G;
@@ -391,7 +426,7 @@ __device__ __forceinline__ void load_q(u32x4 (&qf)[RB][D / 32], const DecodeArgs
     for (int b = 0; b < RB; ++b) {
         const int row = row0 + 16 * b + n;
         if (row < nrows) {
-            const int req = a.rows[it.row_off + row / G];
+            const int req = it.req0 >= 0 ? it.req0 + row / G : a.rows[it.row_off + row / G];
             const int h = it.head * G + row % G;
             const uint16_t *qb = a.q + ((int64_t)req * a.Hq + h) * D;
 #pragma unroll
@@ -450,7 +485,7 @@ __device__ __forceinline__ void store_partial_ml(const DecodeArgs &a, int64_t sl
 
 // Partials of rows row0 + 16b + n: slot = (slot_base + row / G) * Hq + head * G + row % G.
 template <int D, int RB, bool FUSED>
-__device__ __forceinline__ void write_partials(const DecodeArgs &a, const WorkItem &it, int row0, int nrows,
+__device__ __forceinline__ void write_partials(const DecodeArgs &a, const ItemRegs &it, int row0, int nrows,
                                                int nblk, const f32x4 (&o)[RB][D / 16],
                                                const float (&m_ref)[RB], const float (&l_run)[RB], int n,
                                                int c)
@@ -473,18 +508,12 @@ __device__ __forceinline__ void write_partials(const DecodeArgs &a, const WorkIt
     }
 }
 
-// Page table of pages [first, first + count) of an item, one page per lane
-// (count <= 64).
-__device__ __forceinline__ void load_page_table(const DecodeArgs &a, const WorkItem &it, int first, int count,
-                                                int lane, int &lane_pid, int &lane_nt)
+// Page table of pages [first, first + count) of an item, one raw stream
+// entry per lane (count <= 64; 0 past the end).
+__device__ __forceinline__ int load_page_table(const DecodeArgs &a, const ItemRegs &it, int first, int count,
+                                               int lane)
 {
-    lane_pid = 0;
-    lane_nt = 0;
-    if (lane < count) {
-        const int e = a.stream[it.stream_off + first + lane];
-        lane_pid = e >> 5;
-        lane_nt = (e & 31) + 1;
-    }
+    return lane < count ? a.stream[it.stream_off + first + lane] : 0;
 }
 
 // ---------------------------------------------------------------- private path
@@ -505,7 +534,7 @@ __device__ __forceinline__ int next_item_of(const DecodeArgs &a, int ticket)
 }
 
 template <int D, bool FUSED>
-__device__ __forceinline__ void private_item(const DecodeArgs &a, const WorkItem &it, float *mrg, int tid,
+__device__ __forceinline__ void private_item(const DecodeArgs &a, const ItemRegs &it, float *mrg, int tid,
                                              int lane, int n, int c, int *publish, int ticket)
 {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -522,18 +551,29 @@ __device__ __forceinline__ void private_item(const DecodeArgs &a, const WorkItem
     for (int j = 0; j < D / 16; ++j) o[0][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_ref[1] = {-INFINITY}, l_run[1] = {0.f};
     if (count > 0) {
-        int lane_pid, lane_nt;
-        load_page_table(a, it, first, count, lane, lane_pid, lane_nt);
+        const int lane_e = load_page_table(a, it, first, count, lane);
         const int nsteps = (count + 1) >> 1;
         const float sc = a.scale_log2;
+        // Two steps in flight: steps 0 and 1 (pages from the item) are issued
+        // at once, then each step's compute is followed by the loads of the
+        // step two ahead.  The page table (steps 2 on) is waited for right
+        // after the first loads, on every path, so no wait inside the loop
+        // has to cover it; the scheduling barriers keep a step's first MFMA,
+        // and its wait, below the loads issued before it.
         Step<D> fa, fb;
-        load_step<D>(fa, a, it.head, count, 0, lane_pid, lane_nt, n, c);
-        for (int s = 0; s < nsteps; s += 2) {
-            load_step<D>(fb, a, it.head, count, s + 1, lane_pid, lane_nt, n, c);
+        load_step<D>(fa, a, it, wave, count, 0, lane_e, n, c);
+        load_step<D>(fb, a, it, wave, count, 1, lane_e, n, c);
+        asm volatile("" ::"v"(lane_e));
+        __builtin_amdgcn_sched_barrier(0);
+        for (int s = 0;; s += 2) {
             compute_step<D, 1, true>(fa, qf, o, m_ref, l_run, 1, sc, c);
             if (s + 1 >= nsteps) break;
-            load_step<D>(fa, a, it.head, count, s + 2, lane_pid, lane_nt, n, c);
+            load_step<D>(fa, a, it, wave, count, s + 2, lane_e, n, c);
+            __builtin_amdgcn_sched_barrier(0);
             compute_step<D, 1, true>(fb, qf, o, m_ref, l_run, 1, sc, c);
+            if (s + 2 >= nsteps) break;
+            load_step<D>(fb, a, it, wave, count, s + 3, lane_e, n, c);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
@@ -610,14 +650,23 @@ struct SharedTile {
 // Global->LDS loads of step `step` into `slot`: piece k of each wave covers
 // block k * kWaves / kPPB ... (kPPB pieces per block, 4 blocks, kWaves waves).
 template <int D>
-__device__ __forceinline__ void issue_dma(const DecodeArgs &a, int head, int npages, int step, int lane_pid,
+__device__ __forceinline__ void issue_dma(const DecodeArgs &a, const ItemRegs &it, int step, int lane_e,
                                           uint16_t *slot, int wave, int lane)
 {
     using T = SharedTile<D>;
+    const int head = it.head;
     const int i0 = 2 * step;
-    const int i1 = i0 + 1 < npages ? i0 + 1 : i0;
-    const int64_t p0 = __builtin_amdgcn_readlane(lane_pid, i0);
-    const int64_t p1 = __builtin_amdgcn_readlane(lane_pid, i1);
+    const int i1 = i0 + 1 < it.npages ? i0 + 1 : i0;
+    int e0, e1;
+    if (i1 < kInlineEntries) {             // the first pages come with the item
+        e0 = __builtin_amdgcn_readlane(it.lane_ent, i0);
+        e1 = __builtin_amdgcn_readlane(it.lane_ent, i1);
+    } else {
+        e0 = __builtin_amdgcn_readlane(lane_e, i0);
+        e1 = __builtin_amdgcn_readlane(lane_e, i1);
+    }
+    const int64_t p0 = e0 >> 5;
+    const int64_t p1 = e1 >> 5;
 #pragma unroll
     for (int k = 0; k < T::kPPB; ++k) {
         const int piece = wave + kWaves * k;                 // 0 .. 4 * kPPB - 1
@@ -694,17 +743,17 @@ __device__ __forceinline__ void lds_v(u32x4 (&v)[D / 16], const uint16_t *slot, 
 // of step s - 1, which every wave finished reading before this barrier, with
 // step s + kSlots - 1.
 template <int D>
-__device__ __forceinline__ void ring_start(const DecodeArgs &a, int h, int np, int nsteps, int lane_pid,
+__device__ __forceinline__ void ring_start(const DecodeArgs &a, const ItemRegs &it, int nsteps, int lane_e,
                                            uint16_t *lds, int wave, int lane)
 {
 #pragma unroll
     for (int q = 0; q < kSlots; ++q)
-        if (q < nsteps) issue_dma<D>(a, h, np, q, lane_pid, lds + q * SharedTile<D>::kStep, wave, lane);
+        if (q < nsteps) issue_dma<D>(a, it, q, lane_e, lds + q * SharedTile<D>::kStep, wave, lane);
     ring_barrier<SharedTile<D>::kPPB>(min(kSlots, nsteps) - 1);
 }
 
 template <int D>
-__device__ __forceinline__ void ring_next(const DecodeArgs &a, int h, int np, int nsteps, int s, int lane_pid,
+__device__ __forceinline__ void ring_next(const DecodeArgs &a, const ItemRegs &it, int nsteps, int s, int lane_e,
                                           uint16_t *lds, int wave, int lane)
 {
     // issued so far: steps 0 .. min(nsteps, max(kSlots, s + kSlots - 1)) - 1; wait for step s + 1
@@ -712,11 +761,11 @@ __device__ __forceinline__ void ring_next(const DecodeArgs &a, int h, int np, in
     ring_barrier<SharedTile<D>::kPPB>(issued - (s + 2));
     const int nxt = s + kSlots - 1;
     if (s >= 1 && nxt < nsteps)
-        issue_dma<D>(a, h, np, nxt, lane_pid, lds + (nxt % kSlots) * SharedTile<D>::kStep, wave, lane);
+        issue_dma<D>(a, it, nxt, lane_e, lds + (nxt % kSlots) * SharedTile<D>::kStep, wave, lane);
 }
 
 template <int D, bool FUSED>
-__device__ __forceinline__ void shared_item(const DecodeArgs &a, const WorkItem &it, uint16_t *lds, int tid,
+__device__ __forceinline__ void shared_item(const DecodeArgs &a, const ItemRegs &it, uint16_t *lds, int tid,
                                             int lane, int n, int c, int *publish, int ticket)
 {
     using T = SharedTile<D>;
@@ -724,13 +773,12 @@ __device__ __forceinline__ void shared_item(const DecodeArgs &a, const WorkItem 
     const int nrows = it.nreq * a.G;
     const int row0 = 32 * wave;
     const int nblk = nrows > row0 ? min(2, (nrows - row0 + 15) >> 4) : 0;
-    int lane_pid, lane_nt;
-    load_page_table(a, it, 0, it.npages, lane, lane_pid, lane_nt);
+    const int lane_e = load_page_table(a, it, 0, it.npages, lane);
     u32x4 qf[2][D / 32];
     load_q<D, 2>(qf, a, it, row0, nrows, n, c);         // before the ring loads: loads land in order
     const int nsteps = (it.npages + 1) >> 1;
-    const int h = it.head, np = it.npages;
-    ring_start<D>(a, h, np, nsteps, lane_pid, lds, wave, lane);
+    const int np = it.npages;
+    ring_start<D>(a, it, nsteps, lane_e, lds, wave, lane);
 
     f32x4 o[2][D / 16];
 #pragma unroll
@@ -756,10 +804,10 @@ __device__ __forceinline__ void shared_item(const DecodeArgs &a, const WorkItem 
         // they read a stale slot; the result is unused) and the softmax and
         // PV of step s.
         auto half = [&](int s, f32x4 (&c0)[2], f32x4 (&c1)[2], f32x4 (&n0)[2], f32x4 (&n1)[2]) {
-            if (s + 1 < nsteps) ring_next<D>(a, h, np, nsteps, s, lane_pid, lds, wave, lane);
+            if (s + 1 < nsteps) ring_next<D>(a, it, nsteps, s, lane_e, lds, wave, lane);
             lds_k<D>(k0, k1, lds + ((s + 1) % kSlots) * T::kStep, n, c);
-            const int nt0 = __builtin_amdgcn_readlane(lane_nt, 2 * s);
-            const int nt1 = 2 * s + 1 < np ? __builtin_amdgcn_readlane(lane_nt, 2 * s + 1) : 0;
+            const int nt0 = (__builtin_amdgcn_readlane(lane_e, 2 * s) & 31) + 1;
+            const int nt1 = 2 * s + 1 < np ? (__builtin_amdgcn_readlane(lane_e, 2 * s + 1) & 31) + 1 : 0;
             lds_v<D>(v, lds + (s % kSlots) * T::kStep, n, c);
             softmax_prepare<D>(c0, c1, v, nt0, nt1, o, m_ref, l_run, sc, c);
             qk_step<D, 2>(k0, k1, qf, n0, n1, 2);
@@ -782,20 +830,13 @@ __device__ __forceinline__ void shared_item(const DecodeArgs &a, const WorkItem 
             if (s + 1 < nsteps) half(s + 1, sb0, sb1, sa0, sa1);
         }
     } else {
-        for (int s = 0; s + 1 < nsteps; ++s) ring_next<D>(a, h, np, nsteps, s, lane_pid, lds, wave, lane);
+        for (int s = 0; s + 1 < nsteps; ++s) ring_next<D>(a, it, nsteps, s, lane_e, lds, wave, lane);
     }
     if (tid == 0) *publish = next_item_of(a, ticket);   // the ticket has long returned
     write_partials<D, 2, FUSED>(a, it, row0, nrows, nblk, o, m_ref, l_run, n, c);
 }
 
 // ------------------------------------------------------------------ merge
-__device__ __forceinline__ float wave_max(float v)
-{
-#pragma unroll
-    for (int k = 32; k >= 1; k >>= 1) v = fmaxf(v, __shfl_xor(v, k));
-    return v;
-}
-
 // Where a merge reads its partials and writes its output.
 struct MergeView {
     const int32_t *merge_off;    // [R+1]
@@ -806,83 +847,116 @@ struct MergeView {
     int32_t Hq, slots;
 };
 
-// One wave merges the partials of (request r, query head qh) and writes the
-// bf16 output row:  out = sum_i 2^(m_i - M) l_i (o_i / l_i) / sum_i 2^(m_i - M) l_i,
-// the partials holding the normalised o_i / l_i.
-// Lane = (pk, dc): dc picks 4 of the D output dims, pk one of PK = 256 / D
-// partial lanes.  Partials are taken 16 per block, 16 / PK per lane, all
-// their loads issued together; the block maximum comes from a reduction over
-// the pk lanes, the running result is rescaled when it rises, and the pk
-// lanes' sums are added at the end.  COHERENT: sc1 loads (fused step).
+// Loads of one block of up to 16 partials of one merge row: lane i of the
+// wave holds partial row `prow` of partial i of the current list window.
+template <int D>
+struct MergeBlock {
+    static constexpr int NB = 16;
+    float m[NB], l[NB];
+    u32x4 x[NB];
+};
+
 template <int D, bool COHERENT>
-__device__ __forceinline__ void merge_row_wave(const MergeView &v, int r, int qh, int lane)
+__device__ __forceinline__ void merge_load(MergeBlock<D> &b, const MergeView &v, int prow, int k0, int nb,
+                                           int qh, int dc)
 {
-    constexpr int CH = D / 4, PK = kWaveSize / CH, NI = 16 / PK;
-    const int pk = lane / CH, dc = lane % CH;
-    const int beg = v.merge_off[r], end = v.merge_off[r + 1];
-    float M = -INFINITY, L = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int kb = beg; kb < end; kb += 16) {
-        int slot[NI];
-        bool ok[NI];
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const int k = kb + pk + PK * i;
-            ok[i] = k < end;
-            slot[i] = v.merge_rows[ok[i] ? k : end - 1] * v.Hq + qh;
-        }
-        float m[NI], l[NI];
-        f32x4 x[NI];
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            u32x2 bits;
+    for (int i = 0; i < MergeBlock<D>::NB; ++i) {
+        if (i < nb) {
+            const int slot = __builtin_amdgcn_readlane(prow, k0 + i) * v.Hq + qh;
             if constexpr (COHERENT) {
-                l[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                    buf_rsrc(v.part_l, v.slots * 4), slot[i] * 4, 0, kCoherent));
-                m[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                    buf_rsrc(v.part_m, v.slots * 4), slot[i] * 4, 0, kCoherent));
-                bits = __builtin_amdgcn_raw_buffer_load_b64(buf_rsrc(v.part_o, v.slots * D * 2),
-                                                            (slot[i] * D + 4 * dc) * 2, 0, kCoherent);
+                b.m[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                    buf_rsrc(v.part_m, v.slots * 4), slot * 4, 0, kCoherent));
+                b.l[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                    buf_rsrc(v.part_l, v.slots * 4), slot * 4, 0, kCoherent));
+                b.x[i] = __builtin_amdgcn_raw_buffer_load_b128(buf_rsrc(v.part_o, v.slots * D * 2),
+                                                               (slot * D + 8 * dc) * 2, 0, kCoherent);
             } else {
-                l[i] = v.part_l[slot[i]];
-                m[i] = v.part_m[slot[i]];
-                bits = *reinterpret_cast<const u32x2 *>(v.part_o + (int64_t)slot[i] * D + 4 * dc);
+                b.m[i] = v.part_m[slot];
+                b.l[i] = v.part_l[slot];
+                b.x[i] = *reinterpret_cast<const u32x4 *>(v.part_o + (int64_t)slot * D + 8 * dc);
             }
-            typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-            const f16x4 hx = __builtin_bit_cast(f16x4, bits);
-            x[i] = f32x4{(float)hx[0], (float)hx[1], (float)hx[2], (float)hx[3]};
+        } else {
+            b.m[i] = -INFINITY;
+            b.l[i] = 0.f;
+            b.x[i] = u32x4{0u, 0u, 0u, 0u};
         }
-        float mb = -INFINITY;
+    }
+}
+
+// Fold a block into the running (M, L, acc): the reference M rises to the
+// block maximum (rescaling what is summed so far), then each partial adds
+// weight 2^(m_i - M) l_i.
+template <int D>
+__device__ __forceinline__ void merge_fold(const MergeBlock<D> &b, float &M, float &L, float (&acc)[8])
+{
+    typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+    constexpr int NB = MergeBlock<D>::NB;
+    float mb = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < NI; ++i)
-            if (ok[i] && l[i] > 0.f) mb = fmaxf(mb, m[i]);
+    for (int i = 0; i < NB; ++i)
+        if (b.l[i] > 0.f) mb = fmaxf(mb, b.m[i]);
+    const float M_new = fmaxf(M, mb);
+    const float rescale = M_new == -INFINITY ? 0.f : fast_exp2(M - M_new);   // 0 on the first block
+    L *= rescale;
 #pragma unroll
-        for (int sft = CH; sft < kWaveSize; sft <<= 1) mb = fmaxf(mb, __shfl_xor(mb, sft));
-        const float M_new = fmaxf(M, mb);
-        const float rescale = M_new == -INFINITY ? 0.f : fast_exp2(M - M_new);   // 0 on the first block
-        acc *= rescale;
-        L *= rescale;
+    for (int e = 0; e < 8; ++e) acc[e] *= rescale;
 #pragma unroll
-        for (int i = 0; i < NI; ++i) {
-            const float wl = (ok[i] && l[i] > 0.f) ? fast_exp2(m[i] - M_new) * l[i] : 0.f;
-            acc += wl * x[i];
-            L += wl;
+    for (int i = 0; i < NB; ++i) {
+        const float w = b.l[i] > 0.f ? fast_exp2(b.m[i] - M_new) * b.l[i] : 0.f;
+        const f16x8 h = __builtin_bit_cast(f16x8, b.x[i]);
+        L += w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += w * (float)h[e];
+    }
+    M = M_new;
+}
+
+// One wave merges the partials of query heads qh0 .. qh0 + nh - 1 (nh <=
+// RPW = 512 / D) of request r and writes their bf16 output rows:
+//   out = sum_i 2^(m_i - M) l_i (o_i / l_i) / sum_i 2^(m_i - M) l_i,
+// the partials holding the normalised o_i / l_i.  Every query head of a
+// request has the same partial rows (merge list), so the list is read once
+// per wave, 64 entries at a time, one per lane.  Lane = (row rho, dim chunk
+// dc): D / 8 lanes per row, 8 dims (one 16-byte fp16 load per partial) per
+// lane; each lane also loads m and l of its row (the row's lanes share those
+// addresses), so no lane exchanges anything.  Partials go 16 per block, the
+// next block's loads in flight while a block is folded in.  COHERENT: sc1
+// loads (fused step).
+template <int D, bool COHERENT>
+__device__ __forceinline__ void merge_rows(const MergeView &v, int r, int qh0, int nh, int lane)
+{
+    constexpr int LPR = D / 8;                 // lanes per row
+    constexpr int NB = MergeBlock<D>::NB;
+    const int rho = lane / LPR, dc = lane % LPR;
+    const bool active = rho < nh;
+    const int qh = qh0 + (active ? rho : 0);
+    const int beg = v.merge_off[r], np = v.merge_off[r + 1] - beg;
+    float M = -INFINITY, L = 0.f;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int w0 = 0; w0 < np; w0 += kWaveSize) {
+        const int nw = min(kWaveSize, np - w0);
+        const int prow = lane < nw ? v.merge_rows[beg + w0 + lane] : 0;
+        MergeBlock<D> ba, bb;
+        merge_load<D, COHERENT>(ba, v, prow, 0, min(NB, nw), qh, dc);
+        for (int k = 0; k < nw; k += 2 * NB) {
+            if (k + NB < nw) merge_load<D, COHERENT>(bb, v, prow, k + NB, min(NB, nw - k - NB), qh, dc);
+            merge_fold<D>(ba, M, L, acc);
+            if (k + NB >= nw) break;
+            if (k + 2 * NB < nw) merge_load<D, COHERENT>(ba, v, prow, k + 2 * NB, min(NB, nw - k - 2 * NB), qh, dc);
+            merge_fold<D>(bb, M, L, acc);
         }
-        M = M_new;
     }
-#pragma unroll
-    for (int sft = CH; sft < kWaveSize; sft <<= 1) {
-        L += __shfl_xor(L, sft);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], sft);
-    }
-    if (pk == 0) {
+    if (active) {
         const float inv = 1.0f / L;
-        const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)(acc[0] * inv)) |
-                            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc[1] * inv)) << 16);
-        const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)(acc[2] * inv)) |
-                            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc[3] * inv)) << 16);
-        *reinterpret_cast<u32x2 *>(v.out + ((int64_t)r * v.Hq + qh) * D + 4 * dc) = u32x2{lo, hi};
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            o[e] = __builtin_bit_cast(uint16_t, (__bf16)(acc[2 * e] * inv)) |
+                   ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc[2 * e + 1] * inv)) << 16);
+        *reinterpret_cast<u32x4 *>(v.out + ((int64_t)r * v.Hq + qh) * D + 8 * dc) = o;
     }
 }
 
@@ -893,7 +967,7 @@ __device__ __forceinline__ void merge_row_wave(const MergeView &v, int r, int qh
 // resets the counter for the next step.  lst: LDS, [0] = count, then the
 // completed request ids.
 template <int D>
-__device__ __forceinline__ void finish_item(const DecodeArgs &a, const WorkItem &it, int *lst, int tid)
+__device__ __forceinline__ void finish_item(const DecodeArgs &a, const ItemRegs &it, int *lst, int tid)
 {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0): this wave's partial stores are done
@@ -912,10 +986,14 @@ __device__ __forceinline__ void finish_item(const DecodeArgs &a, const WorkItem 
     const int nlast = lst[0];
     if (nlast == 0) return;
     const MergeView v{a.merge_off, a.merge_rows, a.part_o, a.part_m, a.part_l, a.out, a.Hq, a.slots};
-    const int G = a.G;
+    // row sets of up to RPW query heads of this KV head, one wave each
+    constexpr int RPW = kWaveSize / (D / 8);
+    const int G = a.G, sets = (G + RPW - 1) / RPW;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    for (int t = wave; t < nlast * G; t += kWaves)
-        merge_row_wave<D, true>(v, lst[1 + t / G], it.head * G + t % G, tid & (kWaveSize - 1));
+    for (int t = wave; t < nlast * sets; t += kWaves) {
+        const int g0 = (t % sets) * RPW;
+        merge_rows<D, true>(v, lst[1 + t / sets], it.head * G + g0, min(RPW, G - g0), tid & (kWaveSize - 1));
+    }
 }
 
 // Shared items stage KV in LDS for their row-waves; private items split
@@ -962,7 +1040,7 @@ void decode_kernel(DecodeArgs a)
         if (a.queue && tid == 0)
             ticket = __hip_atomic_fetch_add(a.queue + (blockIdx.x % num_queues()) * kQueueStride, 1,
                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const WorkItem &it = a.items[cur];
+        const ItemRegs it = read_item(a.items, cur, lane);
         if (FUSED && tid == 0) lst[0] = 0;     // read after the item's barriers
         if (it.mode == kModeShared)
             shared_item<D, FUSED>(a, it, reinterpret_cast<uint16_t *>(lds), tid, lane, n, c, &next_item[par], ticket);
@@ -987,14 +1065,18 @@ void decode_kernel(DecodeArgs a)
     }
 }
 
-// Two-launch step: one wave per (request, query head).
+// Two-launch step: one one-wave workgroup per request and set of RPW =
+// 512 / D query heads (one-wave workgroups spread over every CU).
 template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a)
+__global__ __launch_bounds__(kWaveSize) void merge_kernel(MergeArgs a)
 {
-    const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
-    if (wid >= a.R * a.Hq) return;
+    constexpr int RPW = kWaveSize / (D / 8);
+    const int sets = (a.Hq + RPW - 1) / RPW;
+    const int wid = blockIdx.x;
+    if (wid >= a.R * sets) return;
     const MergeView v{a.merge_off, a.merge_rows, a.part_o, a.part_m, a.part_l, a.out, a.Hq, 0};
-    merge_row_wave<D, false>(v, wid / a.Hq, wid % a.Hq, threadIdx.x & (kWaveSize - 1));
+    const int qh0 = (wid % sets) * RPW;
+    merge_rows<D, false>(v, wid / sets, qh0, min(RPW, a.Hq - qh0), threadIdx.x & (kWaveSize - 1));
 }
 
 __global__ __launch_bounds__(256) void fill_kernel(uint32_t *buf, size_t words, uint32_t value)
@@ -1087,14 +1169,15 @@ int launch_decode(const DecodeArgs &a, int head_dim, void *stream)
 
 int launch_merge(const MergeArgs &a, int head_dim, void *stream)
 {
-    const int64_t waves = (int64_t)a.R * a.Hq;
+    const int rpw = kWaveSize / (head_dim / 8);
+    const int64_t waves = (int64_t)a.R * ((a.Hq + rpw - 1) / rpw);
     if (waves <= 0) return 0;
-    const dim3 grid((unsigned)((waves + 3) / 4));
+    const dim3 grid((unsigned)waves);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (head_dim == 128)
-        hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kWaveSize), 0, s, a);
     else
-        hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(kWaveSize), 0, s, a);
     return (int)hipGetLastError();
 }
 

@@ -138,6 +138,31 @@ def test_random_small_trees(D, HqHkv):
             run_both(w, ref, f"seed={seed} D={D} Hq={Hq} Hkv={Hkv} {opts}", **opts)
 
 
+def test_requests_not_numbered_in_tree_order():
+    """Request ids shuffled against the tree, so the requests of a node are
+    not consecutive ids: items then take their Q rows through the plan's
+    request table instead of a first id."""
+    from decode_attention_prefix_amd import cap
+    rng = np.random.default_rng(31)
+    nt, par, paths = wl.make_random_tree(rng, num_requests=48, max_depth=3, max_len=120,
+                                         num_q_heads=16, num_kv_heads=4, head_dim=128,
+                                         internal_end_prob=0.2, empty_root=False, min_len=1)
+    paths = [paths[i] for i in rng.permutation(len(paths))]
+    w = wl.make_workload(nt, par, paths, 16, 4, 128, rng)
+    h = cap.cap_tree_upload(w.tree)
+    p = cap.cap_plan_step(h, share_mode=1)
+    try:
+        v = cap.cap_plan_get_view(p)
+        gaps = [np.any(np.diff(v["rows"][ro:ro + nr]) != 1) for _, _, _, ro, nr, _, _, _ in v["items"]]
+        assert any(gaps), "the shuffle left every item's requests consecutive"
+    finally:
+        cap.cap_plan_free(p)
+        cap.cap_tree_free(h)
+    ref = oracle.decode(w.tree, w.q, w.k_pool, w.v_pool)
+    for opts in ({}, {"share_mode": 1}, {"share_mode": 1, "split_pages": 1}, {"shared_rows": 1 << 30}):
+        run_both(w, ref, f"shuffled request ids {opts}", **opts)
+
+
 def test_large_logits_and_single_token_requests():
     """Stretched logits (softmax close to one-hot) and 1-token contexts."""
     rng = np.random.default_rng(77)
