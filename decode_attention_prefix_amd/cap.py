@@ -77,7 +77,7 @@ class PlanView(ctypes.Structure):
                 ("stream_len", ctypes.c_int32), ("stream", ctypes.POINTER(ctypes.c_int32)),
                 ("rows_len", ctypes.c_int32), ("rows", ctypes.POINTER(ctypes.c_int32)),
                 ("num_requests", ctypes.c_int32), ("merge_off", ctypes.POINTER(ctypes.c_int32)),
-                ("merge_rows", ctypes.POINTER(ctypes.c_int32))]
+                ("slot_rows_len", ctypes.c_int32), ("slot_rows", ctypes.POINTER(ctypes.c_int32))]
 
 
 _lib = None
@@ -216,7 +216,7 @@ def cap_plan_get_view(plan: int) -> dict:
             "stream": arr(v.stream, v.stream_len),
             "rows": arr(v.rows, v.rows_len),
             "merge_off": arr(v.merge_off, v.num_requests + 1),
-            "merge_rows": arr(v.merge_rows, int(arr(v.merge_off, v.num_requests + 1)[-1]))}
+            "slot_rows": arr(v.slot_rows, v.slot_rows_len)}
 
 
 def cap_plan_upload(plan: int, dev_buf: int, nbytes: int, stream: int = 0) -> None:

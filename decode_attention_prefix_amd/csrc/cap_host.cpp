@@ -79,9 +79,10 @@ struct cap_plan {
     std::vector<WorkItem> items;          // one workgroup each
     std::vector<int32_t> stream;      // (physical page << 5) | (ntok - 1)
     std::vector<int32_t> rows;        // request ids
-    std::vector<int32_t> merge_off, merge_rows;
+    std::vector<int32_t> merge_off;   // request r's partial rows: merge_off[r] .. merge_off[r+1] - 1
+    std::vector<int32_t> slot_rows;   // partial row of each (task, request) pair, by task
     // device image
-    size_t off_items = 0, off_stream = 0, off_rows = 0, off_moff = 0, off_mrows = 0, off_cnt = 0, off_queue = 0,
+    size_t off_items = 0, off_stream = 0, off_rows = 0, off_moff = 0, off_srows = 0, off_cnt = 0, off_queue = 0,
            dev_bytes = 0;
     bool work_queue = false;          // item_dispatch 1
     std::vector<unsigned char> host_image;
@@ -343,7 +344,7 @@ void fill_defaults(cap_plan_opts &o)
     if (o.shared_rows == 0) o.shared_rows = cap::kPrivateRows;
     if (o.num_cus == 0) o.num_cus = 256;
     if (o.shared_cost == 0.f) o.shared_cost = 2.0f;
-    if (o.rounds == 0.f) o.rounds = 2.0f;
+    if (o.rounds == 0.f) o.rounds = 1.5f;
     if (o.share_margin == 0.f) o.share_margin = 1.0f;
     if (o.order == 0) o.order = 2;
     if (o.private_rounds == 0.f) o.private_rounds = 1.5f;
@@ -530,12 +531,23 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
     } else {
         seq.assign(tasks.begin(), tasks.end());
     }
-    std::vector<std::vector<int32_t>> req_rows(tree->R);
-    int32_t slot_rows = 0;
+    // Partial rows: each request's are one contiguous block (merge_off), so a
+    // merge finds them without a table; a task reaches the row of each of its
+    // requests through slot_rows[sb + q], filled in dispatch order.
+    p->merge_off.assign(tree->R + 1, 0);
+    for (const Task &tk : seq)
+        for (int q = 0; q < tk.nr; ++q) ++p->merge_off[p->rows[tk.ro + q] + 1];
+    int32_t maxp = 0;
+    for (int r = 0; r < tree->R; ++r) {
+        maxp = std::max<int32_t>(maxp, p->merge_off[r + 1]);
+        p->merge_off[r + 1] += p->merge_off[r];
+    }
+    const int32_t slot_rows = p->merge_off[tree->R];
+    std::vector<int32_t> fill(p->merge_off.begin(), p->merge_off.end() - 1);
+    p->slot_rows.reserve(slot_rows);
     for (Task &tk : seq) {
-        tk.sb = slot_rows;
-        for (int q = 0; q < tk.nr; ++q) req_rows[p->rows[tk.ro + q]].push_back(slot_rows + q);
-        slot_rows += tk.nr;
+        tk.sb = (int32_t)p->slot_rows.size();
+        for (int q = 0; q < tk.nr; ++q) p->slot_rows.push_back(fill[p->rows[tk.ro + q]]++);
         pl.max_pages = std::max<int>(pl.max_pages, tk.np);
     }
     p->items.reserve(seq.size() * Hkv);
@@ -543,15 +555,8 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
         for (int h = 0; h < Hkv; ++h)
             p->items.push_back(WorkItem{tk.so, tk.np, h, tk.ro, tk.nr, tk.sb,
                                         tk.shared ? cap::kModeShared : cap::kModePrivate, 0});
-    p->merge_off.assign(tree->R + 1, 0);
-    int32_t maxp = 0;
-    for (int r = 0; r < tree->R; ++r) {
-        p->merge_off[r + 1] = p->merge_off[r] + (int32_t)req_rows[r].size();
-        p->merge_rows.insert(p->merge_rows.end(), req_rows[r].begin(), req_rows[r].end());
-        maxp = std::max<int32_t>(maxp, (int32_t)req_rows[r].size());
-    }
 
-    // device image: items | stream | rows | merge_off | merge_rows | counters |
+    // device image: items | stream | rows | slot_rows | merge_off | counters |
     // queue (the fused step's arrival counters, one per request and KV head,
     // and the work queue's two counters, all zero)
     // device items: each item plus its requests' first id when they are
@@ -588,17 +593,17 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
     p->off_items = 0;
     p->off_stream = align_up(dev_items.size() * sizeof(cap::DevItem));
     p->off_rows = p->off_stream + align_up(p->stream.size() * 4);
-    p->off_moff = p->off_rows + align_up(p->rows.size() * 4);
-    p->off_mrows = p->off_moff + align_up(p->merge_off.size() * 4);
-    p->off_cnt = p->off_mrows + align_up(p->merge_rows.size() * 4);
+    p->off_srows = p->off_rows + align_up(p->rows.size() * 4);
+    p->off_moff = p->off_srows + align_up(p->slot_rows.size() * 4);
+    p->off_cnt = p->off_moff + align_up(p->merge_off.size() * 4);
     p->off_queue = p->off_cnt + align_up((size_t)tree->R * Hkv * 4);
     p->dev_bytes = p->off_queue + align_up(cap::kQueueInts * 4);
     p->host_image.assign(p->dev_bytes, 0);
     std::memcpy(p->host_image.data() + p->off_items, dev_items.data(), dev_items.size() * sizeof(cap::DevItem));
     std::memcpy(p->host_image.data() + p->off_stream, p->stream.data(), p->stream.size() * 4);
     std::memcpy(p->host_image.data() + p->off_rows, p->rows.data(), p->rows.size() * 4);
+    std::memcpy(p->host_image.data() + p->off_srows, p->slot_rows.data(), p->slot_rows.size() * 4);
     std::memcpy(p->host_image.data() + p->off_moff, p->merge_off.data(), p->merge_off.size() * 4);
-    std::memcpy(p->host_image.data() + p->off_mrows, p->merge_rows.data(), p->merge_rows.size() * 4);
 
     cap_plan_stats &s = p->stats;
     s.num_items = (int64_t)p->items.size();
@@ -643,7 +648,8 @@ cap_status cap_plan_get_view(const cap_plan *plan, cap_plan_view *v)
     v->rows = plan->rows.data();
     v->num_requests = plan->tree->R;
     v->merge_off = plan->merge_off.data();
-    v->merge_rows = plan->merge_rows.data();
+    v->slot_rows_len = (int32_t)plan->slot_rows.size();
+    v->slot_rows = plan->slot_rows.data();
     return CAP_OK;
 }
 
@@ -689,6 +695,7 @@ static cap_status decode_args(const cap_plan *plan, const void *q, const void *k
     a.items = reinterpret_cast<const cap::DevItem *>(d + plan->off_items);
     a.stream = reinterpret_cast<const int32_t *>(d + plan->off_stream);
     a.rows = reinterpret_cast<const int32_t *>(d + plan->off_rows);
+    a.slot_rows = reinterpret_cast<const int32_t *>(d + plan->off_srows);
     a.q = static_cast<const uint16_t *>(q);
     a.k_pool = static_cast<const uint16_t *>(k_pool);
     a.v_pool = static_cast<const uint16_t *>(v_pool);
@@ -729,7 +736,6 @@ cap_status cap_decode_step(const cap_plan *plan, const void *q, const void *k_po
     char *d = static_cast<char *>(plan->dev);
     a.counters = reinterpret_cast<int32_t *>(d + plan->off_cnt);
     a.merge_off = reinterpret_cast<const int32_t *>(d + plan->off_moff);
-    a.merge_rows = reinterpret_cast<const int32_t *>(d + plan->off_mrows);
     a.out = static_cast<uint16_t *>(out);
     const int e = cap::launch_decode(a, plan->tree->attn.head_dim, stream);
     if (e != 0) return fail(CAP_ERR_HIP, "decode launch failed: %s", cap::hip_error_string(e));
@@ -749,7 +755,6 @@ cap_status cap_merge_partials(const cap_plan *plan, const void *workspace, size_
     if (st != CAP_OK) return st;
     const char *d = static_cast<const char *>(plan->dev);
     a.merge_off = reinterpret_cast<const int32_t *>(d + plan->off_moff);
-    a.merge_rows = reinterpret_cast<const int32_t *>(d + plan->off_mrows);
     a.part_o = o;
     a.part_m = m;
     a.part_l = l;

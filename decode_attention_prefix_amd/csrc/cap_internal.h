@@ -65,6 +65,7 @@ struct DecodeArgs {
     const DevItem *items;          // one workgroup each
     const int32_t *stream;       // page-stream entries: (physical page << 5) | (ntok - 1)
     const int32_t *rows;         // request ids of each item's request list
+    const int32_t *slot_rows;    // partial row of each item request: slot_rows[slot_base + q]
     const uint16_t *q;           // [R][Hq][D] bf16
     const uint16_t *k_pool;      // [pages][Hkv][D/8][16][8] bf16
     const uint16_t *v_pool;      // [pages][Hkv][D][16] bf16
@@ -80,15 +81,13 @@ struct DecodeArgs {
     int32_t *queue;
     // fused step only (counters == nullptr: partials are left for merge_kernel)
     int32_t *counters;           // [R][Hkv] arrival counts, zero between steps
-    const int32_t *merge_off;    // [R+1] partial rows of each request
-    const int32_t *merge_rows;
+    const int32_t *merge_off;    // [R+1]: request r's partial rows are merge_off[r] .. merge_off[r+1] - 1
     uint16_t *out;               // [R][Hq][D] bf16
     int32_t slots;               // partial slots (fused: slots * D * 2 < 2^31)
 };
 
 struct MergeArgs {
-    const int32_t *merge_off;    // [R+1]
-    const int32_t *merge_rows;   // partial rows per request
+    const int32_t *merge_off;    // [R+1]: request r's partial rows are merge_off[r] .. merge_off[r+1] - 1
     const uint16_t *part_o;      // fp16 o / l
     const float *part_m;
     const float *part_l;

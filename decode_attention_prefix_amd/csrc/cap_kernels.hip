@@ -483,10 +483,23 @@ __device__ __forceinline__ void store_partial_ml(const DecodeArgs &a, int64_t sl
     }
 }
 
-// Partials of rows row0 + 16b + n: slot = (slot_base + row / G) * Hq + head * G + row % G.
+// Partial row of each of a lane's rows row0 + 16b + n (read when the item
+// starts; used when its partials are written).
+template <int RB>
+__device__ __forceinline__ void load_slot_rows(int (&srow)[RB], const DecodeArgs &a, const ItemRegs &it, int row0,
+                                               int nrows, int n)
+{
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+        const int row = row0 + 16 * b + n;
+        srow[b] = row < nrows ? a.slot_rows[it.slot_base + row / a.G] : 0;
+    }
+}
+
+// Partials of rows row0 + 16b + n: slot = srow[b] * Hq + head * G + row % G.
 template <int D, int RB, bool FUSED>
-__device__ __forceinline__ void write_partials(const DecodeArgs &a, const ItemRegs &it, int row0, int nrows,
-                                               int nblk, const f32x4 (&o)[RB][D / 16],
+__device__ __forceinline__ void write_partials(const DecodeArgs &a, const ItemRegs &it, const int (&srow)[RB],
+                                               int row0, int nrows, int nblk, const f32x4 (&o)[RB][D / 16],
                                                const float (&m_ref)[RB], const float (&l_run)[RB], int n,
                                                int c)
 {
@@ -500,7 +513,7 @@ __device__ __forceinline__ void write_partials(const DecodeArgs &a, const ItemRe
         const float inv = l > 0.f ? 1.0f / l : 0.f;
         const int row = row0 + 16 * b + n;
         if (row < nrows) {
-            const int64_t slot = (int64_t)(it.slot_base + row / G) * a.Hq + it.head * G + row % G;
+            const int64_t slot = (int64_t)srow[b] * a.Hq + it.head * G + row % G;
 #pragma unroll
             for (int j = 0; j < D / 16; ++j) store_partial_o<D, FUSED>(a, slot, 16 * j + 4 * c, o[b][j] * inv);
             if (c == 0) store_partial_ml<FUSED>(a, slot, m_ref[b], l);
@@ -546,6 +559,9 @@ __device__ __forceinline__ void private_item(const DecodeArgs &a, const ItemRegs
 
     u32x4 qf[1][D / 32];
     load_q<D, 1>(qf, a, it, 0, nrows, n, c);
+    // partial row of the row this thread stores at the end (row tid / 16)
+    int srow[1];
+    load_slot_rows<1>(srow, a, it, 0, nrows, tid / (kSharedThreads / 16));
     f32x4 o[1][D / 16];
 #pragma unroll
     for (int j = 0; j < D / 16; ++j) o[0][j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -613,7 +629,7 @@ __device__ __forceinline__ void private_item(const DecodeArgs &a, const ItemRegs
     }
     if (row < nrows) {
         const int G = a.G;
-        const int64_t slot = (int64_t)(it.slot_base + row / G) * a.Hq + it.head * G + row % G;
+        const int64_t slot = (int64_t)srow[0] * a.Hq + it.head * G + row % G;
         const float inv = L > 0.f ? 1.0f / L : 0.f;
 #pragma unroll
         for (int v = 0; v < V; v += 4)
@@ -776,6 +792,8 @@ __device__ __forceinline__ void shared_item(const DecodeArgs &a, const ItemRegs 
     const int lane_e = load_page_table(a, it, 0, it.npages, lane);
     u32x4 qf[2][D / 32];
     load_q<D, 2>(qf, a, it, row0, nrows, n, c);         // before the ring loads: loads land in order
+    int srow[2];
+    load_slot_rows<2>(srow, a, it, row0, nrows, n);
     const int nsteps = (it.npages + 1) >> 1;
     const int np = it.npages;
     ring_start<D>(a, it, nsteps, lane_e, lds, wave, lane);
@@ -833,22 +851,21 @@ __device__ __forceinline__ void shared_item(const DecodeArgs &a, const ItemRegs 
         for (int s = 0; s + 1 < nsteps; ++s) ring_next<D>(a, it, nsteps, s, lane_e, lds, wave, lane);
     }
     if (tid == 0) *publish = next_item_of(a, ticket);   // the ticket has long returned
-    write_partials<D, 2, FUSED>(a, it, row0, nrows, nblk, o, m_ref, l_run, n, c);
+    write_partials<D, 2, FUSED>(a, it, srow, row0, nrows, nblk, o, m_ref, l_run, n, c);
 }
 
 // ------------------------------------------------------------------ merge
 // Where a merge reads its partials and writes its output.
 struct MergeView {
-    const int32_t *merge_off;    // [R+1]
-    const int32_t *merge_rows;   // partial rows of each request
+    const int32_t *merge_off;    // [R+1]: request r's partial rows are merge_off[r] .. merge_off[r+1] - 1
     const uint16_t *part_o;      // fp16 o / l
     const float *part_m, *part_l;
     uint16_t *out;               // [R][Hq][D] bf16
     int32_t Hq, slots;
 };
 
-// Loads of one block of up to 16 partials of one merge row: lane i of the
-// wave holds partial row `prow` of partial i of the current list window.
+// Loads of one block of up to 16 partials (partial rows row0 .. row0 + nb - 1)
+// of one merge row.
 template <int D>
 struct MergeBlock {
     static constexpr int NB = 16;
@@ -857,13 +874,12 @@ struct MergeBlock {
 };
 
 template <int D, bool COHERENT>
-__device__ __forceinline__ void merge_load(MergeBlock<D> &b, const MergeView &v, int prow, int k0, int nb,
-                                           int qh, int dc)
+__device__ __forceinline__ void merge_load(MergeBlock<D> &b, const MergeView &v, int row0, int nb, int qh, int dc)
 {
 #pragma unroll
     for (int i = 0; i < MergeBlock<D>::NB; ++i) {
         if (i < nb) {
-            const int slot = __builtin_amdgcn_readlane(prow, k0 + i) * v.Hq + qh;
+            const int slot = (row0 + i) * v.Hq + qh;
             if constexpr (COHERENT) {
                 b.m[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                     buf_rsrc(v.part_m, v.slots * 4), slot * 4, 0, kCoherent));
@@ -915,14 +931,14 @@ __device__ __forceinline__ void merge_fold(const MergeBlock<D> &b, float &M, flo
 // One wave merges the partials of query heads qh0 .. qh0 + nh - 1 (nh <=
 // RPW = 512 / D) of request r and writes their bf16 output rows:
 //   out = sum_i 2^(m_i - M) l_i (o_i / l_i) / sum_i 2^(m_i - M) l_i,
-// the partials holding the normalised o_i / l_i.  Every query head of a
-// request has the same partial rows (merge list), so the list is read once
-// per wave, 64 entries at a time, one per lane.  Lane = (row rho, dim chunk
-// dc): D / 8 lanes per row, 8 dims (one 16-byte fp16 load per partial) per
-// lane; each lane also loads m and l of its row (the row's lanes share those
-// addresses), so no lane exchanges anything.  Partials go 16 per block, the
-// next block's loads in flight while a block is folded in.  COHERENT: sc1
-// loads (fused step).
+// the partials holding the normalised o_i / l_i.  A request's partial rows
+// are one block (merge_off), the same for all its query heads, so a wave only
+// reads where the block starts.  Lane = (row rho, dim chunk dc): D / 8 lanes
+// per row, 8 dims (one 16-byte fp16 load per partial) per lane; each lane
+// also loads m and l of its row (the row's lanes share those addresses), so
+// no lane exchanges anything.  Partials go 16 per block, the next block's
+// loads in flight while a block is folded in.  COHERENT: sc1 loads (fused
+// step, one block at a time).
 template <int D, bool COHERENT>
 __device__ __forceinline__ void merge_rows(const MergeView &v, int r, int qh0, int nh, int lane)
 {
@@ -936,16 +952,21 @@ __device__ __forceinline__ void merge_rows(const MergeView &v, int r, int qh0, i
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    for (int w0 = 0; w0 < np; w0 += kWaveSize) {
-        const int nw = min(kWaveSize, np - w0);
-        const int prow = lane < nw ? v.merge_rows[beg + w0 + lane] : 0;
-        MergeBlock<D> ba, bb;
-        merge_load<D, COHERENT>(ba, v, prow, 0, min(NB, nw), qh, dc);
-        for (int k = 0; k < nw; k += 2 * NB) {
-            if (k + NB < nw) merge_load<D, COHERENT>(bb, v, prow, k + NB, min(NB, nw - k - NB), qh, dc);
+    if constexpr (COHERENT) {
+        // inside the decode kernel: one block at a time (its register budget)
+        for (int k = 0; k < np; k += NB) {
+            MergeBlock<D> ba;
+            merge_load<D, COHERENT>(ba, v, beg + k, min(NB, np - k), qh, dc);
             merge_fold<D>(ba, M, L, acc);
-            if (k + NB >= nw) break;
-            if (k + 2 * NB < nw) merge_load<D, COHERENT>(ba, v, prow, k + 2 * NB, min(NB, nw - k - 2 * NB), qh, dc);
+        }
+    } else {
+        MergeBlock<D> ba, bb;
+        merge_load<D, COHERENT>(ba, v, beg, min(NB, np), qh, dc);
+        for (int k = 0; k < np; k += 2 * NB) {
+            if (k + NB < np) merge_load<D, COHERENT>(bb, v, beg + k + NB, min(NB, np - k - NB), qh, dc);
+            merge_fold<D>(ba, M, L, acc);
+            if (k + NB >= np) break;
+            if (k + 2 * NB < np) merge_load<D, COHERENT>(ba, v, beg + k + 2 * NB, min(NB, np - k - 2 * NB), qh, dc);
             merge_fold<D>(bb, M, L, acc);
         }
     }
@@ -985,7 +1006,7 @@ __device__ __forceinline__ void finish_item(const DecodeArgs &a, const ItemRegs 
     __syncthreads();
     const int nlast = lst[0];
     if (nlast == 0) return;
-    const MergeView v{a.merge_off, a.merge_rows, a.part_o, a.part_m, a.part_l, a.out, a.Hq, a.slots};
+    const MergeView v{a.merge_off, a.part_o, a.part_m, a.part_l, a.out, a.Hq, a.slots};
     // row sets of up to RPW query heads of this KV head, one wave each
     constexpr int RPW = kWaveSize / (D / 8);
     const int G = a.G, sets = (G + RPW - 1) / RPW;
@@ -1074,7 +1095,7 @@ __global__ __launch_bounds__(kWaveSize) void merge_kernel(MergeArgs a)
     const int sets = (a.Hq + RPW - 1) / RPW;
     const int wid = blockIdx.x;
     if (wid >= a.R * sets) return;
-    const MergeView v{a.merge_off, a.merge_rows, a.part_o, a.part_m, a.part_l, a.out, a.Hq, 0};
+    const MergeView v{a.merge_off, a.part_o, a.part_m, a.part_l, a.out, a.Hq, 0};
     const int qh0 = (wid % sets) * RPW;
     merge_rows<D, false>(v, wid / sets, qh0, min(RPW, a.Hq - qh0), threadIdx.x & (kWaveSize - 1));
 }

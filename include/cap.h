@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define CAP_ABI_VERSION 4
+#define CAP_ABI_VERSION 5
 
 typedef enum cap_status {
     CAP_OK = 0,
@@ -120,7 +120,7 @@ typedef struct cap_plan_opts {
     int32_t num_cus;          /* 0 = 256 (MI355X); used by the cost model */
     float shared_cost;        /* 0 = 2.0; cost of a shared item's page relative to a
                                  private item's page, used to size items */
-    float rounds;             /* 0 = 2.0; target work items per CU (two run at once) */
+    float rounds;             /* 0 = 1.5; target work items per CU (two run at once) */
     float share_margin;       /* 0 = 1.0; share a node only if saved bytes exceed
                                  margin x added partial bytes */
     int32_t order;            /* dispatch order of the work items (workgroups start in
@@ -182,7 +182,8 @@ typedef struct cap_work_item {
     int32_t head;         /* KV head */
     int32_t row_off;      /* first entry of its request list in the plan's row table */
     int32_t nreq;         /* requests served; query rows = nreq x G */
-    int32_t slot_base;    /* partial row of its first request */
+    int32_t slot_base;    /* first entry of its requests' partial rows in the plan's
+                             slot-row table (request position q: slot_rows[slot_base + q]) */
     int32_t mode;         /* 0 private, 1 shared */
     int32_t reserved;
 } cap_work_item;
@@ -191,13 +192,15 @@ typedef struct cap_work_item {
  * Page-stream entry e: physical pool page = e >> 5 (resolved from the tree's
  * page table when the plan is built), valid tokens = (e & 31) + 1.
  * Partial slot of item row i (request position i/G, query head head*G + i%G):
- *   (slot_base + i/G) * Hq + head*G + i%G.
- * Request r's partial rows: merge_rows[merge_off[r] .. merge_off[r+1]). */
+ *   slot_rows[slot_base + i/G] * Hq + head*G + i%G.
+ * Request r's partial rows are the block merge_off[r] .. merge_off[r+1] - 1
+ * (each row written by exactly one item per KV head). */
 typedef struct cap_plan_view {
     int32_t num_items;         const cap_work_item *items;
     int32_t stream_len;        const int32_t *stream;
     int32_t rows_len;          const int32_t *rows;
-    int32_t num_requests;      const int32_t *merge_off;  const int32_t *merge_rows;
+    int32_t num_requests;      const int32_t *merge_off;
+    int32_t slot_rows_len;     const int32_t *slot_rows;
 } cap_plan_view;
 
 int32_t cap_abi_version(void);

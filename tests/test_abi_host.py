@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), f"libcap.so does not export {n}"
     assert set(cap.EXPORTED) == names
-    assert cap.cap_abi_version() == 4
+    assert cap.cap_abi_version() == 5
 
 
 def small_tree(**over):
@@ -136,6 +136,7 @@ def check_coverage(tree, plan_handle):
     got = {(r, h): [] for r in range(R) for h in range(Hkv)}
     slot_writes = np.zeros(int(st["partial_rows"]) * Hq, np.int64)
     slot_rows_of = {r: set() for r in range(R)}
+    srows = v["slot_rows"]
     for so, npg, head, ro, nreq, sb, mode, _ in v["items"]:
         max_rows, max_pages = (128, 64) if mode == 1 else (16, 256)
         assert mode in (0, 1)
@@ -144,16 +145,17 @@ def check_coverage(tree, plan_handle):
         pages = [(int(e) >> 5, (int(e) & 31) + 1) for e in ents]
         for qpos, r in enumerate(v["rows"][ro:ro + nreq]):
             got[(int(r), int(head))].extend(pages)
+            row = int(srows[sb + qpos])
             for i in range(G):
-                slot_writes[(sb + qpos) * Hq + head * G + i] += 1
-            slot_rows_of[int(r)].add(int(sb + qpos))
+                slot_writes[row * Hq + head * G + i] += 1
+            slot_rows_of[int(r)].add(row)
     for (r, h), s in got.items():
         assert sorted(s) == want[r], f"request {r} head {h}"
     assert np.all(slot_writes == 1)
+    assert len(srows) == int(st["partial_rows"])
     for r in range(R):
-        ml = v["merge_rows"][v["merge_off"][r]:v["merge_off"][r + 1]]
-        assert len(set(ml.tolist())) == len(ml)
-        assert set(ml.tolist()) == slot_rows_of[r]
+        # request r's partial rows are one contiguous block
+        assert set(range(int(v["merge_off"][r]), int(v["merge_off"][r + 1]))) == slot_rows_of[r]
     assert st["num_items"] == len(v["items"])
     assert st["num_shared_items"] == int((v["items"][:, 6] == 1).sum()) if len(v["items"]) else True
     if G > 16 and len(v["items"]):
