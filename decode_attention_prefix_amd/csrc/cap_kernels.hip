@@ -1,6 +1,7 @@
 // cap_kernels.hip -- gfx950 (CDNA4) kernels of libcap.
 //
-// decode_kernel: one 4-wave workgroup per work item.  A work item is a run of
+// decode_kernel: a 4-wave workgroup per work item (or, with work queues, two
+// resident workgroups per CU taking items in turn).  A work item is a run of
 // KV pages of one KV head together with the query rows (requests x GQA
 // heads) that read those pages, so the pages come from HBM once for the
 // whole row group -- the point of the Capillary Kernels project page
@@ -22,9 +23,12 @@
 // leaves as tokens 4c..4c+3 of both pages, are moved to that order with two
 // lane swaps per register pair.
 //
-// Softmax is online in base 2 (scale folded with log2 e, exp via v_exp_f32)
-// with a lazily moved per-row reference maximum.  Each item writes (m, l, o)
-// for its rows into write-once partial slots; merge_kernel (or, in the fused
+// A workgroup reads its item once into registers; the item carries its first
+// page ids and its first request id, so the first K/V and Q loads need no
+// other table.  Softmax is online in base 2 (scale folded with log2 e, exp
+// via v_exp_f32) with a lazily moved per-row reference maximum.  Each item
+// writes (m, l, o/l) for its rows into write-once partial rows (each
+// request's rows one contiguous block); merge_kernel (or, in the fused
 // step, the item that completes a request) combines the partials of each
 // (request, head) with log-sum-exp rescaling -- the partial-result
 // combination of the project page's second paragraph, through global
