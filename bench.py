@@ -18,7 +18,6 @@ Prints one JSON line.  Default workload: the 64-request shared-system-prompt
 tree (4096-token root, suffixes U[256,1024], 32 q / 8 KV heads, D=128).
 """
 import argparse
-import hashlib
 import json
 import os
 import platform
@@ -29,15 +28,11 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+from decode_attention_prefix_amd.prof_summary import kernel_hash  # noqa: E402
+
 METRIC = "decode attn unique-KV HBM GB/s (% of peak) + request-heads/s per step, 1 GPU"
 PEAK_HBM_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "decode_attention_prefix_amd", "csrc", "cap_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_cfg{cfg}_traffic.txt")
-
-
-def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
 def load_traffic(cfg: int, kernel: str):
@@ -52,7 +47,7 @@ def load_traffic(cfg: int, kernel: str):
         if ":" in line:
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256_16") != kernel_hash() or kv.get("kernel") != kernel:
+    if kv.get("kernel_code_sha256_16") != kernel_hash() or kv.get("kernel") != kernel:
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])

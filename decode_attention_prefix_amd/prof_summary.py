@@ -17,6 +17,7 @@ import argparse
 import csv
 import hashlib
 import os
+import re
 import statistics
 from collections import defaultdict
 
@@ -25,8 +26,14 @@ KERNEL_SRC = os.path.join(ROOT, "decode_attention_prefix_amd", "csrc", "cap_kern
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel source's code: comments and whitespace removed, so
+    an edit of the comments alone keeps counters taken on the same code."""
+    with open(KERNEL_SRC) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    code = "".join(src.split())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def _short(name: str) -> str:
@@ -78,7 +85,7 @@ def main(argv=None):
     lines = [f"rocprofv3 kernel-trace summary: bench.py --config {cfg} ({a.workload})",
              f"command: cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o kt -- "
              f"python3 <repo>/bench.py --config {cfg} {a.bench_args}",
-             f"kernel_source_sha256_16: {h}", "",
+             f"kernel_code_sha256_16: {h}", "",
              f"{'kernel':40s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
     for name, calls, avg, mn, mx in kt:
         lines.append(f"{name:40s} {calls:6d} {avg:9.3f} {mn:9.3f} {mx:9.3f}")
@@ -104,7 +111,7 @@ def main(argv=None):
              f"<repo>/bench.py --config {cfg} --no-cpu-baseline --steps 3 --warmup 1 --copy-probe-mb {a.copy_mb}",
              f"  cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out> -o pmc -- python3 "
              f"<repo>/bench.py --config {cfg} --no-cpu-baseline --steps 3 --warmup 1 --copy-probe-mb {a.copy_mb}",
-             f"kernel_source_sha256_16: {h}",
+             f"kernel_code_sha256_16: {h}",
              f"kernel: {a.kernel}",
              f"copy_kernel_{a.copy_mb}MiB_fetch_kib: {fetch['copy_kernel']:.1f}",
              f"copy_kernel_{a.copy_mb}MiB_write_kib: {write['copy_kernel']:.1f}",
