@@ -53,6 +53,20 @@ __device__ __forceinline__ u32x4 ld16(const uint16_t *p)
     return *reinterpret_cast<const u32x4 *>(p);
 }
 
+// K/V pages are read once per item: non-temporal loads (the nt cache policy:
+// streamed, not kept in L2).  A read-only probe streams ~12% faster with
+// them (7.1 vs 6.3 TB/s with per-workgroup contiguous runs).
+constexpr bool kKvNonTemporal = true;
+constexpr int kKvDmaPolicy = 0;          // cache-policy bits of the ring's global->LDS loads
+
+__device__ __forceinline__ u32x4 ld16_kv(const uint16_t *p)
+{
+    if constexpr (kKvNonTemporal)
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    else
+        return *reinterpret_cast<const u32x4 *>(p);
+}
+
 __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -112,9 +126,11 @@ struct Step {
 // from the item itself (no wait on the page stream for the first two steps),
 // later ones from the wave's page table held in lanes (lane i: raw stream
 // entry of page i) via v_readlane.  Every call issues the same number of
-// loads whatever the step (a missing second page re-reads the first; steps
-// past the end re-read the last), so the wait counts of the software
-// pipeline stay exact.
+// loads whatever the step, so the wait counts of the software pipeline stay
+// the same on every path: a missing second page re-reads the first, and a
+// step past the end (the pipeline's last load) points every lane at the
+// first 16 bytes of Q, which this item has just read (no HBM traffic; the
+// values are never used).
 template <int D>
 __device__ __forceinline__ void load_step(Step<D> &f, const DecodeArgs &a, const ItemRegs &it, int wave, int count,
                                           int s, int lane_e, int n, int c)
@@ -138,18 +154,22 @@ __device__ __forceinline__ void load_step(Step<D> &f, const DecodeArgs &a, const
     const int64_t p1 = e1 >> 5;
     f.nt0 = (e0 & 31) + 1;
     f.nt1 = has1 ? (e1 & 31) + 1 : 0;
-    const uint16_t *kb0 = a.k_pool + (p0 * a.Hkv + head) * blk;
-    const uint16_t *vb0 = a.v_pool + (p0 * a.Hkv + head) * blk;
-    const uint16_t *kb1 = a.k_pool + (p1 * a.Hkv + head) * blk;
-    const uint16_t *vb1 = a.v_pool + (p1 * a.Hkv + head) * blk;
+    const bool live = s < nsteps;
+    const uint16_t *kb0 = live ? a.k_pool + (p0 * a.Hkv + head) * blk : a.q;
+    const uint16_t *vb0 = live ? a.v_pool + (p0 * a.Hkv + head) * blk : a.q;
+    const uint16_t *kb1 = live ? a.k_pool + (p1 * a.Hkv + head) * blk : a.q;
+    const uint16_t *vb1 = live ? a.v_pool + (p1 * a.Hkv + head) * blk : a.q;
+    const int koff = live ? (c * kPage + n) * 8 : 0;                 // lane offsets (elements)
+    const int voff = live ? n * kPage + 8 * (c & 1) : 0;
+    const int kstep = live ? 4 * kPage * 8 : 0, vstep = live ? 16 * kPage : 0;
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) {
-        f.k0[i] = ld16(kb0 + ((4 * i + c) * kPage + n) * 8);
-        f.k1[i] = ld16(kb1 + ((4 * i + c) * kPage + n) * 8);
+        f.k0[i] = ld16_kv(kb0 + koff + i * kstep);
+        f.k1[i] = ld16_kv(kb1 + koff + i * kstep);
     }
-    const uint16_t *vb = ((c >> 1) ? vb1 : vb0) + 8 * (c & 1);
+    const uint16_t *vb = ((c >> 1) ? vb1 : vb0) + voff;
 #pragma unroll
-    for (int j = 0; j < D / 16; ++j) f.v[j] = ld16(vb + (16 * j + n) * kPage);
+    for (int j = 0; j < D / 16; ++j) f.v[j] = ld16_kv(vb + j * vstep);
 }
 
 // Zero the V elements of tokens >= nt -- those slots may hold NaN, and
@@ -703,7 +723,7 @@ __device__ __forceinline__ void issue_dma(const DecodeArgs &a, const ItemRegs &i
         __builtin_amdgcn_global_load_lds(
             (const void __attribute__((address_space(1))) *)g,
             (void __attribute__((address_space(3))) *)(slot + b * T::kBlock + (piece % T::kPPB) * kWaveSize * 8),
-            16, 0, 0);
+            16, 0, kKvDmaPolicy);
     }
 }
 
