@@ -149,7 +149,7 @@ def main():
         evict()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        cap.cap_bench_read(probe.data_ptr(), probe_bytes, sink.data_ptr(), sp)
+        cap.cap_bench_read_stream(probe.data_ptr(), probe_bytes, sink.data_ptr(), sp)
         b.record(stream)
         b.synchronize()
         read_ms.append(a.elapsed_time(b))

@@ -25,7 +25,8 @@ EXPORTED = [
     "cap_abi_version", "cap_last_error", "cap_plan_opts_default", "cap_tree_device_bytes",
     "cap_tree_upload", "cap_tree_free", "cap_plan_step", "cap_plan_get_stats",
     "cap_plan_get_view", "cap_plan_upload", "cap_decode_attention", "cap_merge_partials",
-    "cap_decode_step", "cap_plan_free", "cap_bench_fill", "cap_bench_read", "cap_bench_copy",
+    "cap_decode_step", "cap_plan_free", "cap_bench_fill", "cap_bench_read", "cap_bench_read_stream",
+    "cap_bench_copy",
 ]
 
 
@@ -113,11 +114,12 @@ def lib():
         L.cap_plan_free.restype = None
         L.cap_bench_fill.argtypes = [vp, sz, ctypes.c_uint32, vp]
         L.cap_bench_read.argtypes = [vp, sz, vp, vp]
+        L.cap_bench_read_stream.argtypes = [vp, sz, vp, vp]
         L.cap_bench_copy.argtypes = [vp, vp, sz, vp]
         for name in ("cap_tree_device_bytes", "cap_tree_upload", "cap_plan_step",
                      "cap_plan_get_stats", "cap_plan_get_view", "cap_plan_upload",
                      "cap_decode_attention", "cap_merge_partials", "cap_decode_step", "cap_bench_fill",
-                     "cap_bench_read", "cap_bench_copy"):
+                     "cap_bench_read", "cap_bench_read_stream", "cap_bench_copy"):
             getattr(L, name).restype = st
         _lib = L
     return _lib
@@ -256,6 +258,11 @@ def cap_bench_fill(buf: int, nbytes: int, value: int = 0, stream: int = 0) -> No
 def cap_bench_read(buf: int, nbytes: int, sink: int, stream: int = 0) -> None:
     _check(lib().cap_bench_read(ctypes.c_void_p(buf), nbytes, ctypes.c_void_p(sink),
                                 ctypes.c_void_p(stream or None)))
+
+
+def cap_bench_read_stream(buf: int, nbytes: int, sink: int, stream: int = 0) -> None:
+    _check(lib().cap_bench_read_stream(ctypes.c_void_p(buf), nbytes, ctypes.c_void_p(sink),
+                                       ctypes.c_void_p(stream or None)))
 
 
 def cap_bench_copy(dst: int, src: int, nbytes: int, stream: int = 0) -> None:

@@ -343,11 +343,11 @@ void fill_defaults(cap_plan_opts &o)
     if (o.share_mode == 2) o.share_mode = -1;
     if (o.shared_rows == 0) o.shared_rows = cap::kPrivateRows;
     if (o.num_cus == 0) o.num_cus = 256;
-    if (o.shared_cost == 0.f) o.shared_cost = 2.0f;
+    if (o.shared_cost == 0.f) o.shared_cost = 1.5f;
     if (o.rounds == 0.f) o.rounds = 1.5f;
     if (o.share_margin == 0.f) o.share_margin = 1.0f;
     if (o.order == 0) o.order = 2;
-    if (o.private_rounds == 0.f) o.private_rounds = 1.5f;
+    if (o.private_rounds == 0.f) o.private_rounds = 1.0f;
     if (o.tail_factor == 0.f) o.tail_factor = 1.0f;
     if (o.tail_min_pages == 0) o.tail_min_pages = 16;
 }
@@ -783,6 +783,14 @@ cap_status cap_bench_read(const void *buf, size_t bytes, void *sink, cap_stream_
     if (!buf || !sink || bytes == 0 || (bytes & 15) || ((uintptr_t)buf & 15))
         return fail(CAP_ERR_INVALID_ARG, "read: bad buffer or size");
     const int e = cap::launch_read(buf, bytes / 16, sink, stream);
+    return e ? fail(CAP_ERR_HIP, "read launch failed: %s", cap::hip_error_string(e)) : CAP_OK;
+}
+
+cap_status cap_bench_read_stream(const void *buf, size_t bytes, void *sink, cap_stream_t stream)
+{
+    if (!buf || !sink || bytes == 0 || (bytes & 15) || ((uintptr_t)buf & 15))
+        return fail(CAP_ERR_INVALID_ARG, "read: bad buffer or size");
+    const int e = cap::launch_read_stream(buf, bytes / 16, sink, stream);
     return e ? fail(CAP_ERR_HIP, "read launch failed: %s", cap::hip_error_string(e)) : CAP_OK;
 }
 

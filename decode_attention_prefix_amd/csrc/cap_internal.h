@@ -99,6 +99,7 @@ struct MergeArgs {
 int launch_decode(const DecodeArgs &a, int head_dim, void *stream);
 int launch_merge(const MergeArgs &a, int head_dim, void *stream);
 int launch_fill(void *buf, size_t words, uint32_t value, void *stream);
+int launch_read_stream(const void *buf, size_t vec16, void *sink, void *stream);
 int launch_read(const void *buf, size_t vec16, void *sink, void *stream);
 int launch_copy(void *dst, const void *src, size_t vec16, void *stream);
 const char *hip_error_string(int err);

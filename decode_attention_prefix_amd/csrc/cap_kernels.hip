@@ -1156,6 +1156,42 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4 *buf, size_t n, u
     }
 }
 
+// The achievable-read probe: each workgroup streams contiguous 256 KB runs
+// (the decode kernel's access shape), eight non-temporal 16-byte loads in
+// flight per lane -- the fastest of the read shapes measured on the device
+// (grid-stride, per-workgroup runs of 64 KB to 1 MB, 4 or 8 loads in flight,
+// plain or non-temporal).
+constexpr size_t kStreamRun = 16384;               // 16-byte vectors per run (256 KB)
+
+__global__ __launch_bounds__(256) void read_stream_kernel(const u32x4 *buf, size_t n, uint32_t *sink)
+{
+    constexpr int K = 8;
+    uint32_t x = 0;
+    for (size_t base = (size_t)blockIdx.x * kStreamRun; base < n; base += (size_t)gridDim.x * kStreamRun) {
+        const size_t end = base + kStreamRun < n ? base + kStreamRun : n;
+        size_t i = base + threadIdx.x;
+        for (; i + (K - 1) * 256 < end; i += K * 256) {
+            u32x4 v[K];
+#pragma unroll
+            for (int k = 0; k < K; ++k) v[k] = __builtin_nontemporal_load(&buf[i + k * 256]);
+#pragma unroll
+            for (int k = 0; k < K; ++k) x ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+        }
+        for (; i < end; i += 256) {
+            const u32x4 v = buf[i];
+            x ^= v.x ^ v.y ^ v.z ^ v.w;
+        }
+    }
+    __shared__ uint32_t red[256];
+    red[threadIdx.x] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t y = 0;
+        for (int k = 0; k < 256; ++k) y ^= red[k];
+        sink[blockIdx.x] = y;
+    }
+}
+
 __global__ __launch_bounds__(256) void copy_kernel(u32x4 *dst, const u32x4 *src, size_t n)
 {
     const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -1246,6 +1282,15 @@ int launch_read(const void *buf, size_t vec16, void *sink, void *stream)
     hipLaunchKernelGGL(read_kernel, dim3(grid_for(vec16)), dim3(256), 0,
                        reinterpret_cast<hipStream_t>(stream), (const u32x4 *)buf, vec16,
                        (uint32_t *)sink);
+    return (int)hipGetLastError();
+}
+
+int launch_read_stream(const void *buf, size_t vec16, void *sink, void *stream)
+{
+    size_t g = (vec16 + kStreamRun - 1) / kStreamRun;
+    g = g > 512 ? 512 : (g < 1 ? 1 : g);             // sink holds >= 8192 words
+    hipLaunchKernelGGL(read_stream_kernel, dim3((unsigned)g), dim3(256), 0,
+                       reinterpret_cast<hipStream_t>(stream), (const u32x4 *)buf, vec16, (uint32_t *)sink);
     return (int)hipGetLastError();
 }
 

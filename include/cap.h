@@ -118,7 +118,7 @@ typedef struct cap_plan_opts {
                                  to 16 rows, pages split over the 4 waves).  G > 16
                                  always uses shared items */
     int32_t num_cus;          /* 0 = 256 (MI355X); used by the cost model */
-    float shared_cost;        /* 0 = 2.0; cost of a shared item's page relative to a
+    float shared_cost;        /* 0 = 1.5; cost of a shared item's page relative to a
                                  private item's page, used to size items */
     float rounds;             /* 0 = 1.5; target work items per CU (two run at once) */
     float share_margin;       /* 0 = 1.0; share a node only if saved bytes exceed
@@ -130,7 +130,7 @@ typedef struct cap_plan_opts {
                                  shared items first, then private ones costliest first;
                                  4 = one shared and one private workgroup per CU first
                                  (num_cus of each kind), then as 1 */
-    float private_rounds;     /* 0 = 1.5; like `rounds`, but sizes the private items only
+    float private_rounds;     /* 0 = 1.0; like `rounds`, but sizes the private items only
                                  (splitting a private run adds one request's partial
                                  rows, splitting a shared one adds a whole group's) */
     float tail_factor;        /* 0 = 1.0; with order 2, cut private items so that none

@@ -25,10 +25,16 @@ extern "C" {
  * than L2 + the 256 MB Infinity Cache). */
 cap_status cap_bench_fill(void *buf, size_t bytes, uint32_t value, cap_stream_t stream);
 
-/* Read every byte of buf once (128-bit loads, grid-stride) and write one
- * 32-bit word per workgroup into sink (>= 4 x 8192 bytes) so the reads are not
- * dead.  Its time gives the achievable HBM read rate. */
+/* Read every byte of buf once (128-bit loads, grid-stride, cached) and write
+ * one 32-bit word per workgroup into sink (>= 4 x 8192 bytes) so the reads
+ * are not dead.  Used to evict L2 and the Infinity Cache before a timed step
+ * (reads allocate there; a fill would leave dirty lines behind). */
 cap_status cap_bench_read(const void *buf, size_t bytes, void *sink, cap_stream_t stream);
+
+/* The achievable-read probe: every byte of buf once, each workgroup streaming
+ * contiguous 256 KB runs with non-temporal 128-bit loads (the fastest read
+ * shape measured); sink as above.  bytes a multiple of 16. */
+cap_status cap_bench_read_stream(const void *buf, size_t bytes, void *sink, cap_stream_t stream);
 
 /* Plain copy of `bytes` from src to dst: reads and writes a known byte count,
  * for scaling FETCH_SIZE / WRITE_SIZE counters. */
