@@ -705,8 +705,13 @@ __device__ __forceinline__ void issue_dma(const DecodeArgs &a, const ItemRegs &i
         e0 = __builtin_amdgcn_readlane(lane_e, i0);
         e1 = __builtin_amdgcn_readlane(lane_e, i1);
     }
-    const int64_t p0 = e0 >> 5;
-    const int64_t p1 = e1 >> 5;
+    // byte offsets of the two pages' (page, head) blocks, computed once per
+    // step (the pieces below only pick one of four bases)
+    constexpr uint64_t kBlockBytes = (uint64_t)T::kBlock * 2;
+    const uint64_t o0 = ((uint64_t)(uint32_t)(e0 >> 5) * (uint32_t)a.Hkv + (uint32_t)head) * kBlockBytes;
+    const uint64_t o1 = ((uint64_t)(uint32_t)(e1 >> 5) * (uint32_t)a.Hkv + (uint32_t)head) * kBlockBytes;
+    const char *kp = reinterpret_cast<const char *>(a.k_pool), *vp = reinterpret_cast<const char *>(a.v_pool);
+    __builtin_assume(wave >= 0 && wave < kWaves);           // lets b fold to a constant when kPPB == kWaves
 #pragma unroll
     for (int k = 0; k < T::kPPB; ++k) {
         const int piece = wave + kWaves * k;                 // 0 .. 4 * kPPB - 1
@@ -717,9 +722,8 @@ __device__ __forceinline__ void issue_dma(const DecodeArgs &a, const ItemRegs &i
             const int d = c >> 1;
             src = 2 * d + ((c & 1) ^ ((d >> 2) & 1));
         }
-        const int64_t page = (b & 1) ? p1 : p0;
-        const uint16_t *pool = (b & 2) ? a.v_pool : a.k_pool;
-        const uint16_t *g = pool + (page * a.Hkv + head) * T::kBlock + src * 8;
+        const char *base = (b & 2) ? vp + ((b & 1) ? o1 : o0) : kp + ((b & 1) ? o1 : o0);
+        const char *g = base + src * 16;
         __builtin_amdgcn_global_load_lds(
             (const void __attribute__((address_space(1))) *)g,
             (void __attribute__((address_space(3))) *)(slot + b * T::kBlock + (piece % T::kPPB) * kWaveSize * 8),
