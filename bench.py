@@ -65,6 +65,77 @@ def cpu_model() -> str:
     return platform.processor()
 
 
+def measure_growth(dec, tree, extra_pages, steps, args, evict, stream):
+    """Decode steps on a growing tree: before each step, every request gains
+    one token (cap_tree_append on the host, cap_append_kv on the GPU) and the
+    plan follows (cap_plan_refresh, or a new plan when it must).  Times each
+    part apart; the step itself as in the main timing (cache flushed)."""
+    import numpy as np
+    import torch
+
+    from decode_attention_prefix_amd import cap
+    R, Hkv, D = tree.num_requests, tree.num_kv_heads, tree.head_dim
+    dev = dec.device
+    first_free = int(tree.num_pool_pages) - extra_pages
+    free = list(range(first_free, int(tree.num_pool_pages)))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+    k_new = torch.randn((R, Hkv, D), generator=gen, device=dev).to(torch.bfloat16)
+    v_new = torch.randn((R, Hkv, D), generator=gen, device=dev).to(torch.bfloat16)
+    sp = stream.cuda_stream
+    rec = {"append_host_us": [], "refresh_host_us": [], "append_kv_us": [], "plan_update_us": [],
+           "step_us": []}
+    counts = {"patch": 0, "whole": 0, "replan": 0}
+    words = []
+    for _ in range(steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        cand = np.asarray(free[:R], np.int32)
+        t0 = time.perf_counter()
+        dest = cap.cap_tree_append(dec.tree, R, None, cand)
+        rec["append_host_us"].append((time.perf_counter() - t0) * 1e6)
+        taken = set((dest[(dest >= 0) & ((dest & 15) == 0)] >> 4).tolist())
+        free = [p for p in free if p not in taken]
+        d = torch.from_numpy(dest).to(dev)
+        ev[0].record(stream)
+        cap.cap_append_kv(dec.tree, d.data_ptr(), R, k_new.data_ptr(), v_new.data_ptr(), dec.k.data_ptr(),
+                          dec.v.data_ptr(), sp)
+        ev[1].record(stream)
+        before = dec.stats["refreshes"]
+        try:
+            cap.cap_plan_refresh(dec.plan_h, sp)
+            st = cap.cap_plan_get_stats(dec.plan_h)
+            if st["refreshes"] > before:
+                counts["whole" if st["refresh_full_copy"] else "patch"] += 1
+                rec["refresh_host_us"].append(st["refresh_host_us"])
+                words.append(st["refresh_words"])
+            dec.stats = st
+        except cap.CapError as e:
+            if e.status != cap.CAP_ERR_REPLAN:
+                raise
+            dec.plan(**dec.plan_opts)
+            counts["replan"] += 1
+        ev[2].record(stream)
+        if args.flush_mb > 0:
+            evict()
+        ev[3].record(stream)
+        if args.fused:
+            dec.fused_step()
+        else:
+            dec.decode()
+            dec.merge()
+        ev[4].record(stream)
+        torch.cuda.synchronize(dev)
+        rec["append_kv_us"].append(ev[0].elapsed_time(ev[1]) * 1e3)
+        rec["plan_update_us"].append(ev[1].elapsed_time(ev[2]) * 1e3)
+        rec["step_us"].append(ev[3].elapsed_time(ev[4]) * 1e3)
+    med = {k: (round(statistics.median(v), 2) if v else None) for k, v in rec.items()}
+    return {"steps": steps, "tokens_per_step": R, **{k + "_median": v for k, v in med.items()},
+            "refresh_words_median": (statistics.median(words) if words else None),
+            "plan_updates": counts,
+            "note": "plan_update_us: stream time from the end of the K/V write to the end of the plan "
+                    "update (its host work included while the stream waits on it)"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -88,6 +159,9 @@ def main():
                          "cap_merge_partials")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--read-probe-mb", type=int, default=2048)
+    ap.add_argument("--growth-steps", type=int, default=16,
+                    help="after the timed steps: decode steps that first grow the tree by one token "
+                         "per request (host append, K/V write, plan refresh), timed apart (0 = none)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run one plain copy of this size (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -112,7 +186,11 @@ def main():
     torch.cuda.set_device(dev)
 
     t_gen = time.perf_counter()
-    w = wl.make_config(args.config, seed=args.seed, tail_fill="zero", keep_tokens=args.control)
+    growth = args.growth_steps if not args.control else 0
+    R_cfg = {0: 4, 1: 64, 2: 128, 3: 32, 4: 256}[args.config]
+    extra_pages = R_cfg * (growth // 16 + 3) if growth else 0
+    w = wl.make_config(args.config, seed=args.seed, tail_fill="zero", keep_tokens=args.control,
+                       extra_pool_pages=extra_pages)
     if args.control:
         w = wl.control_workload(w, tail_fill="zero")
     st_tree = wl.tree_stats(w.tree)
@@ -301,6 +379,8 @@ def main():
                       f"{t_or:.3f} s each",
             "cpu": cpu_model(),
         }
+    if growth:
+        result["growth"] = measure_growth(dec, w.tree, extra_pages, growth, args, evict, stream)
     if args.copy_probe_mb > 0:
         nb = args.copy_probe_mb << 20
         src = torch.empty(nb, dtype=torch.uint8, device=dev)

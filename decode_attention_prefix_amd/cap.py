@@ -19,14 +19,16 @@ LIB_PATH = os.path.join(_PKG, "libcap.so")
 CAP_OK = 0
 STATUS_NAMES = {0: "CAP_OK", 1: "CAP_ERR_INVALID_ARG", 2: "CAP_ERR_BAD_TREE",
                 3: "CAP_ERR_WORKSPACE", 4: "CAP_ERR_UNSUPPORTED", 5: "CAP_ERR_HIP",
-                6: "CAP_ERR_STATE"}
+                6: "CAP_ERR_STATE", 7: "CAP_ERR_REPLAN"}
+(CAP_ERR_INVALID_ARG, CAP_ERR_BAD_TREE, CAP_ERR_WORKSPACE, CAP_ERR_UNSUPPORTED, CAP_ERR_HIP,
+ CAP_ERR_STATE, CAP_ERR_REPLAN) = range(1, 8)
 
 EXPORTED = [
     "cap_abi_version", "cap_last_error", "cap_plan_opts_default", "cap_tree_device_bytes",
     "cap_tree_upload", "cap_tree_free", "cap_plan_step", "cap_plan_get_stats",
     "cap_plan_get_view", "cap_plan_upload", "cap_decode_attention", "cap_merge_partials",
-    "cap_decode_step", "cap_plan_free", "cap_bench_fill", "cap_bench_read", "cap_bench_read_stream",
-    "cap_bench_copy",
+    "cap_decode_step", "cap_plan_free", "cap_tree_get_desc", "cap_tree_append", "cap_append_kv",
+    "cap_plan_refresh", "cap_bench_fill", "cap_bench_read", "cap_bench_read_stream", "cap_bench_copy",
 ]
 
 
@@ -56,7 +58,8 @@ class PlanOpts(ctypes.Structure):
                 ("shared_cost", ctypes.c_float), ("rounds", ctypes.c_float),
                 ("share_margin", ctypes.c_float), ("order", ctypes.c_int32),
                 ("private_rounds", ctypes.c_float), ("tail_factor", ctypes.c_float),
-                ("tail_min_pages", ctypes.c_int32), ("item_dispatch", ctypes.c_int32)]
+                ("tail_min_pages", ctypes.c_int32), ("item_dispatch", ctypes.c_int32),
+                ("append_slack", ctypes.c_int32)]
 
 
 class PlanStats(ctypes.Structure):
@@ -65,7 +68,9 @@ class PlanStats(ctypes.Structure):
         "plan_device_bytes", "tree_device_bytes", "kv_bytes_streamed", "kv_bytes_unique",
         "kv_bytes_unshared", "partial_bytes")] + [
         ("max_partials_per_request", ctypes.c_int32), ("max_pages_per_item", ctypes.c_int32),
-        ("plan_host_us", ctypes.c_double)]
+        ("plan_host_us", ctypes.c_double), ("refresh_host_us", ctypes.c_double),
+        ("refresh_words", ctypes.c_int64), ("refresh_full_copy", ctypes.c_int32),
+        ("refreshes", ctypes.c_int32)]
 
 
 class WorkItemC(ctypes.Structure):
@@ -112,13 +117,18 @@ def lib():
         L.cap_decode_step.argtypes = [vp, vp, vp, vp, vp, sz, vp, vp]
         L.cap_plan_free.argtypes = [vp]
         L.cap_plan_free.restype = None
+        L.cap_tree_get_desc.argtypes = [vp, ctypes.POINTER(TreeDesc)]
+        L.cap_tree_append.argtypes = [vp, vp, vp, vp]
+        L.cap_append_kv.argtypes = [vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp]
+        L.cap_plan_refresh.argtypes = [vp, vp]
         L.cap_bench_fill.argtypes = [vp, sz, ctypes.c_uint32, vp]
         L.cap_bench_read.argtypes = [vp, sz, vp, vp]
         L.cap_bench_read_stream.argtypes = [vp, sz, vp, vp]
         L.cap_bench_copy.argtypes = [vp, vp, sz, vp]
         for name in ("cap_tree_device_bytes", "cap_tree_upload", "cap_plan_step",
                      "cap_plan_get_stats", "cap_plan_get_view", "cap_plan_upload",
-                     "cap_decode_attention", "cap_merge_partials", "cap_decode_step", "cap_bench_fill",
+                     "cap_decode_attention", "cap_merge_partials", "cap_decode_step", "cap_tree_get_desc",
+                     "cap_tree_append", "cap_append_kv", "cap_plan_refresh", "cap_bench_fill",
                      "cap_bench_read", "cap_bench_read_stream", "cap_bench_copy"):
             getattr(L, name).restype = st
         _lib = L
@@ -178,6 +188,55 @@ def cap_tree_upload(tree, dev_buf: int = 0, dev_bytes: int = 0, stream: int = 0)
 def cap_tree_free(handle: int) -> None:
     if handle:
         lib().cap_tree_free(ctypes.c_void_p(handle))
+
+
+def cap_tree_get_desc(handle: int) -> dict:
+    """Copies of the tree's host arrays as they stand (after any appends)."""
+    d = TreeDesc()
+    _check(lib().cap_tree_get_desc(ctypes.c_void_p(handle), ctypes.byref(d)))
+
+    def arr(ptr, n, ctype, dtype):
+        if n == 0:
+            return np.zeros((0,), dtype)
+        return np.ctypeslib.as_array(ctypes.cast(ptr, ctypes.POINTER(ctype)), (n,)).copy()
+
+    N, R = int(d.num_nodes), int(d.num_requests)
+    page_offsets = arr(d.page_offsets, N + 1, ctypes.c_int64, np.int64)
+    path_offsets = arr(d.path_offsets, R + 1, ctypes.c_int32, np.int32)
+    return {"parent": arr(d.parent, N, ctypes.c_int32, np.int32),
+            "num_tokens": arr(d.num_tokens, N, ctypes.c_int32, np.int32),
+            "page_offsets": page_offsets,
+            "page_ids": arr(d.page_ids, int(page_offsets[-1]), ctypes.c_int32, np.int32),
+            "path_offsets": path_offsets,
+            "path_nodes": arr(d.path_nodes, int(path_offsets[-1]), ctypes.c_int32, np.int32),
+            "num_pool_pages": int(d.num_pool_pages)}
+
+
+def cap_tree_append(handle: int, num_requests: int, active=None, new_pages=None) -> np.ndarray:
+    """One token for each active request; returns dest [R] ((page << 4) | slot, -1 inactive)."""
+    dest = np.zeros(num_requests, np.int32)
+    act = None if active is None else np.ascontiguousarray(active, dtype=np.uint8)
+    pages = None if new_pages is None else np.ascontiguousarray(new_pages, dtype=np.int32)
+    for a in (act, pages):
+        if a is not None and a.shape != (num_requests,):
+            raise ValueError("active and new_pages need one entry per request")
+    _check(lib().cap_tree_append(ctypes.c_void_p(handle),
+                                 None if act is None else ctypes.c_void_p(act.ctypes.data),
+                                 None if pages is None else ctypes.c_void_p(pages.ctypes.data),
+                                 ctypes.c_void_p(dest.ctypes.data)))
+    return dest
+
+
+def cap_append_kv(tree_handle: int, dest: int, n: int, k_new: int, v_new: int, k_pool: int,
+                  v_pool: int, stream: int = 0) -> None:
+    _check(lib().cap_append_kv(ctypes.c_void_p(tree_handle), ctypes.c_void_p(dest), n,
+                               ctypes.c_void_p(k_new), ctypes.c_void_p(v_new), ctypes.c_void_p(k_pool),
+                               ctypes.c_void_p(v_pool), ctypes.c_void_p(stream or None)))
+
+
+def cap_plan_refresh(plan: int, stream: int = 0) -> None:
+    """Raises CapError with status CAP_ERR_REPLAN when a new plan is needed."""
+    _check(lib().cap_plan_refresh(ctypes.c_void_p(plan), ctypes.c_void_p(stream or None)))
 
 
 def make_opts(**kw) -> PlanOpts:

@@ -22,6 +22,7 @@
 #include <algorithm>
 #include <chrono>
 #include <cmath>
+#include <cstddef>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -70,7 +71,10 @@ struct cap_tree {
     std::vector<int32_t> end_off, end_list;   // requests whose path ends at node
     std::vector<int64_t> ctx_len;
     int64_t unique_tokens = 0, sum_ctx = 0;
-    const int32_t *dev_pages = nullptr;       // device copy of page_ids (may be null)
+    const int32_t *dev_pages = nullptr;       // device copy of page_ids as uploaded (may be null)
+    // mutation state
+    int64_t shape_gen = 0;                    // bumped when nodes or request paths change
+    std::vector<uint64_t> owned;              // bitmap of pool pages held by a node (built on first append)
 };
 
 struct cap_plan {
@@ -87,6 +91,20 @@ struct cap_plan {
     bool work_queue = false;          // item_dispatch 1
     std::vector<unsigned char> host_image;
     void *dev = nullptr;
+    // growth in place (cap_plan_refresh): per request, the leaf run that
+    // ends with the pages of the node its context ends at
+    struct Leaf {
+        int32_t node = -1;            // -1: no run the plan can extend
+        int32_t pages = 0;            // the node's pages as the plan holds them
+        int32_t end = 0;              // stream index one past the run's last entry
+        int32_t limit = 0;            // one past the free entries reserved after it
+        int32_t item0 = 0;            // first of the Hkv items whose page run ends at `end`
+    };
+    std::vector<Leaf> leaf;
+    std::vector<int32_t> node_tokens; // the tree's token counts the plan holds
+    int64_t shape_gen = 0;
+    size_t off_patch = 0, patch_cap = 0;   // patch area: patch_cap (word, value) pairs
+    std::vector<uint32_t> patch;
 };
 
 namespace {
@@ -110,6 +128,39 @@ cap_status check_attn(const cap_attn_desc *a)
     if (!(a->sm_scale > 0.f) || !std::isfinite(a->sm_scale))
         return fail(CAP_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
     return CAP_OK;
+}
+
+// Tables derived from parent, ntok and the request paths: children,
+// node -> requests (passing through / ending at), context lengths and totals.
+void derive(cap_tree &t)
+{
+    const int N = t.N, R = t.R;
+    t.children.assign(N, {});
+    for (int i = 0; i < N; ++i)
+        if (t.parent[i] >= 0) t.children[t.parent[i]].push_back(i);
+    std::vector<std::vector<int32_t>> under(N), ends(N);
+    t.ctx_len.assign(R, 0);
+    for (int r = 0; r < R; ++r) {
+        for (int j = t.path_off[r]; j < t.path_off[r + 1]; ++j) {
+            under[t.path_nodes[j]].push_back(r);
+            t.ctx_len[r] += t.ntok[t.path_nodes[j]];
+        }
+        ends[t.path_nodes[t.path_off[r + 1] - 1]].push_back(r);
+    }
+    t.req_off.assign(N + 1, 0);
+    t.end_off.assign(N + 1, 0);
+    t.req_list.clear();
+    t.end_list.clear();
+    t.unique_tokens = 0;
+    t.sum_ctx = 0;
+    for (int i = 0; i < N; ++i) {
+        t.req_off[i + 1] = t.req_off[i] + (int32_t)under[i].size();
+        t.end_off[i + 1] = t.end_off[i] + (int32_t)ends[i].size();
+        t.req_list.insert(t.req_list.end(), under[i].begin(), under[i].end());
+        t.end_list.insert(t.end_list.end(), ends[i].begin(), ends[i].end());
+        t.unique_tokens += t.ntok[i];
+    }
+    for (int r = 0; r < R; ++r) t.sum_ctx += t.ctx_len[r];
 }
 
 // Validate and copy the description into a new tree object (host only).
@@ -186,34 +237,48 @@ cap_status build_tree(const cap_attn_desc *attn, const cap_tree_desc *d, cap_tre
     t->path_off.assign(d->path_offsets, d->path_offsets + R + 1);
     t->path_nodes.assign(d->path_nodes + 0, d->path_nodes + d->path_offsets[R]);
     t->num_pool_pages = d->num_pool_pages;
-    t->ctx_len = ctx;
-    t->children.assign(N, {});
-    for (int i = 0; i < N; ++i)
-        if (t->parent[i] >= 0) t->children[t->parent[i]].push_back(i);
-    std::vector<std::vector<int32_t>> under(N), ends(N);
-    for (int r = 0; r < R; ++r) {
-        for (int j = t->path_off[r]; j < t->path_off[r + 1]; ++j) under[t->path_nodes[j]].push_back(r);
-        ends[t->path_nodes[t->path_off[r + 1] - 1]].push_back(r);
-    }
-    t->req_off.assign(N + 1, 0);
-    t->end_off.assign(N + 1, 0);
-    for (int i = 0; i < N; ++i) {
-        t->req_off[i + 1] = t->req_off[i] + (int32_t)under[i].size();
-        t->end_off[i + 1] = t->end_off[i] + (int32_t)ends[i].size();
-        t->req_list.insert(t->req_list.end(), under[i].begin(), under[i].end());
-        t->end_list.insert(t->end_list.end(), ends[i].begin(), ends[i].end());
-        t->unique_tokens += t->ntok[i];
-    }
-    for (int r = 0; r < R; ++r) t->sum_ctx += ctx[r];
+    derive(*t);
     *out = t;
     return CAP_OK;
 }
 
 // ------------------------------------------------------------------ planner
 
+// Device form of a work item: the item, its requests' first id when they are
+// consecutive, and the stream entries of its first pages, split over the
+// waves as the decode kernel splits a private item's steps.
+cap::DevItem dev_item(const cap_plan &p, const WorkItem &w)
+{
+    cap::DevItem d{};
+    d.stream_off = w.stream_off;
+    d.npages = w.npages;
+    d.head = w.head;
+    d.row_off = w.row_off;
+    d.nreq = w.nreq;
+    d.slot_base = w.slot_base;
+    d.mode = w.mode;
+    bool consecutive = true;
+    for (int q = 1; q < w.nreq; ++q) consecutive &= p.rows[w.row_off + q] == p.rows[w.row_off] + q;
+    d.req0 = consecutive ? p.rows[w.row_off] : -1;
+    const int32_t *e = p.stream.data() + w.stream_off;
+    if (w.mode == cap::kModeShared) {
+        for (int j = 0; j < cap::kInlineEntries && j < w.npages; ++j) d.ent[j] = e[j];
+    } else {
+        const int nsteps = (w.npages + 1) >> 1;
+        for (int wv = 0; wv < cap::kWaves; ++wv) {
+            const int first = 2 * (nsteps * wv / cap::kWaves);
+            const int count = std::min(w.npages, 2 * (nsteps * (wv + 1) / cap::kWaves)) - first;
+            for (int j = 0; j < cap::kInlinePerWave && j < count; ++j)
+                d.ent[cap::kInlinePerWave * wv + j] = e[first + j];
+        }
+    }
+    return d;
+}
+
 struct Group {
     std::vector<int32_t> reqs;     // sorted request ids
     std::vector<int32_t> entries;  // page-stream entries
+    int32_t at = -1;               // node whose pages end the entries (the walk emitted it there)
 };
 
 struct Planner {
@@ -294,12 +359,13 @@ struct Planner {
         return (double)saved > (double)o.share_margin * (double)added;
     }
 
-    void emit(const int32_t *reqs, int nreq, const std::vector<int32_t> &entries)
+    void emit(const int32_t *reqs, int nreq, const std::vector<int32_t> &entries, int at)
     {
         if (entries.empty() || nreq == 0) return;
         Group g;
         g.reqs.assign(reqs, reqs + nreq);
         g.entries = entries;
+        g.at = at;
         groups.push_back(std::move(g));
     }
 
@@ -309,10 +375,10 @@ struct Planner {
         node_entries(n, entries);
         const int64_t tok = prefix_tokens + t.ntok[n];
         if (decide_share(n, prefix_tokens)) {
-            emit(&t.req_list[t.req_off[n]], t.req_off[n + 1] - t.req_off[n], entries);
+            emit(&t.req_list[t.req_off[n]], t.req_off[n + 1] - t.req_off[n], entries, n);
             for (int c : t.children[n]) walk(c, {}, 0);
         } else {
-            emit(t.end_list.data() + t.end_off[n], t.end_off[n + 1] - t.end_off[n], entries);
+            emit(t.end_list.data() + t.end_off[n], t.end_off[n + 1] - t.end_off[n], entries, n);
             for (int c : t.children[n]) walk(c, entries, tok);
         }
     }
@@ -350,6 +416,7 @@ void fill_defaults(cap_plan_opts &o)
     if (o.private_rounds == 0.f) o.private_rounds = 1.0f;
     if (o.tail_factor == 0.f) o.tail_factor = 1.0f;
     if (o.tail_min_pages == 0) o.tail_min_pages = 16;
+    if (o.append_slack == 0) o.append_slack = 8;
 }
 
 }  // namespace
@@ -411,6 +478,136 @@ cap_status cap_tree_upload(const cap_attn_desc *attn, const cap_tree_desc *desc,
 
 void cap_tree_free(cap_tree *tree) { delete tree; }
 
+cap_status cap_tree_get_desc(const cap_tree *t, cap_tree_desc *d)
+{
+    if (!t || !d) return fail(CAP_ERR_INVALID_ARG, "NULL argument");
+    d->num_nodes = t->N;
+    d->parent = t->parent.data();
+    d->num_tokens = t->ntok.data();
+    d->page_offsets = t->page_off.data();
+    d->page_ids = t->page_ids.data();
+    d->num_requests = t->R;
+    d->path_offsets = t->path_off.data();
+    d->path_nodes = t->path_nodes.data();
+    d->num_pool_pages = t->num_pool_pages;
+    return CAP_OK;
+}
+
+// One decode step's token for each active request.  A request whose path
+// ends at a leaf that no other request passes through extends that leaf
+// (into the free slot of its last page, or a new page when the last page is
+// full or the leaf has none); any other request gets a new one-token child
+// under its end node (a radix-tree branch: the end node stays shared).
+cap_status cap_tree_append(cap_tree *t, const uint8_t *active, const int32_t *new_pages, int32_t *dest)
+{
+    if (!t || !dest) return fail(CAP_ERR_INVALID_ARG, "NULL argument");
+    const int R = t->R;
+    if (t->owned.empty()) {
+        t->owned.assign((size_t)(t->num_pool_pages + 63) / 64, 0);
+        for (int32_t pg : t->page_ids) t->owned[pg >> 6] |= uint64_t(1) << (pg & 63);
+    }
+    enum { kSkip, kSlot, kPage, kBranch };
+    std::vector<uint8_t> kind(R, kSkip);
+    std::vector<int32_t> taken;
+    int32_t branches = 0;
+    for (int r = 0; r < R; ++r) {
+        if (active && !active[r]) continue;
+        const int n = t->path_nodes[t->path_off[r + 1] - 1];
+        const bool exclusive = t->children[n].empty() && t->req_off[n + 1] - t->req_off[n] == 1;
+        if (exclusive && t->ntok[n] == std::numeric_limits<int32_t>::max())
+            return fail(CAP_ERR_UNSUPPORTED, "request %d: node %d holds 2^31 - 1 tokens", r, n);
+        kind[r] = !exclusive ? kBranch : (t->ntok[n] % cap::kPage ? kSlot : kPage);
+        if (kind[r] == kSlot) continue;
+        if (!new_pages) return fail(CAP_ERR_INVALID_ARG, "request %d needs a new page but new_pages is NULL", r);
+        const int32_t pg = new_pages[r];
+        if (pg < 0 || pg >= t->num_pool_pages)
+            return fail(CAP_ERR_BAD_TREE, "new_pages[%d] = %d outside the pool of %lld pages", r, pg,
+                        (long long)t->num_pool_pages);
+        if (t->owned[pg >> 6] >> (pg & 63) & 1)
+            return fail(CAP_ERR_BAD_TREE, "new_pages[%d] = %d is already owned by a node", r, pg);
+        taken.push_back(pg);
+        branches += kind[r] == kBranch;
+    }
+    std::vector<int32_t> sorted = taken;
+    std::sort(sorted.begin(), sorted.end());
+    for (size_t i = 1; i < sorted.size(); ++i)
+        if (sorted[i] == sorted[i - 1])
+            return fail(CAP_ERR_BAD_TREE, "new page %d is given to two requests", sorted[i]);
+    if ((int64_t)t->page_ids.size() + (int64_t)taken.size() >= (int64_t(1) << 26))
+        return fail(CAP_ERR_UNSUPPORTED, "tree would hold 2^26 pages or more");
+    if ((int64_t)t->N + branches > std::numeric_limits<int32_t>::max() / 2)
+        return fail(CAP_ERR_UNSUPPORTED, "tree would hold too many nodes");
+
+    // apply: token counts, then one rebuild of the page lists (and of the
+    // paths and derived tables when a branch was made)
+    const int N0 = t->N;
+    std::vector<std::vector<int32_t>> extra(N0);   // pages appended to existing nodes
+    std::vector<int32_t> new_parent, new_page, new_req;
+    for (int r = 0; r < R; ++r) {
+        if (kind[r] == kSkip) {
+            dest[r] = -1;
+            continue;
+        }
+        const int n = t->path_nodes[t->path_off[r + 1] - 1];
+        if (kind[r] == kBranch) {
+            new_parent.push_back(n);
+            new_page.push_back(new_pages[r]);
+            new_req.push_back(r);
+            dest[r] = new_pages[r] << 4;
+            continue;
+        }
+        const int32_t slot = t->ntok[n] % cap::kPage;
+        int32_t pg;
+        if (kind[r] == kSlot) {
+            pg = t->page_ids[t->page_off[n] + t->ntok[n] / cap::kPage];
+        } else {
+            pg = new_pages[r];
+            extra[n].push_back(pg);
+        }
+        ++t->ntok[n];
+        ++t->ctx_len[r];
+        ++t->sum_ctx;
+        ++t->unique_tokens;
+        dest[r] = pg << 4 | slot;
+    }
+    for (int32_t pg : taken) t->owned[pg >> 6] |= uint64_t(1) << (pg & 63);
+    if (taken.empty()) return CAP_OK;
+    std::vector<int64_t> off(N0 + new_parent.size() + 1, 0);
+    std::vector<int32_t> ids;
+    ids.reserve(t->page_ids.size() + taken.size());
+    for (int n = 0; n < N0; ++n) {
+        ids.insert(ids.end(), t->page_ids.begin() + t->page_off[n], t->page_ids.begin() + t->page_off[n + 1]);
+        ids.insert(ids.end(), extra[n].begin(), extra[n].end());
+        off[n + 1] = (int64_t)ids.size();
+    }
+    for (size_t b = 0; b < new_parent.size(); ++b) {
+        ids.push_back(new_page[b]);
+        off[N0 + b + 1] = (int64_t)ids.size();
+    }
+    t->page_ids.swap(ids);
+    t->page_off.swap(off);
+    if (new_parent.empty()) return CAP_OK;
+    std::vector<int32_t> poff(R + 1, 0), pnodes;
+    pnodes.reserve(t->path_nodes.size() + new_parent.size());
+    size_t b = 0;
+    for (int r = 0; r < R; ++r) {
+        pnodes.insert(pnodes.end(), t->path_nodes.begin() + t->path_off[r],
+                      t->path_nodes.begin() + t->path_off[r + 1]);
+        if (b < new_req.size() && new_req[b] == r) pnodes.push_back(N0 + (int32_t)b++);
+        poff[r + 1] = (int32_t)pnodes.size();
+    }
+    t->path_off.swap(poff);
+    t->path_nodes.swap(pnodes);
+    for (size_t i = 0; i < new_parent.size(); ++i) {
+        t->parent.push_back(new_parent[i]);
+        t->ntok.push_back(1);
+    }
+    t->N = N0 + (int32_t)new_parent.size();
+    derive(*t);
+    ++t->shape_gen;
+    return CAP_OK;
+}
+
 cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap_plan **out)
 {
     if (!tree || !out) return fail(CAP_ERR_INVALID_ARG, "NULL argument");
@@ -428,6 +625,9 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
         return fail(CAP_ERR_INVALID_ARG, "negative planner option");
     if (o.item_dispatch < 0 || o.item_dispatch > 1)
         return fail(CAP_ERR_INVALID_ARG, "item_dispatch %d not in {0, 1}", o.item_dispatch);
+    if (o.append_slack < -1 || o.append_slack > 4096)
+        return fail(CAP_ERR_INVALID_ARG, "append_slack %d not in [-1, 4096]", o.append_slack);
+    if (o.append_slack == -1) o.append_slack = 0;
     if (o.order < 1 || o.order > 4) return fail(CAP_ERR_INVALID_ARG, "order %d not in {0, .., 4}", o.order);
 
     cap_plan *p = new (std::nothrow) cap_plan();
@@ -440,9 +640,12 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
 
     // tasks: (page run, request subgroup); balanced splits of both.  Partial
     // slots are assigned once the dispatch sequence is fixed.
-    struct Task { int32_t so, np, ro, nr, sb; bool shared; double cost; int32_t idx; };
+    struct Task { int32_t so, np, ro, nr, sb; bool shared; double cost; int32_t idx, grp; };
     std::vector<Task> tasks;
-    for (const Group &g : pl.groups) {
+    p->leaf.assign(tree->R, cap_plan::Leaf{});
+    std::vector<int32_t> grp_leaf(pl.groups.size(), -1);   // request whose leaf run the group is
+    for (size_t gi = 0; gi < pl.groups.size(); ++gi) {
+        const Group &g = pl.groups[gi];
         const int64_t npg = (int64_t)g.entries.size();
         const int nreq = (int)g.reqs.size();
         const bool shared = pl.is_shared(nreq);
@@ -450,6 +653,22 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
         const int rg = (nreq + pl.reqs_per_item(nreq) - 1) / pl.reqs_per_item(nreq);
         const int32_t so0 = (int32_t)p->stream.size();
         p->stream.insert(p->stream.end(), g.entries.begin(), g.entries.end());
+        // a run serving one request, ending with the pages of the leaf where
+        // that request's context ends and no other request's path passes,
+        // can take the leaf's new pages in place: free entries follow it
+        if (nreq == 1) {
+            const int r = g.reqs[0], n = g.at;
+            if (tree->path_nodes[tree->path_off[r + 1] - 1] == n && tree->children[n].empty() &&
+                tree->req_off[n + 1] - tree->req_off[n] == 1) {
+                cap_plan::Leaf &lf = p->leaf[r];
+                lf.node = n;
+                lf.pages = (int32_t)(tree->page_off[n + 1] - tree->page_off[n]);
+                lf.end = (int32_t)p->stream.size();
+                lf.limit = lf.end + o.append_slack;
+                p->stream.insert(p->stream.end(), (size_t)o.append_slack, 0);
+                grp_leaf[gi] = r;
+            }
+        }
         const int32_t ro0 = (int32_t)p->rows.size();
         p->rows.insert(p->rows.end(), g.reqs.begin(), g.reqs.end());
         for (int64_t ci = 0; ci < k; ++ci) {
@@ -457,7 +676,8 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
             for (int ri = 0; ri < rg; ++ri) {
                 const int rb = (int)((int64_t)nreq * ri / rg), re = (int)((int64_t)nreq * (ri + 1) / rg);
                 tasks.push_back(Task{(int32_t)(so0 + pb), (int32_t)(pe - pb), ro0 + rb, re - rb, -1, shared,
-                                     (double)(pe - pb) * pl.page_cost(shared), (int32_t)tasks.size()});
+                                     (double)(pe - pb) * pl.page_cost(shared), (int32_t)tasks.size(),
+                                     (int32_t)gi});
             }
         }
     }
@@ -551,45 +771,22 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
         pl.max_pages = std::max<int>(pl.max_pages, tk.np);
     }
     p->items.reserve(seq.size() * Hkv);
-    for (const Task &tk : seq)
+    for (const Task &tk : seq) {
+        const int32_t r = grp_leaf[tk.grp];
+        if (r >= 0 && tk.so + tk.np == p->leaf[r].end) p->leaf[r].item0 = (int32_t)p->items.size();
         for (int h = 0; h < Hkv; ++h)
             p->items.push_back(WorkItem{tk.so, tk.np, h, tk.ro, tk.nr, tk.sb,
                                         tk.shared ? cap::kModeShared : cap::kModePrivate, 0});
+    }
+    p->node_tokens = tree->ntok;
+    p->shape_gen = tree->shape_gen;
 
     // device image: items | stream | rows | slot_rows | merge_off | counters |
-    // queue (the fused step's arrival counters, one per request and KV head,
-    // and the work queue's two counters, all zero)
-    // device items: each item plus its requests' first id when they are
-    // consecutive and the stream entries of its first pages, split over the
-    // waves as the decode kernel splits a private item's steps
+    // queue | patch (the fused step's arrival counters, one per request and
+    // KV head, and the work queues' counters, all zero; then the area that
+    // cap_plan_refresh stages its word patches in)
     std::vector<cap::DevItem> dev_items(p->items.size());
-    for (size_t i = 0; i < p->items.size(); ++i) {
-        const WorkItem &w = p->items[i];
-        cap::DevItem &d = dev_items[i];
-        d = cap::DevItem{};
-        d.stream_off = w.stream_off;
-        d.npages = w.npages;
-        d.head = w.head;
-        d.row_off = w.row_off;
-        d.nreq = w.nreq;
-        d.slot_base = w.slot_base;
-        d.mode = w.mode;
-        bool consecutive = true;
-        for (int q = 1; q < w.nreq; ++q) consecutive &= p->rows[w.row_off + q] == p->rows[w.row_off] + q;
-        d.req0 = consecutive ? p->rows[w.row_off] : -1;
-        const int32_t *e = p->stream.data() + w.stream_off;
-        if (w.mode == cap::kModeShared) {
-            for (int j = 0; j < cap::kInlineEntries && j < w.npages; ++j) d.ent[j] = e[j];
-        } else {
-            const int nsteps = (w.npages + 1) >> 1;
-            for (int wv = 0; wv < cap::kWaves; ++wv) {
-                const int first = 2 * (nsteps * wv / cap::kWaves);
-                const int count = std::min(w.npages, 2 * (nsteps * (wv + 1) / cap::kWaves)) - first;
-                for (int j = 0; j < cap::kInlinePerWave && j < count; ++j)
-                    d.ent[cap::kInlinePerWave * wv + j] = e[first + j];
-            }
-        }
-    }
+    for (size_t i = 0; i < p->items.size(); ++i) dev_items[i] = dev_item(*p, p->items[i]);
     p->off_items = 0;
     p->off_stream = align_up(dev_items.size() * sizeof(cap::DevItem));
     p->off_rows = p->off_stream + align_up(p->stream.size() * 4);
@@ -597,7 +794,9 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
     p->off_moff = p->off_srows + align_up(p->slot_rows.size() * 4);
     p->off_cnt = p->off_moff + align_up(p->merge_off.size() * 4);
     p->off_queue = p->off_cnt + align_up((size_t)tree->R * Hkv * 4);
-    p->dev_bytes = p->off_queue + align_up(cap::kQueueInts * 4);
+    p->off_patch = p->off_queue + align_up(cap::kQueueInts * 4);
+    p->patch_cap = (size_t)4 * tree->R * (Hkv + 1) + 256;
+    p->dev_bytes = p->off_patch + align_up(p->patch_cap * 8);
     p->host_image.assign(p->dev_bytes, 0);
     std::memcpy(p->host_image.data() + p->off_items, dev_items.data(), dev_items.size() * sizeof(cap::DevItem));
     std::memcpy(p->host_image.data() + p->off_stream, p->stream.data(), p->stream.size() * 4);
@@ -663,6 +862,135 @@ cap_status cap_plan_upload(cap_plan *plan, void *dev_buf, size_t bytes, cap_stre
                                   hipMemcpyHostToDevice, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(CAP_ERR_HIP, "plan upload copy failed: %s", hipGetErrorString(e));
     plan->dev = dev_buf;
+    return CAP_OK;
+}
+
+cap_status cap_plan_refresh(cap_plan *p, cap_stream_t stream)
+{
+    if (!p) return fail(CAP_ERR_INVALID_ARG, "NULL argument");
+    const auto t0 = std::chrono::steady_clock::now();
+    const cap_tree &t = *p->tree;
+    if (t.shape_gen != p->shape_gen)
+        return fail(CAP_ERR_REPLAN, "the tree's nodes or request paths changed since the plan was built");
+    // every node whose token count changed must end a leaf run with room
+    std::vector<int32_t> grow;
+    for (int n = 0; n < t.N; ++n) {
+        if (t.ntok[n] == p->node_tokens[n]) continue;
+        const int r = t.end_off[n + 1] - t.end_off[n] == 1 ? t.end_list[t.end_off[n]] : -1;
+        if (t.ntok[n] < p->node_tokens[n] || r < 0 || p->leaf[r].node != n)
+            return fail(CAP_ERR_REPLAN, "node %d changed and the plan has no run of its own for it", n);
+        const cap_plan::Leaf &lf = p->leaf[r];
+        const int32_t add = (int32_t)(t.page_off[n + 1] - t.page_off[n]) - lf.pages;
+        const WorkItem &w = p->items[lf.item0];
+        const int32_t cap = w.mode == cap::kModeShared ? cap::kMaxSharedPages : cap::kMaxPrivatePages;
+        if (lf.end + add > lf.limit || w.npages + add > cap)
+            return fail(CAP_ERR_REPLAN, "request %d: %d new pages exceed the room after its run", r, add);
+        grow.push_back(r);
+    }
+    p->patch.clear();
+    bool overflow = false;
+    int64_t words = 0;
+    auto set = [&](size_t byte_off, uint32_t v) {
+        uint32_t *word = reinterpret_cast<uint32_t *>(p->host_image.data() + byte_off);
+        if (*word == v) return;
+        *word = v;
+        ++words;
+        if (p->patch.size() / 2 < p->patch_cap) {
+            p->patch.push_back((uint32_t)(byte_off / 4));
+            p->patch.push_back(v);
+        } else {
+            overflow = true;
+        }
+    };
+    const int Hkv = t.attn.num_kv_heads;
+    int64_t added = 0;
+    for (int r : grow) {
+        cap_plan::Leaf &lf = p->leaf[r];
+        const int n = lf.node;
+        const int32_t pages = (int32_t)(t.page_off[n + 1] - t.page_off[n]);
+        const int32_t first = lf.end - lf.pages;   // stream index of the node's first page
+        for (int32_t k = std::max(0, lf.pages - 1); k < pages; ++k) {
+            const int64_t left = t.ntok[n] - (int64_t)k * cap::kPage;
+            const int32_t e = (int32_t)(((int64_t)t.page_ids[t.page_off[n] + k] << 5) |
+                                        (std::min<int64_t>(cap::kPage, left) - 1));
+            p->stream[first + k] = e;
+            set(p->off_stream + 4 * (size_t)(first + k), (uint32_t)e);
+        }
+        // the run's Hkv items differ only in their head; of a device item
+        // only the page count and the inline entries can change
+        const int32_t add = pages - lf.pages;
+        for (int h = 0; h < Hkv; ++h) p->items[lf.item0 + h].npages += add;
+        const cap::DevItem d = dev_item(*p, p->items[lf.item0]);
+        p->stats.max_pages_per_item = std::max<int32_t>(p->stats.max_pages_per_item, d.npages);
+        const size_t base = p->off_items + (size_t)lf.item0 * sizeof(cap::DevItem);
+        auto put = [&](size_t field, uint32_t v) {   // same word of all Hkv items
+            if (*reinterpret_cast<const uint32_t *>(p->host_image.data() + base + field) == v) return;
+            for (int h = 0; h < Hkv; ++h) set(base + h * sizeof(cap::DevItem) + field, v);
+        };
+        put(offsetof(cap::DevItem, npages), (uint32_t)d.npages);
+        for (int j = 0; j < cap::kInlineEntries; ++j) put(offsetof(cap::DevItem, ent) + 4 * j, (uint32_t)d.ent[j]);
+        lf.end += add;
+        lf.pages = pages;
+        added += add;
+    }
+    p->node_tokens = t.ntok;
+    const int64_t D = t.attn.head_dim;
+    p->stats.kv_bytes_streamed += added * 2LL * cap::kPage * D * 2 * Hkv;
+    p->stats.kv_bytes_unique = t.unique_tokens * 4LL * D * Hkv;
+    p->stats.kv_bytes_unshared = t.sum_ctx * 4LL * D * Hkv;
+    if (words == 0) return CAP_OK;
+    p->stats.refresh_words = words;
+    p->stats.refresh_full_copy = overflow ? 1 : 0;
+    ++p->stats.refreshes;
+    auto done = [&] {
+        p->stats.refresh_host_us =
+            std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count();
+        return CAP_OK;
+    };
+    if (!p->dev) return done();
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char *dev = static_cast<char *>(p->dev);
+    hipError_t e;
+    if (overflow) {
+        // everything before the counters (they read zero between launches)
+        e = hipMemcpyAsync(dev, p->host_image.data(), p->off_cnt, hipMemcpyHostToDevice, s);
+    } else {
+        e = hipMemcpyAsync(dev + p->off_patch, p->patch.data(), p->patch.size() * 4, hipMemcpyHostToDevice, s);
+        if (e == hipSuccess) {
+            const int le = cap::launch_patch(dev, reinterpret_cast<const uint32_t *>(dev + p->off_patch),
+                                             (int)(p->patch.size() / 2), stream);
+            e = static_cast<hipError_t>(le);
+        }
+    }
+    if (e != hipSuccess) {
+        p->dev = nullptr;   // device copy out of date: upload again
+        return fail(CAP_ERR_HIP, "plan patch upload failed: %s", hipGetErrorString(e));
+    }
+    return done();
+}
+
+cap_status cap_append_kv(const cap_tree *tree, const int32_t *dest, int32_t n, const void *k_new,
+                         const void *v_new, void *k_pool, void *v_pool, cap_stream_t stream)
+{
+    if (!tree || n < 0) return fail(CAP_ERR_INVALID_ARG, "NULL tree or negative count");
+    if (n == 0) return CAP_OK;
+    if (!dest || !k_new || !v_new || !k_pool || !v_pool) return fail(CAP_ERR_INVALID_ARG, "NULL argument");
+    if (((uintptr_t)k_new | (uintptr_t)v_new | (uintptr_t)k_pool | (uintptr_t)v_pool) & 15)
+        return fail(CAP_ERR_INVALID_ARG, "k_new, v_new, k_pool and v_pool must be 16-byte aligned");
+    if ((int64_t)n * tree->attn.num_kv_heads * (tree->attn.head_dim / 8) >= ((int64_t)1 << 31))
+        return fail(CAP_ERR_UNSUPPORTED, "%d tokens: too many for one launch", n);
+    cap::AppendArgs a{};
+    a.dest = dest;
+    a.n = n;
+    a.k_new = static_cast<const uint16_t *>(k_new);
+    a.v_new = static_cast<const uint16_t *>(v_new);
+    a.k_pool = static_cast<uint16_t *>(k_pool);
+    a.v_pool = static_cast<uint16_t *>(v_pool);
+    a.Hkv = tree->attn.num_kv_heads;
+    a.D = tree->attn.head_dim;
+    a.pool_pages = tree->num_pool_pages;
+    const int e = cap::launch_append(a, stream);
+    if (e != 0) return fail(CAP_ERR_HIP, "append launch failed: %s", cap::hip_error_string(e));
     return CAP_OK;
 }
 

@@ -95,10 +95,24 @@ struct MergeArgs {
     int32_t R, Hq;
 };
 
+// New tokens' K/V written into their pool slots.
+struct AppendArgs {
+    const int32_t *dest;         // [n]: (physical page << 4) | slot; negative = skip
+    int32_t n;
+    const uint16_t *k_new;       // [n][Hkv][D] bf16
+    const uint16_t *v_new;       // [n][Hkv][D] bf16
+    uint16_t *k_pool;            // [pages][Hkv][D/8][16][8]
+    uint16_t *v_pool;            // [pages][Hkv][D][16]
+    int32_t Hkv, D;
+    int64_t pool_pages;          // entries with a page at or past this are skipped
+};
+
 // Kernel launchers (cap_kernels.hip); return the hipError_t as int.
 int launch_decode(const DecodeArgs &a, int head_dim, void *stream);
 int launch_merge(const MergeArgs &a, int head_dim, void *stream);
 int launch_fill(void *buf, size_t words, uint32_t value, void *stream);
+int launch_patch(void *base, const uint32_t *patch, int n, void *stream);
+int launch_append(const AppendArgs &a, void *stream);
 int launch_read_stream(const void *buf, size_t vec16, void *sink, void *stream);
 int launch_read(const void *buf, size_t vec16, void *sink, void *stream);
 int launch_copy(void *dst, const void *src, size_t vec16, void *stream);

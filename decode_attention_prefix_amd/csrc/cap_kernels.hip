@@ -1128,6 +1128,36 @@ __global__ __launch_bounds__(kWaveSize) void merge_kernel(MergeArgs a)
     merge_rows<D, false>(v, wid / sets, qh0, min(RPW, a.Hq - qh0), threadIdx.x & (kWaveSize - 1));
 }
 
+// Plan patch: word patch[2i] of the plan buffer takes the value patch[2i+1].
+__global__ __launch_bounds__(256) void patch_kernel(uint32_t *base, const uint32_t *patch, int n)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) base[patch[2 * i]] = patch[2 * i + 1];
+}
+
+// New tokens' K/V into their pool slots: one lane per (token, KV head,
+// 8-dim chunk).  K: the chunk is one 16-byte piece of the page block; V:
+// eight 2-byte values, one per dim row of the block.
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a)
+{
+    const int chunks = a.D / 8;
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= a.n * a.Hkv * chunks) return;
+    const int c = t % chunks, h = (t / chunks) % a.Hkv, i = t / (chunks * a.Hkv);
+    const int32_t e = a.dest[i];
+    if (e < 0 || (int64_t)(e >> 4) >= a.pool_pages) return;
+    const int64_t blk = (int64_t)(e >> 4) * a.Hkv + h;
+    const int slot = e & 15;
+    const int64_t src = ((int64_t)i * a.Hkv + h) * a.D + c * 8;
+    const u32x4 k = *reinterpret_cast<const u32x4 *>(a.k_new + src);
+    *reinterpret_cast<u32x4 *>(a.k_pool + ((blk * chunks + c) * kPage + slot) * 8) = k;
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(a.v_new + src);
+    uint16_t *vd = a.v_pool + (blk * a.D + c * 8) * kPage + slot;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vd[j * kPage] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
+}
+
 __global__ __launch_bounds__(256) void fill_kernel(uint32_t *buf, size_t words, uint32_t value)
 {
     const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -1278,6 +1308,23 @@ int launch_fill(void *buf, size_t words, uint32_t value, void *stream)
 {
     hipLaunchKernelGGL(fill_kernel, dim3(grid_for(words)), dim3(256), 0,
                        reinterpret_cast<hipStream_t>(stream), (uint32_t *)buf, words, value);
+    return (int)hipGetLastError();
+}
+
+int launch_patch(void *base, const uint32_t *patch, int n, void *stream)
+{
+    if (n <= 0) return 0;
+    hipLaunchKernelGGL(patch_kernel, dim3((n + 255) / 256), dim3(256), 0,
+                       reinterpret_cast<hipStream_t>(stream), (uint32_t *)base, patch, n);
+    return (int)hipGetLastError();
+}
+
+int launch_append(const AppendArgs &a, void *stream)
+{
+    const int lanes = a.n * a.Hkv * (a.D / 8);
+    if (lanes <= 0) return 0;
+    hipLaunchKernelGGL(append_kernel, dim3((lanes + 255) / 256), dim3(256), 0,
+                       reinterpret_cast<hipStream_t>(stream), a);
     return (int)hipGetLastError();
 }
 

@@ -39,6 +39,8 @@ class TreeDecoder:
         self.plan_buf = None
         self.ws = None
         self.stats = None
+        self.plan_opts = dict(plan_opts)
+        self._grow_bufs = None
         self.plan(**plan_opts)
 
     def stream(self) -> int:
@@ -46,6 +48,7 @@ class TreeDecoder:
 
     def plan(self, **opts):
         torch = self.torch
+        self.plan_opts = dict(opts)
         if self.plan_h:
             torch.cuda.current_stream(self.device).synchronize()
             cap.cap_plan_free(self.plan_h)
@@ -60,6 +63,35 @@ class TreeDecoder:
             self.ws = torch.empty(max(wb // 4, 64), dtype=torch.float32, device=self.device)
         cap.cap_plan_upload(self.plan_h, self.plan_buf.data_ptr(), self.plan_buf.numel(), self.stream())
         return self.stats
+
+    def set_q(self, q: np.ndarray):
+        """Next step's queries (uint16 bf16 bits [R][Hq][D])."""
+        self.q.copy_(_dev_u16(self.torch, q, self.device))
+
+    def grow(self, k_new: np.ndarray, v_new: np.ndarray, new_pages=None, active=None):
+        """One decode step's new tokens (uint16 bf16 bits [R][Hkv][D]): extend
+        the tree on the host (cap_tree_append), write their K/V into the pools
+        (cap_append_kv) and bring the plan up to date (cap_plan_refresh, or a
+        new plan with the same options when it answers CAP_ERR_REPLAN).
+        Returns (dest, replanned)."""
+        torch = self.torch
+        dest = cap.cap_tree_append(self.tree, self.R, active, new_pages)
+        d = torch.from_numpy(dest).to(self.device)
+        k = _dev_u16(torch, k_new, self.device)
+        v = _dev_u16(torch, v_new, self.device)
+        self._grow_bufs = (d, k, v)
+        cap.cap_append_kv(self.tree, d.data_ptr(), self.R, k.data_ptr(), v.data_ptr(), self.k.data_ptr(),
+                          self.v.data_ptr(), self.stream())
+        try:
+            cap.cap_plan_refresh(self.plan_h, self.stream())
+            replanned = False
+        except cap.CapError as e:
+            if e.status != cap.CAP_ERR_REPLAN:
+                raise
+            self.plan(**self.plan_opts)
+            replanned = True
+        self.stats = cap.cap_plan_get_stats(self.plan_h)
+        return dest, replanned
 
     def poison_workspace(self):
         """Fill the partial workspace with all-ones bytes, a NaN in fp32 and in

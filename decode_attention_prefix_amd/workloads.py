@@ -41,7 +41,8 @@ BF16_NAN = np.uint16(0x7FC0)
 __all__ = [
     "PAGE", "Tree", "Workload", "f32_to_bf16_bits", "bf16_bits_to_f32",
     "tree_from_lengths", "make_config", "make_random_tree", "make_workload",
-    "control_workload", "CONFIG_NAMES", "tree_stats",
+    "control_workload", "CONFIG_NAMES", "tree_stats", "free_pages", "grow_tree",
+    "write_new_tokens",
 ]
 
 CONFIG_NAMES = {
@@ -305,13 +306,23 @@ def pack_pools(tree: Tree, kt: np.ndarray, vt: np.ndarray, tok_offs: np.ndarray,
 
 
 def make_config(cfg: int, seed: int = 0, tail_fill: str = "nan",
-                keep_tokens: bool = True, permute_pages: bool = True) -> Workload:
+                keep_tokens: bool = True, permute_pages: bool = True,
+                extra_pool_pages: int = 0) -> Workload:
     """The five seeded shapes.  RNG = default_rng([seed, cfg]); draw order:
-    tree structure, then Q, then K, then V; physical pages are a permutation."""
+    tree structure, then Q, then K, then V; physical pages are a permutation.
+    ``extra_pool_pages`` free pages (filled like unused slots) are appended to
+    the pools afterwards, for decode steps that grow the tree; the draws do
+    not depend on it."""
     rng = np.random.default_rng([seed, cfg])
     nt, par, paths, Hq, Hkv, D = _config_shape(cfg, rng)
     w = make_workload(nt, par, paths, Hq, Hkv, D, rng, permute_pages=permute_pages,
                       tail_fill=tail_fill, keep_tokens=keep_tokens)
+    if extra_pool_pages > 0:
+        fill = BF16_NAN if tail_fill == "nan" else np.uint16(0)
+        n = int(extra_pool_pages)
+        w.k_pool = np.concatenate([w.k_pool, np.full((n,) + w.k_pool.shape[1:], fill, np.uint16)])
+        w.v_pool = np.concatenate([w.v_pool, np.full((n,) + w.v_pool.shape[1:], fill, np.uint16)])
+        w.tree.num_pool_pages += n
     w.meta.update(config=cfg, seed=seed, name=CONFIG_NAMES[cfg])
     return w
 
@@ -359,3 +370,77 @@ def tree_stats(t: Tree) -> dict:
         "request_heads": t.num_requests * t.num_q_heads,
         "sum_context": int(ctx.sum()),
     }
+
+
+# --------------------------------------------------------------- decode growth
+
+def free_pages(tree: Tree) -> np.ndarray:
+    """Pool pages that no node holds, ascending."""
+    used = np.zeros(int(tree.num_pool_pages), dtype=bool)
+    used[tree.page_ids.astype(np.int64)] = True
+    return np.flatnonzero(~used).astype(np.int32)
+
+
+def grow_tree(tree: Tree, active=None, new_pages=None):
+    """The tree after one decode step: every active request gains one token at
+    the end of its context.
+
+    Rule: when a request's path ends at a leaf that no other request's path
+    passes through, the leaf takes the token, in the next slot of its last
+    page or, when that page is full (or the leaf has no page), in page
+    ``new_pages[r]``; otherwise a new one-token child of the end node, holding
+    page ``new_pages[r]``, becomes the request's leaf (new ids in request
+    order).  Returns ``(new_tree, dest)`` with dest[r] = (page << 4) | slot,
+    -1 for an inactive request.  Pure bookkeeping on the description."""
+    N, R = tree.num_nodes, tree.num_requests
+    act = np.ones(R, dtype=bool) if active is None else np.asarray(active, dtype=bool)
+    ntok = [int(x) for x in tree.num_tokens]
+    parent = [int(x) for x in tree.parent]
+    pages = [list(tree.page_ids[tree.page_offsets[n]:tree.page_offsets[n + 1]]) for n in range(N)]
+    paths = [list(tree.path(r)) for r in range(R)]
+    passing = np.zeros(N, dtype=np.int64)
+    for p in paths:
+        passing[p] += 1
+    has_child = np.zeros(N, dtype=bool)
+    for c in range(N):
+        if parent[c] >= 0:
+            has_child[parent[c]] = True
+    dest = np.full(R, -1, dtype=np.int32)
+    for r in range(R):
+        if not act[r]:
+            continue
+        n = paths[r][-1]
+        if not has_child[n] and passing[n] == 1:
+            if ntok[n] % PAGE == 0:
+                pages[n].append(int(new_pages[r]))
+            dest[r] = (int(pages[n][ntok[n] // PAGE]) << 4) | (ntok[n] % PAGE)
+            ntok[n] += 1
+        else:
+            parent.append(n)
+            ntok.append(1)
+            pages.append([int(new_pages[r])])
+            paths[r].append(len(parent) - 1)
+            dest[r] = int(new_pages[r]) << 4
+    offs = np.zeros(len(pages) + 1, dtype=np.int64)
+    np.cumsum([len(p) for p in pages], out=offs[1:])
+    ids = np.asarray([pg for p in pages for pg in p], dtype=np.int32)
+    poffs = np.zeros(R + 1, dtype=np.int32)
+    np.cumsum([len(p) for p in paths], out=poffs[1:])
+    pn = np.asarray([n for p in paths for n in p], dtype=np.int32)
+    new = Tree(tree.num_q_heads, tree.num_kv_heads, tree.head_dim,
+               np.asarray(parent, dtype=np.int32), np.asarray(ntok, dtype=np.int32), offs, ids,
+               poffs, pn, tree.num_pool_pages, tree.sm_scale, tree.page_size)
+    return new, dest
+
+
+def write_new_tokens(k_pool: np.ndarray, v_pool: np.ndarray, dest: np.ndarray,
+                     k_new: np.ndarray, v_new: np.ndarray) -> None:
+    """Store token i's K/V bits ([n][Hkv][D] each) at page dest[i] >> 4, slot
+    dest[i] & 15 of the host pools (in place); negative entries are skipped."""
+    for i, e in enumerate(np.asarray(dest)):
+        if e < 0:
+            continue
+        pg, slot = int(e) >> 4, int(e) & 15
+        Hkv, D = k_new.shape[1], k_new.shape[2]
+        k_pool[pg, :, :, slot, :] = k_new[i].reshape(Hkv, D // 8, 8)
+        v_pool[pg, :, :, slot] = v_new[i]

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define CAP_ABI_VERSION 5
+#define CAP_ABI_VERSION 6
 
 typedef enum cap_status {
     CAP_OK = 0,
@@ -60,7 +60,9 @@ typedef enum cap_status {
     CAP_ERR_WORKSPACE = 3,     /* a caller buffer is smaller than required / misaligned */
     CAP_ERR_UNSUPPORTED = 4,   /* shape outside the supported envelope */
     CAP_ERR_HIP = 5,           /* a HIP runtime call or kernel launch failed */
-    CAP_ERR_STATE = 6          /* handle used in the wrong state (e.g. plan not uploaded) */
+    CAP_ERR_STATE = 6,         /* handle used in the wrong state (e.g. plan not uploaded) */
+    CAP_ERR_REPLAN = 7         /* cap_plan_refresh: the plan cannot take the tree's changes in
+                                  place; build a new plan with cap_plan_step */
 } cap_status;
 
 /* A hipStream_t, passed through untouched. */
@@ -148,6 +150,10 @@ typedef struct cap_plan_opts {
                                  counters in the plan buffer.  Both read the same
                                  bytes; with the memory system saturated neither is
                                  faster on the measured trees, 0 by a little */
+    int32_t append_slack;     /* 0 = 8; -1 = none; at most 4096.  Free page-stream entries
+                                 reserved after each request's own leaf run, so that
+                                 cap_plan_refresh can add that many new leaf pages per
+                                 request before a new plan is needed */
 } cap_plan_opts;
 
 /* Plan summary (host-side numbers; bytes are per decode step). */
@@ -167,6 +173,10 @@ typedef struct cap_plan_stats {
     int32_t max_partials_per_request;
     int32_t max_pages_per_item;
     double plan_host_us;          /* host time spent in cap_plan_step */
+    double refresh_host_us;       /* host time of the last cap_plan_refresh (0: none yet) */
+    int64_t refresh_words;        /* 32-bit words of the plan image it changed */
+    int32_t refresh_full_copy;    /* 1 if it sent the whole image instead of a word list */
+    int32_t refreshes;            /* cap_plan_refresh calls that changed the plan */
 } cap_plan_stats;
 
 typedef struct cap_tree cap_tree;   /* opaque host handles */
@@ -216,7 +226,8 @@ cap_status cap_tree_device_bytes(const cap_attn_desc *attn, const cap_tree_desc 
  * kernels never read the tree's page table; dev_buf is optional (may be NULL)
  * and, when given (>= cap_tree_device_bytes, 16-byte aligned), receives a
  * device copy of page_ids with one asynchronous copy on `stream` for callers
- * that want the table on the GPU.  The host arrays may be freed on return.
+ * that want the table on the GPU (the table as uploaded: cap_tree_append does
+ * not update it).  The host arrays may be freed on return.
  * On success *out owns a handle the caller releases with cap_tree_free
  * (after the stream has passed the copy, if one was made).
  * Errors: CAP_ERR_INVALID_ARG (NULL desc/out), CAP_ERR_UNSUPPORTED (shape),
@@ -226,6 +237,47 @@ cap_status cap_tree_upload(const cap_attn_desc *attn, const cap_tree_desc *tree,
                            void *dev_buf, size_t dev_bytes, cap_stream_t stream,
                            cap_tree **out);
 void cap_tree_free(cap_tree *tree);
+
+/* Host view of the tree as it stands (after any appends), in the form of
+ * cap_tree_desc.  The pointers refer to the tree's own arrays and stay valid
+ * until the next cap_tree_append or cap_tree_free.  Errors: CAP_ERR_INVALID_ARG. */
+cap_status cap_tree_get_desc(const cap_tree *tree, cap_tree_desc *desc);
+
+/* Grow the tree by one decode step: each active request (active[r] != 0;
+ * active NULL = every request) gains one context token, the token whose K/V
+ * the step produced, at the end of its context.  Where the cache keeps it
+ * (the radix-tree KV cache of the Capillary Kernels project page, abstract,
+ * first paragraph; the pages give no update rule, so this is the plain one):
+ *  - the request's path ends at a leaf that no other request's path passes
+ *    through: the leaf grows by one token, into the next slot of its last
+ *    page, or into the page new_pages[r] when that page is full or the leaf
+ *    has none;
+ *  - otherwise (its end node is shared or has children): a new one-token
+ *    child of that node holding page new_pages[r] becomes the request's
+ *    leaf (node id = the next free id, in request order); the end node and
+ *    its pages stay as they are for the other requests.
+ * Host-only bookkeeping: no device call.  dest[r] (out, host [R]) receives
+ * (physical page << 4) | slot of the new token, or -1 for an inactive
+ * request; slot 0 means new_pages[r] was taken, otherwise it is still free.
+ * new_pages (host [R]) may be NULL when no request needs a page; each page a
+ * request takes must be in [0, num_pool_pages), owned by no node, and not
+ * given to two requests.  A new child changes the tree's shape: plans built
+ * before it answer cap_plan_refresh with CAP_ERR_REPLAN.  Validation happens
+ * before any change.  Errors: CAP_ERR_INVALID_ARG (NULL tree/dest, new_pages
+ * needed but NULL), CAP_ERR_BAD_TREE (a new page out of range, owned or given
+ * twice), CAP_ERR_UNSUPPORTED (2^26 pages or more). */
+cap_status cap_tree_append(cap_tree *tree, const uint8_t *active, const int32_t *new_pages,
+                           int32_t *dest);
+
+/* Write the new tokens' K and V into the pools: token i, KV head h goes to
+ * page dest[i] >> 4, slot dest[i] & 15 of head h's block (the pool layouts
+ * above).  dest: DEVICE int32 [n] (e.g. cap_tree_append's output copied to
+ * the GPU); entries < 0 or with a page >= the tree's num_pool_pages are
+ * skipped.  k_new, v_new: device bf16 [n][Hkv][D], 16-byte aligned.  One
+ * launch on `stream`; n = 0 launches nothing.  Errors: CAP_ERR_INVALID_ARG,
+ * CAP_ERR_UNSUPPORTED (n x Hkv x D/8 >= 2^31), CAP_ERR_HIP. */
+cap_status cap_append_kv(const cap_tree *tree, const int32_t *dest, int32_t n, const void *k_new,
+                         const void *v_new, void *k_pool, void *v_pool, cap_stream_t stream);
 
 /* Per-step planner (host only, no device calls): share/fold decisions per
  * node, KV split lengths, request groups, work-item order, partial slots and
@@ -242,9 +294,32 @@ cap_status cap_plan_get_view(const cap_plan *plan, cap_plan_view *view);
  * step's arrival counters, R x Hkv int32, and the work queues' counters;
  * all zero after the upload and again after every completed launch), so it
  * must stay writable device memory, and launches that use one plan buffer
- * must not overlap (on one stream they never do).
+ * must not overlap (on one stream they never do).  After the counters comes
+ * the area cap_plan_refresh stages its patches in.
  * Errors: CAP_ERR_INVALID_ARG, CAP_ERR_WORKSPACE, CAP_ERR_HIP. */
 cap_status cap_plan_upload(cap_plan *plan, void *dev_buf, size_t bytes, cap_stream_t stream);
+
+/* Bring the plan up to date with the tree after cap_tree_append, without
+ * planning again: each leaf run that serves one request and ends with the
+ * pages of that request's own leaf takes the leaf's new token count and new
+ * pages (into the free entries reserved after the run, see append_slack);
+ * the items of that run stream the longer run, the partial rows stay.  The
+ * host plan changes first; if the plan has been uploaded, the changed
+ * 32-bit words go to its device buffer on `stream`: one copy of a
+ * (word, value) list into the buffer's patch area and one small kernel that
+ * applies it (one copy of the whole plan image before the counters, when
+ * the list outgrows the area).  Stream-ordered like cap_plan_upload: launches
+ * on `stream` after it see the new plan; the list is read from host memory
+ * the plan owns, as in cap_plan_upload.  Splits and balance stay those of
+ * the plan's own build, so a long-lived plan drifts from what cap_plan_step
+ * would choose; callers replan now and then.  Returns CAP_ERR_REPLAN, with
+ * nothing changed, when a changed node has no such run (a node shared with
+ * other requests, or a leaf folded into a run with others), when a run has
+ * no room left (free entries, or the item's page limit: 64 shared, 256
+ * private), or when the tree's shape changed (a new node).  Errors:
+ * CAP_ERR_INVALID_ARG, CAP_ERR_REPLAN, CAP_ERR_HIP (the device copy is then
+ * out of date and the plan counts as not uploaded). */
+cap_status cap_plan_refresh(cap_plan *plan, cap_stream_t stream);
 
 /* Launch the decode kernel: every work item streams its KV pages once for
  * all its query rows and writes (m, l, o/l) partials into `workspace`
