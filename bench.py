@@ -159,6 +159,8 @@ def main():
                          "cap_merge_partials")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--read-probe-mb", type=int, default=2048)
+    ap.add_argument("--contiguous", action="store_true",
+                    help="physical pages in tree order instead of a seeded permutation of the pool")
     ap.add_argument("--growth-steps", type=int, default=16,
                     help="after the timed steps: decode steps that first grow the tree by one token "
                          "per request (host append, K/V write, plan refresh), timed apart (0 = none)")
@@ -190,7 +192,7 @@ def main():
     R_cfg = {0: 4, 1: 64, 2: 128, 3: 32, 4: 256}[args.config]
     extra_pages = R_cfg * (growth // 16 + 3) if growth else 0
     w = wl.make_config(args.config, seed=args.seed, tail_fill="zero", keep_tokens=args.control,
-                       extra_pool_pages=extra_pages)
+                       extra_pool_pages=extra_pages, permute_pages=not args.contiguous)
     if args.control:
         w = wl.control_workload(w, tail_fill="zero")
     st_tree = wl.tree_stats(w.tree)
@@ -323,6 +325,7 @@ def main():
             "requests": w.tree.num_requests, "q_heads": w.tree.num_q_heads,
             "kv_heads": w.tree.num_kv_heads, "head_dim": w.tree.head_dim, "page_size": 16,
             "seed": args.seed, "nodes": w.tree.num_nodes,
+            "pages": "tree order" if args.contiguous else "seeded permutation of the pool",
         },
         "roofline": {
             "bound": "hbm",
@@ -370,14 +373,19 @@ def main():
             oracle.decode(w.tree, w.q, w.k_pool, w.v_pool, nthreads=ncores)
             runs.append(time.perf_counter() - t1)
         t_or = statistics.median(runs)
+        cores = oracle.threads()
+        t1 = time.perf_counter()
+        oracle.decode(w.tree, w.q, w.k_pool, w.v_pool, nthreads=1)
+        t_one = time.perf_counter() - t1
         result["cpu_baseline"] = {
             "value": round(uniq / t_or / 1e9, 4),
             "unit": "GB/s",
-            "cores": oracle.threads(),
+            "cores": cores,
             "kind": "oracle",
             "sample": f"whole workload ({w.tree.num_requests} requests), median of {len(runs)} runs, "
                       f"{t_or:.3f} s each",
             "cpu": cpu_model(),
+            "one_core": {"value": round(uniq / t_one / 1e9, 4), "unit": "GB/s", "sample": f"one run, {t_one:.3f} s"},
         }
     if growth:
         result["growth"] = measure_growth(dec, w.tree, extra_pages, growth, args, evict, stream)

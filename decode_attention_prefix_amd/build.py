@@ -10,7 +10,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libcap.so")
-SOURCES = [os.path.join(CSRC, "cap_host.cpp"), os.path.join(CSRC, "cap_kernels.hip")]
+SOURCES = [os.path.join(CSRC, "cap_host.cpp"), os.path.join(CSRC, "cap_kernels.hip"),
+           os.path.join(CSRC, "cap_aux.hip")]
 HEADERS = [os.path.join(CSRC, "cap_internal.h"), os.path.join(ROOT, "include", "cap.h"),
            os.path.join(ROOT, "include", "cap_bench.h")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -23,6 +24,7 @@ FLAGS = ["--offload-arch=gfx950", "-O2", "-std=c++17", "-fPIC", "-shared", "-Wal
          # atomics stay per lane: the wave-aggregating rewrite would wait for the
          # decode kernel's work-queue ticket right where it is issued
          "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
+         "-Wl,--no-undefined",
          "-I", os.path.join(ROOT, "include")]
 
 

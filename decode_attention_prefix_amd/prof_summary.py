@@ -37,7 +37,8 @@ def kernel_hash() -> str:
 
 
 def _short(name: str) -> str:
-    for key in ("decode_kernel", "merge_kernel", "read_kernel", "fill_kernel", "copy_kernel"):
+    for key in ("decode_kernel", "merge_kernel", "read_stream_kernel", "read_kernel", "fill_kernel",
+                "copy_kernel", "patch_kernel", "append_kernel"):
         if key in name:
             tail = name[name.index(key):]
             return tail.split("(")[0]
@@ -75,6 +76,7 @@ def main(argv=None):
     ap.add_argument("--kernel", default="decode_kernel<128, false>")
     ap.add_argument("--bench-args", default="--no-cpu-baseline")
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
+    ap.add_argument("--name", default="", help="summary file name (default decode_kernel_cfg<N>_kernel_trace.txt)")
     a = ap.parse_args(argv)
     if a.fetch and a.write and a.alg_bytes <= 0:
         ap.error("--alg-bytes is needed with --fetch/--write")
@@ -89,8 +91,11 @@ def main(argv=None):
              f"{'kernel':40s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
     for name, calls, avg, mn, mx in kt:
         lines.append(f"{name:40s} {calls:6d} {avg:9.3f} {mn:9.3f} {mx:9.3f}")
-    lines += ["", "(read_kernel and fill_kernel are the bench's cache-eviction read and buffer setup)"]
-    with open(os.path.join(a.out, f"decode_kernel_cfg{cfg}_kernel_trace.txt"), "w") as f:
+    lines += ["", "(read_kernel and fill_kernel: the bench's cache-eviction read and buffer setup; "
+              "read_stream_kernel: its achievable-read probe; append_kernel and patch_kernel: "
+              "cap_append_kv and cap_plan_refresh in its growth steps)"]
+    name = a.name or f"decode_kernel_cfg{cfg}_kernel_trace.txt"
+    with open(os.path.join(a.out, name), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
     if not (a.fetch and a.write):
@@ -108,9 +113,9 @@ def main(argv=None):
     lines = [f"HBM traffic of one {a.kernel} launch, bench.py --config {cfg} ({a.workload})",
              "commands (each its own run):",
              f"  cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out> -o pmc -- python3 "
-             f"<repo>/bench.py --config {cfg} --no-cpu-baseline --steps 3 --warmup 1 --copy-probe-mb {a.copy_mb}",
+             f"<repo>/bench.py --config {cfg} {a.bench_args} --steps 3 --warmup 1 --copy-probe-mb {a.copy_mb}",
              f"  cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out> -o pmc -- python3 "
-             f"<repo>/bench.py --config {cfg} --no-cpu-baseline --steps 3 --warmup 1 --copy-probe-mb {a.copy_mb}",
+             f"<repo>/bench.py --config {cfg} {a.bench_args} --steps 3 --warmup 1 --copy-probe-mb {a.copy_mb}",
              f"kernel_code_sha256_16: {h}",
              f"kernel: {a.kernel}",
              f"copy_kernel_{a.copy_mb}MiB_fetch_kib: {fetch['copy_kernel']:.1f}",
