@@ -152,6 +152,7 @@ def main():
     ap.add_argument("--rounds", type=float, default=0.0)
     ap.add_argument("--order", type=int, default=0, help="work-item order (planner option)")
     ap.add_argument("--shared-cost", type=float, default=0.0)
+    ap.add_argument("--share-margin", type=float, default=0.0, help="planner option (0 = default)")
     ap.add_argument("--dispatch", type=int, default=0, choices=[0, 1],
                     help="0 one workgroup per item (default), 1 work queues (planner option item_dispatch)")
     ap.add_argument("--fused", action="store_true",
@@ -206,6 +207,8 @@ def main():
         opts["order"] = args.order
     if args.shared_cost:
         opts["shared_cost"] = args.shared_cost
+    if args.share_margin:
+        opts["share_margin"] = args.share_margin
     if args.dispatch:
         opts["item_dispatch"] = args.dispatch
     dec = TreeDecoder(w.tree, w.q, w.k_pool, w.v_pool, device=dev, **opts)

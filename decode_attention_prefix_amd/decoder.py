@@ -9,7 +9,13 @@ import numpy as np
 from . import cap
 
 
-def _dev_u16(torch, a: np.ndarray, device):
+def _dev_u16(torch, a, device):
+    """Device int16 tensor of bf16 bits: numpy arrays are copied over, device
+    tensors (int16 or bfloat16, contiguous) are used as they are."""
+    if isinstance(a, torch.Tensor):
+        if a.device != device or not a.is_contiguous() or a.element_size() != 2:
+            raise ValueError("device arrays must be contiguous 2-byte tensors on the decoder's device")
+        return a.view(torch.int16)
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device)
 
 
@@ -17,7 +23,8 @@ class TreeDecoder:
     """One radix tree resident on the GPU, ready to plan and decode steps.
 
     tree: a ``workloads.Tree`` (or any object with the same attributes);
-    q, k_pool, v_pool: uint16 bf16-bit arrays in the layouts of include/cap.h.
+    q, k_pool, v_pool: uint16 bf16-bit arrays in the layouts of include/cap.h,
+    or device tensors already holding them.
     """
 
     def __init__(self, tree, q, k_pool, v_pool, device="cuda", **plan_opts):
@@ -26,6 +33,8 @@ class TreeDecoder:
         self.device = torch.device(device)
         if self.device.type != "cuda" or not torch.cuda.is_available():
             raise RuntimeError("TreeDecoder needs a GPU (ROCm) device")
+        if self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
         self.tree_host = tree
         self.R, self.Hq, self.D = int(tree.num_requests), int(tree.num_q_heads), int(tree.head_dim)
         self.q = _dev_u16(torch, q, self.device)
