@@ -42,7 +42,7 @@ __all__ = [
     "PAGE", "Tree", "Workload", "f32_to_bf16_bits", "bf16_bits_to_f32",
     "tree_from_lengths", "make_config", "make_random_tree", "make_workload",
     "control_workload", "CONFIG_NAMES", "tree_stats", "free_pages", "grow_tree",
-    "write_new_tokens",
+    "write_new_tokens", "ROW_KINDS", "make_rows",
 ]
 
 CONFIG_NAMES = {
@@ -444,3 +444,28 @@ def write_new_tokens(k_pool: np.ndarray, v_pool: np.ndarray, dest: np.ndarray,
         Hkv, D = k_new.shape[1], k_new.shape[2]
         k_pool[pg, :, :, slot, :] = k_new[i].reshape(Hkv, D // 8, 8)
         v_pool[pg, :, :, slot] = v_new[i]
+
+
+# ------------------------------------------------- wide-row reduction inputs
+
+# rows per workload as in the CREDIT summary's evaluation (section V.A):
+# 2048 for LayerNorm, 4096 for the others; widths 4K..64K
+ROW_KINDS = {"softmax": 4096, "layernorm": 2048}
+
+
+def make_rows(kind: str, width: int, rows: Optional[int] = None, seed: int = 0):
+    """Seeded FP32 inputs of one row workload: x [rows][width] ~ N(0, 1);
+    LayerNorm also gets per-column gamma ~ 1 + 0.1 N(0, 1) and beta ~
+    0.1 N(0, 1).  RNG = default_rng([seed, 7, width, kind index]); draw
+    order x, gamma, beta.  Returns (x, gamma, beta), the last two None for
+    softmax."""
+    if kind not in ROW_KINDS:
+        raise ValueError(f"unknown row workload {kind}")
+    rows = ROW_KINDS[kind] if rows is None else int(rows)
+    rng = np.random.default_rng([seed, 7, int(width), list(ROW_KINDS).index(kind)])
+    x = rng.standard_normal((rows, int(width)), dtype=np.float32)
+    if kind != "layernorm":
+        return x, None, None
+    gamma = (1.0 + 0.1 * rng.standard_normal(int(width))).astype(np.float32)
+    beta = (0.1 * rng.standard_normal(int(width))).astype(np.float32)
+    return x, gamma, beta

@@ -8,6 +8,9 @@ nothing from it: callers hand it plain numpy arrays.
 Two independent implementations of the same definition:
 * ``decode`` -- the C oracle in ``cap_oracle.c`` (OpenMP over request x KV head);
 * ``ref_np.decode_np`` -- a numpy twin written separately, used to cross-check.
+
+``rows_np`` holds the fp64 oracle of the wide-row reduction-reuse workloads
+(softmax over logits, LayerNorm).
 """
 import ctypes
 import os
