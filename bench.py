@@ -65,6 +65,114 @@ def cpu_model() -> str:
     return platform.processor()
 
 
+def bench_rows(args, dev):
+    """One JSON line for a wide-row workload: the chosen schedule's HBM rate
+    on the evaluation's row count, with the two-pass schedule and torch's own
+    kernel timed beside it and the fp64 oracle on a bounded sample."""
+    import torch
+
+    from decode_attention_prefix_amd import cap
+    from decode_attention_prefix_amd import workloads as wl
+    from decode_attention_prefix_amd.prof_summary import ROWS_SRC
+
+    kind, W = args.rows, args.width
+    x, g, b = wl.make_rows(kind, W, seed=args.seed)
+    M = x.shape[0]
+    xd = torch.from_numpy(x).to(dev)
+    yd = torch.empty_like(xd)
+    gd = torch.from_numpy(g).to(dev) if g is not None else None
+    bd = torch.from_numpy(b).to(dev) if b is not None else None
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    flush = torch.empty(max(args.flush_mb, 1) << 20, dtype=torch.uint8, device=dev)
+    sink = torch.empty(8192, dtype=torch.int32, device=dev)
+    cap.cap_bench_fill(flush.data_ptr(), flush.numel(), 0, sp)
+
+    def launch(mode):
+        if kind == "softmax":
+            cap.cap_rows_softmax(xd.data_ptr(), yd.data_ptr(), M, W, mode, sp)
+        else:
+            cap.cap_rows_layernorm(xd.data_ptr(), gd.data_ptr(), bd.data_ptr(), yd.data_ptr(), M, W, 1e-5,
+                                   mode, sp)
+
+    def torch_op():
+        # torch's own kernel, for context only (its output is discarded)
+        if kind == "softmax":
+            torch.softmax(xd, dim=1)
+        else:
+            torch.nn.functional.layer_norm(xd, (W,), gd, bd, eps=1e-5)
+
+    def timed(fn, steps):
+        for _ in range(args.warmup):
+            fn()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for e in ev:
+            if args.flush_mb > 0:
+                cap.cap_bench_read(flush.data_ptr(), flush.numel(), sink.data_ptr(), sp)
+            e[0].record(stream)
+            fn()
+            e[1].record(stream)
+        torch.cuda.synchronize(dev)
+        return [a.elapsed_time(b_) * 1e3 for a, b_ in ev]
+
+    # achievable read + write rate: a plain copy of as many bytes as x
+    nb = M * W * 4
+    cdst = torch.empty(nb, dtype=torch.uint8, device=dev)
+    copy_us = timed(lambda: cap.cap_bench_copy(cdst.data_ptr(), xd.data_ptr(), nb, sp), args.steps)
+    del cdst
+    mode = args.row_mode
+    us = timed(lambda: launch(mode), args.steps)
+    reread_us = timed(lambda: launch(2), args.steps)
+    torch_us = timed(torch_op, max(3, args.steps // 3))
+    mean_us = statistics.fmean(us)
+    alg = 2 * M * W * 4 + (2 * W * 4 if kind == "layernorm" else 0)
+    value = alg / (mean_us * 1e-6) / 1e9
+    src_hash = kernel_hash(ROWS_SRC)
+    retained = mode == 1 or (mode == 0 and W <= 65536 and W % 4 == 0) or (mode == 0 and W <= 16384)
+    kname = "rows_retained_kernel" if retained else "rows_reread_kernel"
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", f"rows_{kind}_{W}_traffic.txt")
+    if os.path.exists(tpath):
+        kv = {}
+        for line in open(tpath):
+            if ":" in line:
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+        if kv.get("kernel_code_sha256_16") == src_hash and kv.get("kernel", "").startswith(kname):
+            traffic = float(kv["hbm_bytes_per_launch"])
+    result = {
+        "metric": f"row {kind} HBM GB/s (rows read + written once), 1 GPU",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(mean_us / 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{kind} over {M} rows x {W} FP32 (N(0,1) inputs)", "rows": M, "width": W,
+                   "mode": {0: "auto", 1: "retained row", 2: "two passes"}[mode]},
+        "roofline": {"bound": "hbm", "achieved": round(value, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(value / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel": kname,
+                     "algorithmic_bytes_per_launch": alg, "kernel_us_mean": round(mean_us, 3)},
+        "t_us": {"mean": round(mean_us, 3), "median": round(statistics.median(us), 3), "min": round(min(us), 3)},
+        "two_pass_us_mean": round(statistics.fmean(reread_us), 3),
+        "torch_us_mean": round(statistics.fmean(torch_us), 3),
+        "speedup_vs_two_pass": round(statistics.fmean(reread_us) / mean_us, 3),
+        "speedup_vs_torch": round(statistics.fmean(torch_us) / mean_us, 3),
+        "kernel_code_sha256_16": src_hash,
+        "copy_same_bytes_gbs": round(2 * nb / (min(copy_us) * 1e-6) / 1e9, 1),
+        "pct_of_copy_rate": round(100 * value / (2 * nb / (min(copy_us) * 1e-6) / 1e9), 2),
+    }
+    if not args.no_cpu_baseline:
+        from oracle import rows_np
+        n = max(1, min(M, (1 << 22) // W))        # about 4M values: a few seconds of fp64 numpy
+        t1 = time.perf_counter()
+        if kind == "softmax":
+            rows_np.softmax_rows(x[:n])
+        else:
+            rows_np.layernorm_rows(x[:n], g, b)
+        t = time.perf_counter() - t1
+        result["cpu_baseline"] = {"value": round(2 * n * W * 4 / t / 1e9, 4), "unit": "GB/s", "cores": 1,
+                                  "kind": "oracle", "sample": f"first {n} of {M} rows, {t:.3f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def measure_growth(dec, tree, extra_pages, steps, args, evict, stream):
     """Decode steps on a growing tree: before each step, every request gains
     one token (cap_tree_append on the host, cap_append_kv on the GPU) and the
@@ -165,6 +273,11 @@ def main():
     ap.add_argument("--growth-steps", type=int, default=16,
                     help="after the timed steps: decode steps that first grow the tree by one token "
                          "per request (host append, K/V write, plan refresh), timed apart (0 = none)")
+    ap.add_argument("--rows", choices=["softmax", "layernorm"], default=None,
+                    help="time a wide-row reduction-reuse workload instead of decode attention")
+    ap.add_argument("--width", type=int, default=65536, help="row width for --rows")
+    ap.add_argument("--row-mode", type=int, default=0, choices=[0, 1, 2],
+                    help="0 auto, 1 retained row, 2 two passes (for --rows)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run one plain copy of this size (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -187,6 +300,9 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.rows:
+        bench_rows(args, dev)
+        return
 
     t_gen = time.perf_counter()
     growth = args.growth_steps if not args.control else 0

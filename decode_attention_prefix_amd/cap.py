@@ -1,4 +1,4 @@
-"""Thin ctypes binding of libcap (include/cap.h, include/cap_bench.h).
+"""Thin ctypes binding of libcap (include/cap.h, include/cap_bench.h, include/cap_rows.h).
 
 Argument marshalling only: every step of the attention path runs in the
 library's HIP kernels.  Functions keep the C names; device buffers are
@@ -29,6 +29,7 @@ EXPORTED = [
     "cap_plan_get_view", "cap_plan_upload", "cap_decode_attention", "cap_merge_partials",
     "cap_decode_step", "cap_plan_free", "cap_tree_get_desc", "cap_tree_append", "cap_append_kv",
     "cap_plan_refresh", "cap_bench_fill", "cap_bench_read", "cap_bench_read_stream", "cap_bench_copy",
+    "cap_rows_softmax", "cap_rows_layernorm",
 ]
 
 
@@ -121,6 +122,9 @@ def lib():
         L.cap_tree_append.argtypes = [vp, vp, vp, vp]
         L.cap_append_kv.argtypes = [vp, vp, ctypes.c_int32, vp, vp, vp, vp, vp]
         L.cap_plan_refresh.argtypes = [vp, vp]
+        i64, i32 = ctypes.c_int64, ctypes.c_int32
+        L.cap_rows_softmax.argtypes = [vp, vp, i64, i64, i32, vp]
+        L.cap_rows_layernorm.argtypes = [vp, vp, vp, vp, i64, i64, ctypes.c_float, i32, vp]
         L.cap_bench_fill.argtypes = [vp, sz, ctypes.c_uint32, vp]
         L.cap_bench_read.argtypes = [vp, sz, vp, vp]
         L.cap_bench_read_stream.argtypes = [vp, sz, vp, vp]
@@ -128,7 +132,8 @@ def lib():
         for name in ("cap_tree_device_bytes", "cap_tree_upload", "cap_plan_step",
                      "cap_plan_get_stats", "cap_plan_get_view", "cap_plan_upload",
                      "cap_decode_attention", "cap_merge_partials", "cap_decode_step", "cap_tree_get_desc",
-                     "cap_tree_append", "cap_append_kv", "cap_plan_refresh", "cap_bench_fill",
+                     "cap_tree_append", "cap_append_kv", "cap_plan_refresh", "cap_rows_softmax",
+                     "cap_rows_layernorm", "cap_bench_fill",
                      "cap_bench_read", "cap_bench_read_stream", "cap_bench_copy"):
             getattr(L, name).restype = st
         _lib = L
@@ -308,6 +313,17 @@ def cap_decode_step(plan: int, q: int, k_pool: int, v_pool: int, workspace: int,
 def cap_plan_free(plan: int) -> None:
     if plan:
         lib().cap_plan_free(ctypes.c_void_p(plan))
+
+
+def cap_rows_softmax(x: int, y: int, rows: int, width: int, mode: int = 0, stream: int = 0) -> None:
+    _check(lib().cap_rows_softmax(ctypes.c_void_p(x), ctypes.c_void_p(y), rows, width, mode,
+                                  ctypes.c_void_p(stream or None)))
+
+
+def cap_rows_layernorm(x: int, gamma: int, beta: int, y: int, rows: int, width: int, eps: float = 1e-5,
+                       mode: int = 0, stream: int = 0) -> None:
+    _check(lib().cap_rows_layernorm(ctypes.c_void_p(x), ctypes.c_void_p(gamma), ctypes.c_void_p(beta),
+                                    ctypes.c_void_p(y), rows, width, eps, mode, ctypes.c_void_p(stream or None)))
 
 
 def cap_bench_fill(buf: int, nbytes: int, value: int = 0, stream: int = 0) -> None:

@@ -32,6 +32,7 @@
 #include <vector>
 
 #include "../../include/cap_bench.h"
+#include "../../include/cap_rows.h"
 #include "cap_internal.h"
 
 using cap::WorkItem;
@@ -1095,6 +1096,66 @@ cap_status cap_merge_partials(const cap_plan *plan, const void *workspace, size_
 }
 
 void cap_plan_free(cap_plan *plan) { delete plan; }
+
+// ------------------------------------------------------- wide-row workloads
+
+static cap_status rows_launch(cap::RowArgs &a, int32_t mode, cap_stream_t stream)
+{
+    if (!a.x || !a.y) return fail(CAP_ERR_INVALID_ARG, "NULL argument");
+    if (a.rows < 0 || a.width < 1) return fail(CAP_ERR_INVALID_ARG, "rows %lld / width %lld out of range",
+                                             (long long)a.rows, (long long)a.width);
+    if (mode < 0 || mode > 2) return fail(CAP_ERR_INVALID_ARG, "mode %d not in {0, 1, 2}", mode);
+    if (a.rows > std::numeric_limits<int32_t>::max())
+        return fail(CAP_ERR_UNSUPPORTED, "%lld rows: at most 2^31 - 1", (long long)a.rows);
+    if (a.width > ((int64_t)1 << 24))
+        return fail(CAP_ERR_UNSUPPORTED, "width %lld above 2^24", (long long)a.width);
+    if (mode == 1 && a.width > cap::kMaxRetainedWidth)
+        return fail(CAP_ERR_UNSUPPORTED, "width %lld: a retained row holds at most %lld values",
+                    (long long)a.width, (long long)cap::kMaxRetainedWidth);
+    const size_t bytes = (size_t)a.rows * a.width * 4;
+    const uintptr_t x0 = (uintptr_t)a.x, y0 = (uintptr_t)a.y;
+    if (x0 != y0 && x0 < y0 + bytes && y0 < x0 + bytes)
+        return fail(CAP_ERR_INVALID_ARG, "x and y overlap without being the same buffer");
+    if (a.rows == 0) return CAP_OK;
+    uintptr_t align = x0 | y0;
+    if (a.kind == cap::kRowLayerNorm) align |= (uintptr_t)a.gamma | (uintptr_t)a.beta;
+    const bool vec4 = (a.width % 4 == 0) && (align & 15) == 0;
+    // auto: retained up to 64K values with 16-byte accesses; with 4-byte
+    // accesses only up to 16K (a wider retained row spills registers)
+    const bool retained = mode == 1 || (mode == 0 && a.width <= (vec4 ? cap::kMaxRetainedWidth : 16384));
+    const int e = cap::launch_rows(a, vec4, retained, stream);
+    if (e != 0) return fail(CAP_ERR_HIP, "row kernel launch failed: %s", cap::hip_error_string(e));
+    return CAP_OK;
+}
+
+cap_status cap_rows_softmax(const float *x, float *y, int64_t rows, int64_t width, int32_t mode,
+                            cap_stream_t stream)
+{
+    cap::RowArgs a{};
+    a.x = x;
+    a.y = y;
+    a.rows = rows;
+    a.width = width;
+    a.kind = cap::kRowSoftmax;
+    return rows_launch(a, mode, stream);
+}
+
+cap_status cap_rows_layernorm(const float *x, const float *gamma, const float *beta, float *y, int64_t rows,
+                              int64_t width, float eps, int32_t mode, cap_stream_t stream)
+{
+    if (!gamma || !beta) return fail(CAP_ERR_INVALID_ARG, "NULL gamma or beta");
+    if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(CAP_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    cap::RowArgs a{};
+    a.x = x;
+    a.gamma = gamma;
+    a.beta = beta;
+    a.y = y;
+    a.rows = rows;
+    a.width = width;
+    a.eps = eps;
+    a.kind = cap::kRowLayerNorm;
+    return rows_launch(a, mode, stream);
+}
 
 // ------------------------------------------------------------ bench helpers
 

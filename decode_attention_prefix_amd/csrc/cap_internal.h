@@ -107,12 +107,26 @@ struct AppendArgs {
     int64_t pool_pages;          // entries with a page at or past this are skipped
 };
 
-// Kernel launchers (cap_kernels.hip); return the hipError_t as int.
+// Wide-row reduction-reuse workloads (cap_rows.hip).
+constexpr int kRowSoftmax = 0, kRowLayerNorm = 1;
+constexpr int64_t kMaxRetainedWidth = 65536;   // one row in one workgroup's registers
+struct RowArgs {
+    const float *x;              // [rows][width]
+    const float *gamma, *beta;   // [width] (LayerNorm)
+    float *y;                    // [rows][width]
+    int64_t rows, width;
+    float eps;
+    int32_t kind;
+};
+
+// Kernel launchers (cap_kernels.hip, cap_aux.hip, cap_rows.hip); return the
+// hipError_t as int.
 int launch_decode(const DecodeArgs &a, int head_dim, void *stream);
 int launch_merge(const MergeArgs &a, int head_dim, void *stream);
 int launch_fill(void *buf, size_t words, uint32_t value, void *stream);
 int launch_patch(void *base, const uint32_t *patch, int n, void *stream);
 int launch_append(const AppendArgs &a, void *stream);
+int launch_rows(const RowArgs &a, bool vec4, bool retained, void *stream);
 int launch_read_stream(const void *buf, size_t vec16, void *sink, void *stream);
 int launch_read(const void *buf, size_t vec16, void *sink, void *stream);
 int launch_copy(void *dst, const void *src, size_t vec16, void *stream);

@@ -25,10 +25,15 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SRC = os.path.join(ROOT, "decode_attention_prefix_amd", "csrc", "cap_kernels.hip")
 
 
-def kernel_hash() -> str:
-    """Hash of the kernel source's code: comments and whitespace removed, so
-    an edit of the comments alone keeps counters taken on the same code."""
-    with open(KERNEL_SRC) as f:
+ROWS_SRC = os.path.join(ROOT, "decode_attention_prefix_amd", "csrc", "cap_rows.hip")
+
+
+def kernel_hash(src: str = KERNEL_SRC) -> str:
+    """Hash of a kernel source file's code (by default the attention kernels,
+    decode and merge; the growth and measurement kernels live in another
+    file): comments and whitespace removed, so an edit of the comments alone
+    keeps counters taken on the same code."""
+    with open(src) as f:
         src = f.read()
     src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
     src = re.sub(r"//[^\n]*", " ", src)
