@@ -42,8 +42,9 @@ def kernel_hash(src: str = KERNEL_SRC) -> str:
 
 
 def _short(name: str) -> str:
-    for key in ("decode_kernel", "merge_kernel", "read_stream_kernel", "read_kernel", "fill_kernel",
-                "copy_kernel", "patch_kernel", "append_kernel"):
+    for key in ("decode_kernel", "merge_kernel", "rows_retained_kernel", "rows_reread_kernel",
+                "read_stream_kernel", "read_kernel", "fill_kernel", "copy_kernel", "patch_kernel",
+                "append_kernel"):
         if key in name:
             tail = name[name.index(key):]
             return tail.split("(")[0]
@@ -70,7 +71,7 @@ def counter_means(pmc_dir: str, counter: str) -> dict[str, float]:
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
-    ap.add_argument("--config", type=int, required=True)
+    ap.add_argument("--config", type=int, default=None, help="bench.py --config (omit for --rows runs)")
     ap.add_argument("--workload", default="", help="one-line workload description")
     ap.add_argument("--kt", required=True)
     ap.add_argument("--fetch", default=None, help="omit to write the kernel-trace summary only")
@@ -82,23 +83,29 @@ def main(argv=None):
     ap.add_argument("--bench-args", default="--no-cpu-baseline")
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     ap.add_argument("--name", default="", help="summary file name (default decode_kernel_cfg<N>_kernel_trace.txt)")
+    ap.add_argument("--traffic-name", default="", help="traffic file name (default decode_kernel_cfg<N>_traffic.txt)")
+    ap.add_argument("--target", default="decode_kernel", help="kernel name prefix the traffic is taken for")
+    ap.add_argument("--src", choices=["attention", "rows"], default="attention",
+                    help="kernel source the code hash covers")
     a = ap.parse_args(argv)
     if a.fetch and a.write and a.alg_bytes <= 0:
         ap.error("--alg-bytes is needed with --fetch/--write")
-    h = kernel_hash()
+    h = kernel_hash(ROWS_SRC if a.src == "rows" else KERNEL_SRC)
     cfg = a.config
+    bench = (f"--config {cfg} " if cfg is not None else "") + a.bench_args
 
     kt = kernel_stats(a.kt)
-    lines = [f"rocprofv3 kernel-trace summary: bench.py --config {cfg} ({a.workload})",
+    lines = [f"rocprofv3 kernel-trace summary: bench.py {bench} ({a.workload})",
              f"command: cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o kt -- "
-             f"python3 <repo>/bench.py --config {cfg} {a.bench_args}",
+             f"python3 <repo>/bench.py {bench}",
              f"kernel_code_sha256_16: {h}", "",
              f"{'kernel':40s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
     for name, calls, avg, mn, mx in kt:
         lines.append(f"{name:40s} {calls:6d} {avg:9.3f} {mn:9.3f} {mx:9.3f}")
     lines += ["", "(read_kernel and fill_kernel: the bench's cache-eviction read and buffer setup; "
               "read_stream_kernel: its achievable-read probe; append_kernel and patch_kernel: "
-              "cap_append_kv and cap_plan_refresh in its growth steps)"]
+              "cap_append_kv and cap_plan_refresh in its growth steps; rows_reread_kernel, copy_kernel "
+              "and at::native kernels: the two-pass, copy and torch references of a --rows run)"]
     name = a.name or f"decode_kernel_cfg{cfg}_kernel_trace.txt"
     with open(os.path.join(a.out, name), "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -111,16 +118,17 @@ def main(argv=None):
     copy_kib = a.copy_mb * 1024.0
     fs = copy_kib / fetch["copy_kernel"]
     ws = copy_kib / write["copy_kernel"]
-    dk = [k for k in fetch if k.startswith("decode_kernel")][0]
+    dk = [k for k in fetch if k.startswith(a.target)][0]
     fb = fetch[dk] * fs * 1024.0
     wb = write[dk] * ws * 1024.0
     mk = [k for k in fetch if k.startswith("merge_kernel")]
-    lines = [f"HBM traffic of one {a.kernel} launch, bench.py --config {cfg} ({a.workload})",
+    probe = f" --copy-probe-mb {a.copy_mb}" if a.target == "decode_kernel" else ""
+    lines = [f"HBM traffic of one {a.kernel} launch, bench.py {bench} ({a.workload})",
              "commands (each its own run):",
              f"  cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out> -o pmc -- python3 "
-             f"<repo>/bench.py --config {cfg} {a.bench_args} --steps 3 --warmup 1 --copy-probe-mb {a.copy_mb}",
+             f"<repo>/bench.py {bench} --steps 3 --warmup 1{probe}",
              f"  cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out> -o pmc -- python3 "
-             f"<repo>/bench.py --config {cfg} {a.bench_args} --steps 3 --warmup 1 --copy-probe-mb {a.copy_mb}",
+             f"<repo>/bench.py {bench} --steps 3 --warmup 1{probe}",
              f"kernel_code_sha256_16: {h}",
              f"kernel: {a.kernel}",
              f"copy_kernel_{a.copy_mb}MiB_fetch_kib: {fetch['copy_kernel']:.1f}",
@@ -129,15 +137,20 @@ def main(argv=None):
              f"write_scale: {ws:.5f}",
              f"decode_fetch_kib_per_dispatch: {fetch[dk]:.1f}",
              f"decode_write_kib_per_dispatch: {write[dk]:.1f}"]
+    if a.target != "decode_kernel":
+        lines = [l.replace("decode_", "kernel_") for l in lines]
     if mk:
         lines += [f"merge_fetch_kib_per_dispatch: {fetch[mk[0]]:.1f}",
                   f"merge_write_kib_per_dispatch: {write[mk[0]]:.1f}"]
-    lines += [f"decode_fetch_bytes: {fb:.0f}",
-              f"decode_write_bytes: {wb:.0f}",
+    pre = "decode" if a.target == "decode_kernel" else "kernel"
+    lines += [f"{pre}_fetch_bytes: {fb:.0f}",
+              f"{pre}_write_bytes: {wb:.0f}",
               f"hbm_bytes_per_launch: {fb + wb:.0f}",
               f"algorithmic_bytes_per_launch: {a.alg_bytes:.0f}",
-              f"fetch_over_algorithmic: {fb / a.alg_bytes:.4f}"]
-    with open(os.path.join(a.out, f"decode_kernel_cfg{cfg}_traffic.txt"), "w") as f:
+              f"fetch_over_algorithmic: {fb / a.alg_bytes:.4f}",
+              f"hbm_over_algorithmic: {(fb + wb) / a.alg_bytes:.4f}"]
+    tname = a.traffic_name or f"decode_kernel_cfg{cfg}_traffic.txt"
+    with open(os.path.join(a.out, tname), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
