@@ -273,6 +273,8 @@ def main():
                     help="time the one-launch cap_decode_step instead of cap_decode_attention + "
                          "cap_merge_partials")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the step from a HIP graph (captured once) instead of launching it")
     ap.add_argument("--read-probe-mb", type=int, default=2048)
     ap.add_argument("--contiguous", action="store_true",
                     help="physical pages in tree order instead of a seeded permutation of the pool")
@@ -361,6 +363,8 @@ def main():
     read_gbs = probe_bytes / (min(read_ms) * 1e-3) / 1e9
     del probe
 
+    graph = dec.capture_step(fused=args.fused) if args.graph else None
+
     def one_step(evs=None):
         # events only around the whole step: an event recorded between the two
         # kernels would itself add a few microseconds of queue overhead
@@ -368,7 +372,9 @@ def main():
             evict()
         if evs is not None:
             evs[0].record(stream)
-        if args.fused:
+        if graph is not None:
+            graph.replay()
+        elif args.fused:
             dec.fused_step()
         else:
             dec.decode()
@@ -468,7 +474,8 @@ def main():
         "req_heads_per_s": round(st_tree["request_heads"] / (mean_ms * 1e-3), 1),
         "mfma_util": round(st_tree["useful_flop"] / (mean_ms * 1e-3) / 2.5e15, 5),
         "t_decode_us": {"mean": round(dec_mean * 1e3, 3), "median": round(statistics.median(dec_ms) * 1e3, 3)},
-        "step_form": "fused cap_decode_step" if fused else "cap_decode_attention + cap_merge_partials",
+        "step_form": ("fused cap_decode_step" if fused else "cap_decode_attention + cap_merge_partials")
+                     + (", replayed from a HIP graph" if args.graph else ""),
         "t_merge_us": ({"mean": round(statistics.fmean(mrg_ms) * 1e3, 3),
                         "median": round(statistics.median(mrg_ms) * 1e3, 3)} if mrg_ms else None),
         "t_step_us": {"mean": round(mean_ms * 1e3, 3), "median": round(med_ms * 1e3, 3),

@@ -126,6 +126,20 @@ class TreeDecoder:
             self.decode()
             self.merge()
 
+    def capture_step(self, fused: bool = False):
+        """Record one step (decode + merge, or the fused launch) into a HIP
+        graph through torch's stream capture and return it; replay() runs the
+        same kernels with the same buffers.  The graph holds no memset (the
+        kernels clear their own counters), and the plan buffer must stay
+        uploaded and unchanged while it is used."""
+        torch = self.torch
+        torch.cuda.synchronize(self.device)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step(fused=fused)
+        torch.cuda.synchronize(self.device)
+        return g
+
     def output_bits(self) -> np.ndarray:
         self.torch.cuda.current_stream(self.device).synchronize()
         return self.out.cpu().numpy().view(np.uint16)

@@ -211,3 +211,29 @@ def test_counters_reset_across_plans_and_steps():
                 assert np.array_equal(after, image), f"plan buffer changed by a step {opts} fused={fused}"
     finally:
         dec.close()
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_graph_replay_matches_eager(fused):
+    """The step captured in a HIP graph: every replay gives the eager bits,
+    with eager steps and host syncs between the replays."""
+    torch = _torch()
+    from decode_attention_prefix_amd.decoder import TreeDecoder
+    w, ref = config_case(0)
+    dec = TreeDecoder(w.tree, w.q, w.k_pool, w.v_pool, split_pages=2)
+    try:
+        dec.out.fill_(-1)
+        dec.step(fused=fused)
+        eager = dec.output_bits()
+        check(dec.output(), ref, f"eager fused={fused}")
+        g = dec.capture_step(fused=fused)
+        for i in range(4):
+            dec.out.fill_(-1)
+            dec.poison_workspace()
+            g.replay()
+            assert np.array_equal(dec.output_bits(), eager), f"replay {i} differs from the eager step"
+            dec.out.fill_(-1)
+            dec.step(fused=fused)
+            assert np.array_equal(dec.output_bits(), eager)
+    finally:
+        dec.close()
