@@ -112,6 +112,26 @@ def test_full_configs_forced_modes(cfg, mode):
     run_both(w, ref, f"cfg{cfg} mode={mode}", share_mode=mode)
 
 
+def test_items_at_page_limits():
+    """Unsplit runs on the long shared document: shared items of 64 pages and
+    private items of 253 pages, and with every node folded, private items of
+    the full 256 pages."""
+    from decode_attention_prefix_amd import cap
+    w, ref = config_case(3)
+    for opts, want in (({"split_pages": 100000, "tail_factor": 1e30}, {1: 64, 0: 253}),
+                       ({"split_pages": 100000, "tail_factor": 1e30, "share_mode": 0}, {0: 256})):
+        h = cap.cap_tree_upload(w.tree)
+        p = cap.cap_plan_step(h, **opts)
+        try:
+            it = cap.cap_plan_get_view(p)["items"]
+            for mode, pages in want.items():
+                assert it[it[:, 6] == mode][:, 1].max() == pages, (opts, mode)
+        finally:
+            cap.cap_plan_free(p)
+            cap.cap_tree_free(h)
+        run_both(w, ref, f"cfg3 page limits {opts}", **opts)
+
+
 @pytest.mark.parametrize("shared_rows", [1, 1 << 30])
 def test_shared_and_private_paths_full_config(shared_rows):
     """Every group on shared workgroups, or every group on private waves."""
