@@ -1032,6 +1032,7 @@ static cap_status decode_args(const cap_plan *plan, const void *q, const void *k
     a.Hq = plan->tree->attn.num_q_heads;
     a.Hkv = plan->tree->attn.num_kv_heads;
     a.G = plan->tree->G;
+    a.log2G = __builtin_ctz((unsigned)a.G);   // G is a power of two (checked with the shape)
     a.scale_log2 = (float)((double)plan->tree->attn.sm_scale * 1.4426950408889634);
     if (plan->work_queue) a.queue = reinterpret_cast<int32_t *>(static_cast<char *>(plan->dev) + plan->off_queue);
     return CAP_OK;

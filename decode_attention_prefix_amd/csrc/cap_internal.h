@@ -72,8 +72,9 @@ struct DecodeArgs {
     uint16_t *part_o;            // [slots][D] fp16: o / l (the normalised partial output)
     float *part_m;               // [slots]
     float *part_l;               // [slots]
-    int32_t n_items;
+    int32_t n_items;             // the grid never exceeds it
     int32_t Hq, Hkv, G;
+    int32_t log2G;               // G is a power of two: row / G = row >> log2G
     float scale_log2;            // sm_scale * log2(e)
     // work queues (nullptr: one workgroup per item): kQueues counters of items
     // handed out, then the count of finished workgroups, each kQueueStride

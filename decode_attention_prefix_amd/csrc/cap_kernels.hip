@@ -450,8 +450,8 @@ __device__ __forceinline__ void load_q(u32x4 (&qf)[RB][D / 32], const DecodeArgs
     for (int b = 0; b < RB; ++b) {
         const int row = row0 + 16 * b + n;
         if (row < nrows) {
-            const int req = it.req0 >= 0 ? it.req0 + row / G : a.rows[it.row_off + row / G];
-            const int h = it.head * G + row % G;
+            const int req = it.req0 >= 0 ? it.req0 + (row >> a.log2G) : a.rows[it.row_off + (row >> a.log2G)];
+            const int h = it.head * G + (row & (G - 1));
             const uint16_t *qb = a.q + ((int64_t)req * a.Hq + h) * D;
 #pragma unroll
             for (int i = 0; i < D / 32; ++i) qf[b][i] = ld16(qb + 8 * (4 * i + c));
@@ -516,7 +516,7 @@ __device__ __forceinline__ void load_slot_rows(int (&srow)[RB], const DecodeArgs
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
         const int row = row0 + 16 * b + n;
-        srow[b] = row < nrows ? a.slot_rows[it.slot_base + row / a.G] : 0;
+        srow[b] = row < nrows ? a.slot_rows[it.slot_base + (row >> a.log2G)] : 0;
     }
 }
 
@@ -537,7 +537,7 @@ __device__ __forceinline__ void write_partials(const DecodeArgs &a, const ItemRe
         const float inv = l > 0.f ? 1.0f / l : 0.f;
         const int row = row0 + 16 * b + n;
         if (row < nrows) {
-            const int64_t slot = (int64_t)srow[b] * a.Hq + it.head * G + row % G;
+            const int64_t slot = (int64_t)srow[b] * a.Hq + it.head * G + (row & (G - 1));
 #pragma unroll
             for (int j = 0; j < D / 16; ++j) store_partial_o<D, FUSED>(a, slot, 16 * j + 4 * c, o[b][j] * inv);
             if (c == 0) store_partial_ml<FUSED>(a, slot, m_ref[b], l);
@@ -653,7 +653,7 @@ __device__ __forceinline__ void private_item(const DecodeArgs &a, const ItemRegs
     }
     if (row < nrows) {
         const int G = a.G;
-        const int64_t slot = (int64_t)srow[0] * a.Hq + it.head * G + row % G;
+        const int64_t slot = (int64_t)srow[0] * a.Hq + it.head * G + (row & (G - 1));
         const float inv = L > 0.f ? 1.0f / L : 0.f;
 #pragma unroll
         for (int v = 0; v < V; v += 4)
@@ -1074,8 +1074,11 @@ void decode_kernel(DecodeArgs a)
     __shared__ __attribute__((aligned(16))) float lds[kLdsBytes / 4 + kLstInts + 2];
     int *const lst = reinterpret_cast<int *>(lds + kLdsBytes / 4);
     int *const next_item = lst + kLstInts;
+    // the grid never exceeds the item count, so the first item needs no
+    // check (and n_items no early wait)
     int cur = blockIdx.x;
-    for (int par = 0; cur < a.n_items; par ^= 1) {
+    int par = 0;
+    do {
         // the lane index is re-derived each item (opaque to the compiler), so
         // nothing lane-dependent is hoisted out of the loop to hold registers
         int tid = threadIdx.x;
@@ -1101,7 +1104,8 @@ void decode_kernel(DecodeArgs a)
         __builtin_amdgcn_s_waitcnt(0xC07F);    // lgkmcnt(0)
         asm volatile("s_barrier" ::: "memory");
         cur = __builtin_amdgcn_readfirstlane(next_item[par]);
-    }
+        par ^= 1;
+    } while (cur < a.n_items);
     if (a.queue && threadIdx.x == 0) {
         // every ticket of this workgroup has returned (the last one ended the loop)
         int *const done_ctr = a.queue + kQueues * kQueueStride;
@@ -1114,18 +1118,16 @@ void decode_kernel(DecodeArgs a)
     }
 }
 
-// Two-launch step: one one-wave workgroup per request and set of RPW =
-// 512 / D query heads (one-wave workgroups spread over every CU).
+// Two-launch step: one one-wave workgroup per request (grid x) and set of
+// RPW = 512 / D query heads (grid y); the grid is exact, so a workgroup
+// finds its request and heads without a bounds check or a division.
 template <int D>
 __global__ __launch_bounds__(kWaveSize) void merge_kernel(MergeArgs a)
 {
     constexpr int RPW = kWaveSize / (D / 8);
-    const int sets = (a.Hq + RPW - 1) / RPW;
-    const int wid = blockIdx.x;
-    if (wid >= a.R * sets) return;
     const MergeView v{a.merge_off, a.part_o, a.part_m, a.part_l, a.out, a.Hq, 0};
-    const int qh0 = (wid % sets) * RPW;
-    merge_rows<D, false>(v, wid / sets, qh0, min(RPW, a.Hq - qh0), threadIdx.x & (kWaveSize - 1));
+    const int qh0 = blockIdx.y * RPW;
+    merge_rows<D, false>(v, blockIdx.x, qh0, min(RPW, a.Hq - qh0), threadIdx.x & (kWaveSize - 1));
 }
 
 }  // namespace
@@ -1180,9 +1182,8 @@ int launch_decode(const DecodeArgs &a, int head_dim, void *stream)
 int launch_merge(const MergeArgs &a, int head_dim, void *stream)
 {
     const int rpw = kWaveSize / (head_dim / 8);
-    const int64_t waves = (int64_t)a.R * ((a.Hq + rpw - 1) / rpw);
-    if (waves <= 0) return 0;
-    const dim3 grid((unsigned)waves);
+    if (a.R <= 0 || a.Hq <= 0) return 0;
+    const dim3 grid((unsigned)a.R, (unsigned)((a.Hq + rpw - 1) / rpw));
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (head_dim == 128)
         hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kWaveSize), 0, s, a);
