@@ -24,6 +24,10 @@ FLAGS = ["--offload-arch=gfx950", "-O2", "-std=c++17", "-fPIC", "-shared", "-Wal
          # atomics stay per lane: the wave-aggregating rewrite would wait for the
          # decode kernel's work-queue ticket right where it is issued
          "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
+         # the first two argument dwords of each kernel (the decode kernel's
+         # work-item pointer) arrive in SGPRs, without a load; the code object
+         # keeps the loading prologue for firmware that does not preload
+         "-mllvm", "-amdgpu-kernarg-preload-count=2",
          "-Wl,--no-undefined",
          "-I", os.path.join(ROOT, "include")]
 

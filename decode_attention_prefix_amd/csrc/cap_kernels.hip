@@ -968,14 +968,13 @@ __device__ __forceinline__ void merge_fold(const MergeBlock<D> &b, float &M, flo
 // loads in flight while a block is folded in.  COHERENT: sc1 loads (fused
 // step, one block at a time).
 template <int D, bool COHERENT>
-__device__ __forceinline__ void merge_rows(const MergeView &v, int r, int qh0, int nh, int lane)
+__device__ __forceinline__ void merge_rows(const MergeView &v, int r, int beg, int np, int qh0, int nh, int lane)
 {
     constexpr int LPR = D / 8;                 // lanes per row
     constexpr int NB = MergeBlock<D>::NB;
     const int rho = lane / LPR, dc = lane % LPR;
     const bool active = rho < nh;
     const int qh = qh0 + (active ? rho : 0);
-    const int beg = v.merge_off[r], np = v.merge_off[r + 1] - beg;
     float M = -INFINITY, L = 0.f;
     float acc[8];
 #pragma unroll
@@ -1041,7 +1040,10 @@ __device__ __forceinline__ void finish_item(const DecodeArgs &a, const ItemRegs 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     for (int t = wave; t < nlast * sets; t += kWaves) {
         const int g0 = (t % sets) * RPW;
-        merge_rows<D, true>(v, lst[1 + t / sets], it.head * G + g0, min(RPW, G - g0), tid & (kWaveSize - 1));
+        const int r = lst[1 + t / sets];
+        const int beg = v.merge_off[r];
+        merge_rows<D, true>(v, r, beg, v.merge_off[r + 1] - beg, it.head * G + g0, min(RPW, G - g0),
+                            tid & (kWaveSize - 1));
     }
 }
 
@@ -1061,7 +1063,7 @@ __device__ __forceinline__ void finish_item(const DecodeArgs &a, const ItemRegs 
 // one shader engine, so a free slot can wait for a busy engine.
 template <int D, bool FUSED>
 __global__ __launch_bounds__(kSharedThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void decode_kernel(DecodeArgs a)
+void decode_kernel(const DevItem *items, DecodeArgs a)
 {
     constexpr int kTileBytes = kSlots * SharedTile<D>::kStep * 2;  // shared path: the LDS ring
     constexpr int kMergeBytes = (kWaves * 16 * D + 2 * kWaves * 16) * 4;   // private path: merge buffer
@@ -1074,10 +1076,14 @@ void decode_kernel(DecodeArgs a)
     __shared__ __attribute__((aligned(16))) float lds[kLdsBytes / 4 + kLstInts + 2];
     int *const lst = reinterpret_cast<int *>(lds + kLdsBytes / 4);
     int *const next_item = lst + kLstInts;
-    // the grid never exceeds the item count, so the first item needs no
-    // check (and n_items no early wait)
+    // The grid never exceeds the item count, so the first item needs no
+    // check (and n_items no early wait).  `items` comes first among the
+    // kernel arguments, which the build preloads into SGPRs: the first item's
+    // read is the workgroup's first load, in flight while the other arguments
+    // load.
     int cur = blockIdx.x;
     int par = 0;
+    ItemRegs it = read_item(items, cur, threadIdx.x & (kWaveSize - 1));
     do {
         // the lane index is re-derived each item (opaque to the compiler), so
         // nothing lane-dependent is hoisted out of the loop to hold registers
@@ -1092,7 +1098,6 @@ void decode_kernel(DecodeArgs a)
         if (a.queue && tid == 0)
             ticket = __hip_atomic_fetch_add(a.queue + (blockIdx.x % num_queues()) * kQueueStride, 1,
                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const ItemRegs it = read_item(a.items, cur, lane);
         if (FUSED && tid == 0) lst[0] = 0;     // read after the item's barriers
         if (it.mode == kModeShared)
             shared_item<D, FUSED>(a, it, reinterpret_cast<uint16_t *>(lds), tid, lane, n, c, &next_item[par], ticket);
@@ -1105,6 +1110,7 @@ void decode_kernel(DecodeArgs a)
         asm volatile("s_barrier" ::: "memory");
         cur = __builtin_amdgcn_readfirstlane(next_item[par]);
         par ^= 1;
+        if (cur < a.n_items) it = read_item(items, cur, lane);
     } while (cur < a.n_items);
     if (a.queue && threadIdx.x == 0) {
         // every ticket of this workgroup has returned (the last one ended the loop)
@@ -1120,14 +1126,18 @@ void decode_kernel(DecodeArgs a)
 
 // Two-launch step: one one-wave workgroup per request (grid x) and set of
 // RPW = 512 / D query heads (grid y); the grid is exact, so a workgroup
-// finds its request and heads without a bounds check or a division.
+// finds its request and heads without a bounds check or a division.  The
+// merge offsets come first among the arguments (preloaded into SGPRs), so
+// the request's offsets load at once.
 template <int D>
-__global__ __launch_bounds__(kWaveSize) void merge_kernel(MergeArgs a)
+__global__ __launch_bounds__(kWaveSize) void merge_kernel(const int32_t *merge_off, MergeArgs a)
 {
     constexpr int RPW = kWaveSize / (D / 8);
-    const MergeView v{a.merge_off, a.part_o, a.part_m, a.part_l, a.out, a.Hq, 0};
+    const int r = blockIdx.x;
+    const int beg = merge_off[r], np = merge_off[r + 1] - beg;     // first: no argument needed
+    const MergeView v{merge_off, a.part_o, a.part_m, a.part_l, a.out, a.Hq, 0};
     const int qh0 = blockIdx.y * RPW;
-    merge_rows<D, false>(v, blockIdx.x, qh0, min(RPW, a.Hq - qh0), threadIdx.x & (kWaveSize - 1));
+    merge_rows<D, false>(v, r, beg, np, qh0, min(RPW, a.Hq - qh0), threadIdx.x & (kWaveSize - 1));
 }
 
 }  // namespace
@@ -1167,14 +1177,14 @@ int launch_decode(const DecodeArgs &a, int head_dim, void *stream)
     const dim3 g((unsigned)grid), b(kSharedThreads);
     if (head_dim == 128) {
         if (fused)
-            hipLaunchKernelGGL((decode_kernel<128, true>), g, b, 0, s, a);
+            hipLaunchKernelGGL((decode_kernel<128, true>), g, b, 0, s, a.items, a);
         else
-            hipLaunchKernelGGL((decode_kernel<128, false>), g, b, 0, s, a);
+            hipLaunchKernelGGL((decode_kernel<128, false>), g, b, 0, s, a.items, a);
     } else {
         if (fused)
-            hipLaunchKernelGGL((decode_kernel<64, true>), g, b, 0, s, a);
+            hipLaunchKernelGGL((decode_kernel<64, true>), g, b, 0, s, a.items, a);
         else
-            hipLaunchKernelGGL((decode_kernel<64, false>), g, b, 0, s, a);
+            hipLaunchKernelGGL((decode_kernel<64, false>), g, b, 0, s, a.items, a);
     }
     return (int)hipGetLastError();
 }
@@ -1186,9 +1196,9 @@ int launch_merge(const MergeArgs &a, int head_dim, void *stream)
     const dim3 grid((unsigned)a.R, (unsigned)((a.Hq + rpw - 1) / rpw));
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (head_dim == 128)
-        hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kWaveSize), 0, s, a);
+        hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kWaveSize), 0, s, a.merge_off, a);
     else
-        hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(kWaveSize), 0, s, a);
+        hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(kWaveSize), 0, s, a.merge_off, a);
     return (int)hipGetLastError();
 }
 
