@@ -410,7 +410,7 @@ void fill_defaults(cap_plan_opts &o)
     if (o.share_mode == 2) o.share_mode = -1;
     if (o.shared_rows == 0) o.shared_rows = cap::kPrivateRows;
     if (o.num_cus == 0) o.num_cus = 256;
-    if (o.shared_cost == 0.f) o.shared_cost = 1.5f;
+    if (o.shared_cost == 0.f) o.shared_cost = 2.0f;
     if (o.rounds == 0.f) o.rounds = 1.5f;
     if (o.share_margin == 0.f) o.share_margin = 1.0f;
     if (o.order == 0) o.order = 2;

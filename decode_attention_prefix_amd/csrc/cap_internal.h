@@ -16,7 +16,7 @@ constexpr int kSharedThreads = kWaves * kWaveSize;
 constexpr int kPrivateRows = 16;     // query rows of a private (one-wave) item
 constexpr int kSharedRows = 32 * kWaves;  // query rows of a shared item: 32 per wave
 constexpr int kRowsPerItem = 32;     // the GQA group must divide this
-constexpr int kMaxSharedPages = 64;   // a shared item's waves each keep its page table, one page per lane
+constexpr int kMaxSharedPages = 128;  // a shared item's waves keep its page table in two registers, one page per lane each
 constexpr int kMaxPrivatePages = 64 * kWaves; // a private item: 64 pages per wave
 constexpr int kModePrivate = 0, kModeShared = 1;
 

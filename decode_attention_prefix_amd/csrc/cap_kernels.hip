@@ -553,6 +553,17 @@ __device__ __forceinline__ int load_page_table(const DecodeArgs &a, const ItemRe
     return lane < count ? a.stream[it.stream_off + first + lane] : 0;
 }
 
+// Page table of a shared item (up to 2 x 64 pages): entry i of the run in
+// lane i of `lo` (i < 64) or lane i - 64 of `hi`; i is uniform.
+struct PageTab {
+    int lo, hi;
+};
+
+__device__ __forceinline__ int page_entry(const PageTab &t, int i)
+{
+    return i < kWaveSize ? __builtin_amdgcn_readlane(t.lo, i) : __builtin_amdgcn_readlane(t.hi, i - kWaveSize);
+}
+
 // ---------------------------------------------------------------- private path
 // One workgroup, one item of at most 16 rows.  The waves split the item's
 // 2-page steps into contiguous sub-streams, one per wave; each streams its
@@ -690,7 +701,7 @@ struct SharedTile {
 // Global->LDS loads of step `step` into `slot`: piece k of each wave covers
 // block k * kWaves / kPPB ... (kPPB pieces per block, 4 blocks, kWaves waves).
 template <int D>
-__device__ __forceinline__ void issue_dma(const DecodeArgs &a, const ItemRegs &it, int step, int lane_e,
+__device__ __forceinline__ void issue_dma(const DecodeArgs &a, const ItemRegs &it, int step, const PageTab &pt,
                                           uint16_t *slot, int wave, int lane)
 {
     using T = SharedTile<D>;
@@ -702,8 +713,8 @@ __device__ __forceinline__ void issue_dma(const DecodeArgs &a, const ItemRegs &i
         e0 = __builtin_amdgcn_readlane(it.lane_ent, i0);
         e1 = __builtin_amdgcn_readlane(it.lane_ent, i1);
     } else {
-        e0 = __builtin_amdgcn_readlane(lane_e, i0);
-        e1 = __builtin_amdgcn_readlane(lane_e, i1);
+        e0 = page_entry(pt, i0);
+        e1 = page_entry(pt, i1);
     }
     // byte offsets of the two pages' (page, head) blocks, computed once per
     // step (the pieces below only pick one of four bases)
@@ -787,25 +798,25 @@ __device__ __forceinline__ void lds_v(u32x4 (&v)[D / 16], const uint16_t *slot, 
 // of step s - 1, which every wave finished reading before this barrier, with
 // step s + kSlots - 1.
 template <int D>
-__device__ __forceinline__ void ring_start(const DecodeArgs &a, const ItemRegs &it, int nsteps, int lane_e,
+__device__ __forceinline__ void ring_start(const DecodeArgs &a, const ItemRegs &it, int nsteps, const PageTab &pt,
                                            uint16_t *lds, int wave, int lane)
 {
 #pragma unroll
     for (int q = 0; q < kSlots; ++q)
-        if (q < nsteps) issue_dma<D>(a, it, q, lane_e, lds + q * SharedTile<D>::kStep, wave, lane);
+        if (q < nsteps) issue_dma<D>(a, it, q, pt, lds + q * SharedTile<D>::kStep, wave, lane);
     ring_barrier<SharedTile<D>::kPPB>(min(kSlots, nsteps) - 1);
 }
 
 template <int D>
-__device__ __forceinline__ void ring_next(const DecodeArgs &a, const ItemRegs &it, int nsteps, int s, int lane_e,
-                                          uint16_t *lds, int wave, int lane)
+__device__ __forceinline__ void ring_next(const DecodeArgs &a, const ItemRegs &it, int nsteps, int s,
+                                          const PageTab &pt, uint16_t *lds, int wave, int lane)
 {
     // issued so far: steps 0 .. min(nsteps, max(kSlots, s + kSlots - 1)) - 1; wait for step s + 1
     const int issued = min(nsteps, max(kSlots, s + kSlots - 1));
     ring_barrier<SharedTile<D>::kPPB>(issued - (s + 2));
     const int nxt = s + kSlots - 1;
     if (s >= 1 && nxt < nsteps)
-        issue_dma<D>(a, it, nxt, lane_e, lds + (nxt % kSlots) * SharedTile<D>::kStep, wave, lane);
+        issue_dma<D>(a, it, nxt, pt, lds + (nxt % kSlots) * SharedTile<D>::kStep, wave, lane);
 }
 
 template <int D, bool FUSED>
@@ -817,14 +828,16 @@ __device__ __forceinline__ void shared_item(const DecodeArgs &a, const ItemRegs 
     const int nrows = it.nreq * a.G;
     const int row0 = 32 * wave;
     const int nblk = nrows > row0 ? min(2, (nrows - row0 + 15) >> 4) : 0;
-    const int lane_e = load_page_table(a, it, 0, it.npages, lane);
+    PageTab pt;
+    pt.lo = load_page_table(a, it, 0, min(it.npages, kWaveSize), lane);
+    pt.hi = it.npages > kWaveSize ? load_page_table(a, it, kWaveSize, it.npages - kWaveSize, lane) : 0;
     u32x4 qf[2][D / 32];
     load_q<D, 2>(qf, a, it, row0, nrows, n, c);         // before the ring loads: loads land in order
     int srow[2];
     load_slot_rows<2>(srow, a, it, row0, nrows, n);
     const int nsteps = (it.npages + 1) >> 1;
     const int np = it.npages;
-    ring_start<D>(a, it, nsteps, lane_e, lds, wave, lane);
+    ring_start<D>(a, it, nsteps, pt, lds, wave, lane);
 
     f32x4 o[2][D / 16];
 #pragma unroll
@@ -850,10 +863,10 @@ __device__ __forceinline__ void shared_item(const DecodeArgs &a, const ItemRegs 
         // they read a stale slot; the result is unused) and the softmax and
         // PV of step s.
         auto half = [&](int s, f32x4 (&c0)[2], f32x4 (&c1)[2], f32x4 (&n0)[2], f32x4 (&n1)[2]) {
-            if (s + 1 < nsteps) ring_next<D>(a, it, nsteps, s, lane_e, lds, wave, lane);
+            if (s + 1 < nsteps) ring_next<D>(a, it, nsteps, s, pt, lds, wave, lane);
             lds_k<D>(k0, k1, lds + ((s + 1) % kSlots) * T::kStep, n, c);
-            const int nt0 = (__builtin_amdgcn_readlane(lane_e, 2 * s) & 31) + 1;
-            const int nt1 = 2 * s + 1 < np ? (__builtin_amdgcn_readlane(lane_e, 2 * s + 1) & 31) + 1 : 0;
+            const int nt0 = (page_entry(pt, 2 * s) & 31) + 1;
+            const int nt1 = 2 * s + 1 < np ? (page_entry(pt, 2 * s + 1) & 31) + 1 : 0;
             lds_v<D>(v, lds + (s % kSlots) * T::kStep, n, c);
             softmax_prepare<D>(c0, c1, v, nt0, nt1, o, m_ref, l_run, sc, c);
             qk_step<D, 2>(k0, k1, qf, n0, n1, 2);
@@ -876,7 +889,7 @@ __device__ __forceinline__ void shared_item(const DecodeArgs &a, const ItemRegs 
             if (s + 1 < nsteps) half(s + 1, sb0, sb1, sa0, sa1);
         }
     } else {
-        for (int s = 0; s + 1 < nsteps; ++s) ring_next<D>(a, it, nsteps, s, lane_e, lds, wave, lane);
+        for (int s = 0; s + 1 < nsteps; ++s) ring_next<D>(a, it, nsteps, s, pt, lds, wave, lane);
     }
     if (tid == 0) *publish = next_item_of(a, ticket);   // the ticket has long returned
     write_partials<D, 2, FUSED>(a, it, srow, row0, nrows, nblk, o, m_ref, l_run, n, c);

@@ -113,14 +113,14 @@ typedef struct cap_plan_opts {
                                  every request streams its whole context), 1 share
                                  every non-empty node, 2 auto (same as -1) */
     int32_t split_pages;      /* 0 auto; else the most KV pages one work item streams
-                                 (shared items hold at most 64, private at most 256) */
+                                 (shared items hold at most 128, private at most 256) */
     int32_t shared_rows;      /* 0 = 16: request groups with more query rows than this
                                  (requests x G) are served by shared items (KV staged in
                                  LDS for up to 128 rows); the others by private items (up
                                  to 16 rows, pages split over the 4 waves).  G > 16
                                  always uses shared items */
     int32_t num_cus;          /* 0 = 256 (MI355X); used by the cost model */
-    float shared_cost;        /* 0 = 1.5; cost of a shared item's page relative to a
+    float shared_cost;        /* 0 = 2.0; cost of a shared item's page relative to a
                                  private item's page, used to size items */
     float rounds;             /* 0 = 1.5; target work items per CU (two run at once) */
     float share_margin;       /* 0 = 1.0; share a node only if saved bytes exceed
@@ -185,7 +185,7 @@ typedef struct cap_plan cap_plan;
 /* Work item as stored in the plan (exposed for inspection and tests).  Each
  * is run by one 4-wave workgroup: a private item (mode 0) serves up to 16
  * query rows and streams up to 256 pages; a shared item (mode 1) serves up to
- * 128 rows and streams up to 64 pages. */
+ * 128 rows and streams up to 128 pages. */
 typedef struct cap_work_item {
     int32_t stream_off;   /* first entry of its page run in the plan's page stream */
     int32_t npages;       /* pages in the run */
@@ -315,7 +315,7 @@ cap_status cap_plan_upload(cap_plan *plan, void *dev_buf, size_t bytes, cap_stre
  * would choose; callers replan now and then.  Returns CAP_ERR_REPLAN, with
  * nothing changed, when a changed node has no such run (a node shared with
  * other requests, or a leaf folded into a run with others), when a run has
- * no room left (free entries, or the item's page limit: 64 shared, 256
+ * no room left (free entries, or the item's page limit: 128 shared, 256
  * private), or when the tree's shape changed (a new node).  Errors:
  * CAP_ERR_INVALID_ARG, CAP_ERR_REPLAN, CAP_ERR_HIP (the device copy is then
  * out of date and the plan counts as not uploaded). */

@@ -138,7 +138,7 @@ def check_coverage(tree, plan_handle):
     slot_rows_of = {r: set() for r in range(R)}
     srows = v["slot_rows"]
     for so, npg, head, ro, nreq, sb, mode, _ in v["items"]:
-        max_rows, max_pages = (128, 64) if mode == 1 else (16, 256)
+        max_rows, max_pages = (128, 128) if mode == 1 else (16, 256)
         assert mode in (0, 1)
         assert 1 <= npg <= max_pages and 0 <= head < Hkv and 1 <= nreq and nreq * G <= max_rows
         ents = v["stream"][so:so + npg]

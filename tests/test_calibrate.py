@@ -20,8 +20,10 @@ def test_planner_decision_is_the_closed_form(c, ell, margin):
     added = 2 * c * G * PARTIAL_ROW_BYTES
     if abs(saved - margin * added) < 0.05 * saved:
         pytest.skip("too close to the threshold")
-    t = cal.family_tree(ell, c, subtrees=8)
-    assert cal.planner_shares_roots(t, 8, c, share_margin=margin) == (saved > margin * added)
+    # 64 subtrees, as the calibration uses: enough work that a root of at
+    # most four pages stays one page run
+    t = cal.family_tree(ell, c, subtrees=64)
+    assert cal.planner_shares_roots(t, 64, c, share_margin=margin) == (saved > margin * added)
 
 
 def test_forced_modes_are_seen():

@@ -113,12 +113,12 @@ def test_full_configs_forced_modes(cfg, mode):
 
 
 def test_items_at_page_limits():
-    """Unsplit runs on the long shared document: shared items of 64 pages and
-    private items of 253 pages, and with every node folded, private items of
-    the full 256 pages."""
+    """Unsplit runs on the long shared document: shared items of 128 pages
+    (the page table in two registers) and private items of 253 pages, and
+    with every node folded, private items of the full 256 pages."""
     from decode_attention_prefix_amd import cap
     w, ref = config_case(3)
-    for opts, want in (({"split_pages": 100000, "tail_factor": 1e30}, {1: 64, 0: 253}),
+    for opts, want in (({"split_pages": 100000, "tail_factor": 1e30}, {1: 128, 0: 253}),
                        ({"split_pages": 100000, "tail_factor": 1e30, "share_mode": 0}, {0: 256})):
         h = cap.cap_tree_upload(w.tree)
         p = cap.cap_plan_step(h, **opts)
