@@ -10,9 +10,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libcap.so")
-SOURCES = [os.path.join(CSRC, "cap_host.cpp"), os.path.join(CSRC, "cap_kernels.hip"),
+SOURCES = [os.path.join(CSRC, "cap_tree.cpp"), os.path.join(CSRC, "cap_plan.cpp"),
+           os.path.join(CSRC, "cap_launch.cpp"), os.path.join(CSRC, "cap_kernels.hip"),
            os.path.join(CSRC, "cap_aux.hip"), os.path.join(CSRC, "cap_rows.hip")]
-HEADERS = [os.path.join(CSRC, "cap_internal.h"), os.path.join(ROOT, "include", "cap.h"),
+HEADERS = [os.path.join(CSRC, "cap_internal.h"), os.path.join(CSRC, "cap_host_internal.h"), os.path.join(ROOT, "include", "cap.h"),
            os.path.join(ROOT, "include", "cap_bench.h"), os.path.join(ROOT, "include", "cap_rows.h")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # -O2, not -O3: with this compiler (ROCm 7.2 clang) -O3 corrupts the o
