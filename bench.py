@@ -276,6 +276,9 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="replay the step from a HIP graph (captured once) instead of launching it")
     ap.add_argument("--read-probe-mb", type=int, default=2048)
+    ap.add_argument("--tp-share", type=int, default=1,
+                    help="keep 1/N of the query and KV heads (same tree): one GPU's share of an "
+                         "N-way split by KV head")
     ap.add_argument("--contiguous", action="store_true",
                     help="physical pages in tree order instead of a seeded permutation of the pool")
     ap.add_argument("--growth-steps", type=int, default=16,
@@ -317,7 +320,8 @@ def main():
     R_cfg = {0: 4, 1: 64, 2: 128, 3: 32, 4: 256}[args.config]
     extra_pages = R_cfg * (growth // 16 + 3) if growth else 0
     w = wl.make_config(args.config, seed=args.seed, tail_fill="zero", keep_tokens=args.control,
-                       extra_pool_pages=extra_pages, permute_pages=not args.contiguous)
+                       extra_pool_pages=extra_pages, permute_pages=not args.contiguous,
+                       heads_divisor=args.tp_share)
     if args.control:
         w = wl.control_workload(w, tail_fill="zero")
     st_tree = wl.tree_stats(w.tree)
@@ -436,7 +440,7 @@ def main():
     alg_bytes_decode = uniq + st_tree["q_bytes"] + (st_tree["out_bytes"] if fused else 0)
     achieved = alg_bytes_decode / (dec_mean * 1e-3) / 1e9
     kernel_name = f"decode_kernel<{w.tree.head_dim}, {'true' if fused else 'false'}>"
-    traffic = load_traffic(args.config, kernel_name) if not args.control else None
+    traffic = load_traffic(args.config, kernel_name) if not args.control and args.tp_share == 1 else None
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -457,6 +461,8 @@ def main():
             "kv_heads": w.tree.num_kv_heads, "head_dim": w.tree.head_dim, "page_size": 16,
             "seed": args.seed, "nodes": w.tree.num_nodes,
             "pages": "tree order" if args.contiguous else "seeded permutation of the pool",
+            **({"heads_share": f"1/{args.tp_share} of the heads (one GPU of a {args.tp_share}-way KV-head split)"}
+               if args.tp_share != 1 else {}),
         },
         "roofline": {
             "bound": "hbm",

@@ -307,14 +307,19 @@ def pack_pools(tree: Tree, kt: np.ndarray, vt: np.ndarray, tok_offs: np.ndarray,
 
 def make_config(cfg: int, seed: int = 0, tail_fill: str = "nan",
                 keep_tokens: bool = True, permute_pages: bool = True,
-                extra_pool_pages: int = 0) -> Workload:
+                extra_pool_pages: int = 0, heads_divisor: int = 1) -> Workload:
     """The five seeded shapes.  RNG = default_rng([seed, cfg]); draw order:
     tree structure, then Q, then K, then V; physical pages are a permutation.
     ``extra_pool_pages`` free pages (filled like unused slots) are appended to
     the pools afterwards, for decode steps that grow the tree; the draws do
-    not depend on it."""
+    not depend on it.  ``heads_divisor`` = N keeps 1/N of the query and KV
+    heads (same tree): one GPU's share when the heads are split over N GPUs."""
     rng = np.random.default_rng([seed, cfg])
     nt, par, paths, Hq, Hkv, D = _config_shape(cfg, rng)
+    if heads_divisor != 1:
+        if Hkv % heads_divisor:
+            raise ValueError(f"{Hkv} KV heads do not split {heads_divisor} ways")
+        Hq, Hkv = Hq // heads_divisor, Hkv // heads_divisor
     w = make_workload(nt, par, paths, Hq, Hkv, D, rng, permute_pages=permute_pages,
                       tail_fill=tail_fill, keep_tokens=keep_tokens)
     if extra_pool_pages > 0:

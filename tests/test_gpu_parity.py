@@ -132,6 +132,15 @@ def test_items_at_page_limits():
         run_both(w, ref, f"cfg3 page limits {opts}", **opts)
 
 
+def test_one_gpu_share_of_a_kv_head_split():
+    """The long shared document with 1/8 of its heads (Hq = 8, Hkv = 1, same
+    tree): one GPU's share of an 8-way split by KV head."""
+    w = wl.make_config(3, heads_divisor=8, keep_tokens=False)
+    assert (w.tree.num_q_heads, w.tree.num_kv_heads) == (8, 1)
+    ref = oracle.decode(w.tree, w.q, w.k_pool, w.v_pool)
+    run_both(w, ref, "cfg3 heads/8")
+
+
 @pytest.mark.parametrize("shared_rows", [1, 1 << 30])
 def test_shared_and_private_paths_full_config(shared_rows):
     """Every group on shared workgroups, or every group on private waves."""
