@@ -353,13 +353,16 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
         double remaining = 0;
         for (const Task &tk : tasks) remaining += tk.cost;
         const double slots = 2.0 * o.num_cus / std::max(1, Hkv);   // task slots: Hkv items each
+        // when every task already starts in the first round, a cut cannot
+        // shorten the step: it only adds an item and a partial row
+        const bool cut = (double)tasks.size() > slots;
         while (!heap.empty()) {
             std::pop_heap(heap.begin(), heap.end(), less);
             Task tk = heap.back();
             heap.pop_back();
             const double cap_cost = remaining / (slots * o.tail_factor);
             const int32_t cap_pages = std::max<int32_t>(o.tail_min_pages, (int32_t)(cap_cost / pl.page_cost(false)));
-            if (!tk.shared && tk.np > cap_pages + o.tail_min_pages) {
+            if (cut && !tk.shared && tk.np > cap_pages + o.tail_min_pages) {
                 Task rest = tk;
                 tk.np = cap_pages;
                 tk.cost = tk.np * pl.page_cost(false);
