@@ -344,8 +344,13 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
 
+    uniq = st_tree["unique_kv_bytes"]
+    fused = args.fused
+    # the fused launch also writes the bf16 output
+    alg_bytes_decode = uniq + st_tree["q_bytes"] + (st_tree["out_bytes"] if fused else 0)
+
     # achievable HBM read rate (plain streaming read of a buffer >> caches)
-    probe_bytes = args.read_probe_mb << 20
+    probe_bytes = max(args.read_probe_mb << 20, (alg_bytes_decode + 15) // 16 * 16)
     probe = torch.empty(probe_bytes, dtype=torch.uint8, device=dev)
     sink = torch.empty(8192, dtype=torch.int32, device=dev)
     flush = torch.empty(max(args.flush_mb, 1) << 20, dtype=torch.uint8, device=dev)
@@ -365,6 +370,21 @@ def main():
         b.synchronize()
         read_ms.append(a.elapsed_time(b))
     read_gbs = probe_bytes / (min(read_ms) * 1e-3) / 1e9
+    # the same plain read of only the decode launch's algorithmic bytes, timed
+    # like that launch (caches evicted, events around the one launch): what a
+    # kernel that does nothing but stream those bytes reaches at this size,
+    # launch latency, ramp-up and drain included
+    sm_bytes = (alg_bytes_decode + 15) // 16 * 16
+    sm_ms = []
+    for _ in range(max(args.steps, 5)):
+        evict()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        cap.cap_bench_read_stream(probe.data_ptr(), sm_bytes, sink.data_ptr(), sp)
+        b.record(stream)
+        b.synchronize()
+        sm_ms.append(a.elapsed_time(b))
+    sm_mean = statistics.fmean(sm_ms)
     del probe
 
     graph = dec.capture_step(fused=args.fused) if args.graph else None
@@ -432,12 +452,8 @@ def main():
         torch.cuda.synchronize(dev)
         mrg_ms = [e[0].elapsed_time(e[1]) for e in mev]
 
-    uniq = st_tree["unique_kv_bytes"]
     value = uniq / (mean_ms * 1e-3) / 1e9
     dec_mean = statistics.fmean(dec_ms)
-    fused = args.fused
-    # the fused launch also writes the bf16 output
-    alg_bytes_decode = uniq + st_tree["q_bytes"] + (st_tree["out_bytes"] if fused else 0)
     achieved = alg_bytes_decode / (dec_mean * 1e-3) / 1e9
     kernel_name = f"decode_kernel<{w.tree.head_dim}, {'true' if fused else 'false'}>"
     traffic = load_traffic(args.config, kernel_name) if not args.control and args.tp_share == 1 else None
@@ -489,6 +505,9 @@ def main():
         "value_median_step": round(uniq / (med_ms * 1e-3) / 1e9, 2),
         "wall_ms_per_step_incl_flush": round(wall_s * 1e3 / args.steps, 4),
         "read_roofline_gbs": round(read_gbs, 1),
+        "size_matched_read": {"bytes": sm_bytes, "us_mean": round(sm_mean * 1e3, 3),
+                              "gbs": round(sm_bytes / (sm_mean * 1e-3) / 1e9, 1),
+                              "decode_over_read": round(dec_mean / sm_mean, 4)},
         "bytes": {"unique_kv": uniq, "unshared_kv": st_tree["unshared_kv_bytes"],
                   "kv_streamed_by_items": plan["kv_bytes_streamed"],
                   "partial": plan["partial_bytes"], "q": st_tree["q_bytes"], "out": st_tree["out_bytes"]},
