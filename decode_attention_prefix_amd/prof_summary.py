@@ -103,7 +103,7 @@ def main(argv=None):
     for name, calls, avg, mn, mx in kt:
         lines.append(f"{name:40s} {calls:6d} {avg:9.3f} {mn:9.3f} {mx:9.3f}")
     lines += ["", "(read_kernel and fill_kernel: the bench's cache-eviction read and buffer setup; "
-              "read_stream_kernel: its achievable-read probe; append_kernel and patch_kernel: "
+              "read_stream_kernel: its plain-read probes (2 GiB, and the decode launch's own bytes); append_kernel and patch_kernel: "
               "cap_append_kv and cap_plan_refresh in its growth steps; rows_reread_kernel, copy_kernel "
               "and at::native kernels: the two-pass, copy and torch references of a --rows run)"]
     name = a.name or f"decode_kernel_cfg{cfg}_kernel_trace.txt"
