@@ -33,6 +33,7 @@ from decode_attention_prefix_amd.prof_summary import kernel_hash  # noqa: E402
 METRIC = "decode attn unique-KV HBM GB/s (% of peak) + request-heads/s per step, 1 GPU"
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel_cfg{cfg}_traffic.txt")
+TRACE_FILE = os.path.join(ROOT, "profiles", "decode_kernel_cfg{cfg}_kernel_trace.txt")
 
 
 def load_traffic(cfg: int, kernel: str):
@@ -53,6 +54,25 @@ def load_traffic(cfg: int, kernel: str):
         return float(kv["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def load_trace_us(cfg: int, kernel: str):
+    """Average duration (us) of the decode kernel in a committed rocprofv3
+    --kernel-trace --stats summary, if it was taken on the current kernel
+    source; else None."""
+    path = TRACE_FILE.format(cfg=cfg)
+    if not os.path.exists(path):
+        return None
+    h = None
+    for line in open(path):
+        if line.startswith("kernel_code_sha256_16:"):
+            h = line.split(":", 1)[1].strip()
+        elif line.startswith(kernel) and h == kernel_hash():
+            try:
+                return float(line[len(kernel):].split()[1])
+            except (IndexError, ValueError):
+                return None
+    return None
 
 
 def cpu_model() -> str:
@@ -456,7 +476,12 @@ def main():
     dec_mean = statistics.fmean(dec_ms)
     achieved = alg_bytes_decode / (dec_mean * 1e-3) / 1e9
     kernel_name = f"decode_kernel<{w.tree.head_dim}, {'true' if fused else 'false'}>"
-    traffic = load_traffic(args.config, kernel_name) if not args.control and args.tp_share == 1 else None
+    # the committed profiles were taken with the default plan of the same workload
+    profiled = (not args.control and args.tp_share == 1 and not args.contiguous and args.seed == 0
+                and args.share == -1 and not args.split_pages and not args.shared_rows and not args.rounds
+                and not args.order and not args.shared_cost and not args.share_margin and not args.dispatch)
+    traffic = load_traffic(args.config, kernel_name) if profiled else None
+    trace_us = load_trace_us(args.config, kernel_name) if profiled else None
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -490,6 +515,12 @@ def main():
             "kernel": kernel_name,
             "algorithmic_bytes_per_launch": alg_bytes_decode,
             "decode_us_mean": round(dec_mean * 1e3, 3),
+            # the same kernel's average in the committed rocprofv3 kernel trace
+            # (start to end of the kernel, without the dispatch latency that
+            # the events above include), and the fraction it gives
+            "trace_avg_us": trace_us,
+            "frac_by_trace": (round(alg_bytes_decode / (trace_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+                              if trace_us else None),
         },
         "pct_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
         "pct_measured_read_roofline": round(100 * value / read_gbs, 2),

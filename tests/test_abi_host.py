@@ -166,9 +166,9 @@ def check_coverage(tree, plan_handle):
 @pytest.mark.parametrize("share_mode", [-1, 0, 1])
 @pytest.mark.parametrize("split_pages", [0, 1, 3, 64, 600])
 def test_planner_coverage_random_trees(share_mode, split_pages):
-    for seed in range(8):
+    for seed in range(12):
         rng = np.random.default_rng(seed)
-        Hq, Hkv = [(8, 2), (32, 8), (32, 1), (4, 4)][seed % 4]
+        Hq, Hkv = [(8, 2), (32, 8), (32, 1), (4, 4), (4, 2), (16, 1)][seed % 6]
         nt, par, paths = wl.make_random_tree(rng, num_requests=int(rng.integers(1, 80)), max_depth=4,
                                              max_len=90, num_q_heads=Hq, num_kv_heads=Hkv,
                                              head_dim=64, internal_end_prob=0.3,

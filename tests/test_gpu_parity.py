@@ -149,7 +149,7 @@ def test_shared_and_private_paths_full_config(shared_rows):
 
 
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("HqHkv", [(8, 8), (8, 2), (32, 8), (16, 2), (32, 1)])
+@pytest.mark.parametrize("HqHkv", [(8, 8), (4, 2), (8, 2), (32, 8), (16, 2), (16, 1), (32, 1)])
 def test_random_small_trees(D, HqHkv):
     Hq, Hkv = HqHkv
     for seed in range(4):
