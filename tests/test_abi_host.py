@@ -213,3 +213,48 @@ def test_planner_coverage_configs(cfg):
                 cap.cap_plan_free(p)
     finally:
         cap.cap_tree_free(h)
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("tail", [(3.0, 16), (1.0, 16), (8.0, 4)])
+def test_cuts_keep_shared_runs_whole_and_pieces_above_the_minimum(cfg, tail):
+    """The scheduler cuts private runs only, never below tail_min_pages; with
+    the cuts switched off every run is whole, so the cut plan has the same
+    shared items and no more pieces per private run than its pages allow."""
+    tf, tmin = tail
+    rng = np.random.default_rng([0, cfg])
+    nt, par, paths, Hq, Hkv, D = wl._config_shape(cfg, rng)
+    t = wl.tree_from_lengths(nt, par, paths, Hq, Hkv, D, page_perm_rng=rng)
+    h = cap.cap_tree_upload(t)
+    try:
+        whole = cap.cap_plan_step(h, tail_factor=1e31)
+        cut = cap.cap_plan_step(h, tail_factor=tf, tail_min_pages=tmin)
+        try:
+            vw, vc = cap.cap_plan_get_view(whole), cap.cap_plan_get_view(cut)
+            iw, ic = vw["items"], vc["items"]
+            # shared items: identical (page run, row range) multisets per head
+            def shared(items, v):
+                return sorted((int(it[1]), tuple(v["rows"][it[3]:it[3] + it[4]]), int(it[2]))
+                              for it in items if it[6] == 1)
+            assert shared(iw, vw) == shared(ic, vc)
+            # private runs of the uncut plan, by (request rows, head): their lengths
+            runs = {}
+            for it in iw:
+                if it[6] == 0:
+                    key = (tuple(vw["rows"][it[3]:it[3] + it[4]]), int(it[2]))
+                    runs.setdefault(key, []).append(int(it[1]))
+            pieces = {}
+            for it in ic:
+                if it[6] == 0:
+                    key = (tuple(vc["rows"][it[3]:it[3] + it[4]]), int(it[2]))
+                    pieces.setdefault(key, []).append(int(it[1]))
+            assert set(pieces) == set(runs)
+            for key, ps in pieces.items():
+                assert sum(ps) == sum(runs[key])
+                if len(ps) > len(runs[key]):          # cut: no piece below the minimum
+                    assert min(ps) >= min(tmin, min(runs[key]))
+        finally:
+            cap.cap_plan_free(whole)
+            cap.cap_plan_free(cut)
+    finally:
+        cap.cap_tree_free(h)
