@@ -824,6 +824,10 @@ __device__ __forceinline__ void shared_item(const DecodeArgs &a, const ItemRegs 
                                             int lane, int n, int c, int *publish, int ticket)
 {
     using T = SharedTile<D>;
+    // A shared item's waves share each SIMD with a private item's wave, which
+    // mostly waits on memory; their step (MFMA and softmax for up to 128
+    // rows) sets the pace of the whole item, so they issue first.
+    __builtin_amdgcn_s_setprio(1);
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nrows = it.nreq * a.G;
     const int row0 = 32 * wave;
@@ -893,6 +897,7 @@ __device__ __forceinline__ void shared_item(const DecodeArgs &a, const ItemRegs 
     }
     if (tid == 0) *publish = next_item_of(a, ticket);   // the ticket has long returned
     write_partials<D, 2, FUSED>(a, it, srow, row0, nrows, nblk, o, m_ref, l_run, n, c);
+    __builtin_amdgcn_s_setprio(0);
 }
 
 // ------------------------------------------------------------------ merge
