@@ -29,7 +29,7 @@ EXPORTED = [
     "cap_plan_get_view", "cap_plan_upload", "cap_decode_attention", "cap_merge_partials",
     "cap_decode_step", "cap_plan_free", "cap_tree_get_desc", "cap_tree_append", "cap_append_kv",
     "cap_plan_refresh", "cap_bench_fill", "cap_bench_read", "cap_bench_read_stream", "cap_bench_copy",
-    "cap_rows_softmax", "cap_rows_layernorm",
+    "cap_bench_decode_timed", "cap_rows_softmax", "cap_rows_layernorm",
 ]
 
 
@@ -129,12 +129,13 @@ def lib():
         L.cap_bench_read.argtypes = [vp, sz, vp, vp]
         L.cap_bench_read_stream.argtypes = [vp, sz, vp, vp]
         L.cap_bench_copy.argtypes = [vp, vp, sz, vp]
+        L.cap_bench_decode_timed.argtypes = [vp, vp, vp, vp, vp, sz, vp, ctypes.POINTER(ctypes.c_float)]
         for name in ("cap_tree_device_bytes", "cap_tree_upload", "cap_plan_step",
                      "cap_plan_get_stats", "cap_plan_get_view", "cap_plan_upload",
                      "cap_decode_attention", "cap_merge_partials", "cap_decode_step", "cap_tree_get_desc",
                      "cap_tree_append", "cap_append_kv", "cap_plan_refresh", "cap_rows_softmax",
                      "cap_rows_layernorm", "cap_bench_fill",
-                     "cap_bench_read", "cap_bench_read_stream", "cap_bench_copy"):
+                     "cap_bench_read", "cap_bench_read_stream", "cap_bench_copy", "cap_bench_decode_timed"):
             getattr(L, name).restype = st
         _lib = L
     return _lib
@@ -288,6 +289,18 @@ def cap_plan_get_view(plan: int) -> dict:
 def cap_plan_upload(plan: int, dev_buf: int, nbytes: int, stream: int = 0) -> None:
     _check(lib().cap_plan_upload(ctypes.c_void_p(plan), ctypes.c_void_p(dev_buf), nbytes,
                                  ctypes.c_void_p(stream or None)))
+
+
+def cap_bench_decode_timed(plan: int, q: int, k_pool: int, v_pool: int, workspace: int,
+                           ws_bytes: int, stream: int = 0) -> float:
+    """cap_decode_attention timed by events bound to its dispatch; returns the
+    kernel's execution time in microseconds (blocks until it ends)."""
+    us = ctypes.c_float(0.0)
+    _check(lib().cap_bench_decode_timed(ctypes.c_void_p(plan), ctypes.c_void_p(q),
+                                        ctypes.c_void_p(k_pool), ctypes.c_void_p(v_pool),
+                                        ctypes.c_void_p(workspace), ws_bytes,
+                                        ctypes.c_void_p(stream or None), ctypes.byref(us)))
+    return float(us.value)
 
 
 def cap_decode_attention(plan: int, q: int, k_pool: int, v_pool: int, workspace: int,

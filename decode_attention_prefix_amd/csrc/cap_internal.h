@@ -122,7 +122,10 @@ struct RowArgs {
 
 // Kernel launchers (cap_kernels.hip, cap_aux.hip, cap_rows.hip); return the
 // hipError_t as int.
-int launch_decode(const DecodeArgs &a, int head_dim, void *stream);
+// ev_start / ev_stop (hipEvent_t, or null): events bound to the launch's own
+// dispatch (hipExtLaunchKernel), which time the kernel's execution alone
+int launch_decode(const DecodeArgs &a, int head_dim, void *stream, void *ev_start = nullptr,
+                  void *ev_stop = nullptr);
 int launch_merge(const MergeArgs &a, int head_dim, void *stream);
 int launch_fill(void *buf, size_t words, uint32_t value, void *stream);
 int launch_patch(void *base, const uint32_t *patch, int n, void *stream);

@@ -33,6 +33,7 @@
 // (request, head) with log-sum-exp rescaling -- the partial-result
 // combination of the project page's second paragraph, through global
 // memory/L2 because CDNA4 has no cross-CU shared memory.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -1179,7 +1180,7 @@ static int device_cus(int *cus)
     return 0;
 }
 
-int launch_decode(const DecodeArgs &a, int head_dim, void *stream)
+int launch_decode(const DecodeArgs &a, int head_dim, void *stream, void *ev_start, void *ev_stop)
 {
     if (a.n_items <= 0) return 0;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -1193,17 +1194,13 @@ int launch_decode(const DecodeArgs &a, int head_dim, void *stream)
         grid = std::min(a.n_items, 2 * cus);
     }
     const dim3 g((unsigned)grid), b(kSharedThreads);
-    if (head_dim == 128) {
-        if (fused)
-            hipLaunchKernelGGL((decode_kernel<128, true>), g, b, 0, s, a.items, a);
-        else
-            hipLaunchKernelGGL((decode_kernel<128, false>), g, b, 0, s, a.items, a);
-    } else {
-        if (fused)
-            hipLaunchKernelGGL((decode_kernel<64, true>), g, b, 0, s, a.items, a);
-        else
-            hipLaunchKernelGGL((decode_kernel<64, false>), g, b, 0, s, a.items, a);
-    }
+    hipEvent_t e0 = reinterpret_cast<hipEvent_t>(ev_start), e1 = reinterpret_cast<hipEvent_t>(ev_stop);
+    auto k = head_dim == 128 ? (fused ? decode_kernel<128, true> : decode_kernel<128, false>)
+                             : (fused ? decode_kernel<64, true> : decode_kernel<64, false>);
+    if (e0 || e1)
+        hipExtLaunchKernelGGL(k, g, b, 0, s, e0, e1, 0, a.items, a);
+    else
+        hipLaunchKernelGGL(k, g, b, 0, s, a.items, a);
     return (int)hipGetLastError();
 }
 

@@ -103,6 +103,28 @@ cap_status cap_decode_attention(const cap_plan *plan, const void *q, const void 
     return CAP_OK;
 }
 
+cap_status cap_bench_decode_timed(const cap_plan *plan, const void *q, const void *k_pool, const void *v_pool,
+                                  void *workspace, size_t ws_bytes, cap_stream_t stream, float *us)
+{
+    if (!us) return fail(CAP_ERR_INVALID_ARG, "NULL argument");
+    cap::DecodeArgs a;
+    cap_status st = decode_args(plan, q, k_pool, v_pool, workspace, ws_bytes, a);
+    if (st != CAP_OK) return st;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    hipError_t he = hipEventCreate(&e0);
+    if (he == hipSuccess) he = hipEventCreate(&e1);
+    int e = he == hipSuccess ? cap::launch_decode(a, plan->tree->attn.head_dim, stream, e0, e1) : 0;
+    if (he == hipSuccess && e == 0) he = hipEventSynchronize(e1);
+    float ms = 0.f;
+    if (he == hipSuccess && e == 0) he = hipEventElapsedTime(&ms, e0, e1);
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    if (e != 0) return fail(CAP_ERR_HIP, "decode launch failed: %s", cap::hip_error_string(e));
+    if (he != hipSuccess) return fail(CAP_ERR_HIP, "timing events: %s", hipGetErrorString(he));
+    *us = ms * 1000.f;
+    return CAP_OK;
+}
+
 cap_status cap_decode_step(const cap_plan *plan, const void *q, const void *k_pool, const void *v_pool,
                            void *workspace, size_t ws_bytes, void *out, cap_stream_t stream)
 {

@@ -111,6 +111,12 @@ class TreeDecoder:
         cap.cap_decode_attention(self.plan_h, self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(),
                                  self.ws.data_ptr(), self.ws.numel() * 4, self.stream())
 
+    def decode_timed(self) -> float:
+        """decode(), timed by events bound to the kernel's dispatch (blocks);
+        returns the kernel's execution time in microseconds."""
+        return cap.cap_bench_decode_timed(self.plan_h, self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(),
+                                          self.ws.data_ptr(), self.ws.numel() * 4, self.stream())
+
     def merge(self):
         cap.cap_merge_partials(self.plan_h, self.ws.data_ptr(), self.ws.numel() * 4,
                                self.out.data_ptr(), self.stream())

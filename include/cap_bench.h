@@ -40,6 +40,18 @@ cap_status cap_bench_read_stream(const void *buf, size_t bytes, void *sink, cap_
  * for scaling FETCH_SIZE / WRITE_SIZE counters. */
 cap_status cap_bench_copy(void *dst, const void *src, size_t bytes, cap_stream_t stream);
 
+/* cap_decode_attention (same arguments, same checks and errors), launched
+ * with two HIP events bound to the kernel's own dispatch (hipExtLaunchKernel)
+ * that the call creates and destroys; it waits for the kernel and writes its
+ * execution time in microseconds to *us (from the start of the dispatch to
+ * the end of its last workgroup, without the queueing and the end-of-kernel
+ * cache flush that events recorded on the stream around a launch include:
+ * what a profiler's kernel trace reports).  Blocks the calling thread;
+ * CAP_ERR_HIP if an event call fails. */
+cap_status cap_bench_decode_timed(const cap_plan *plan, const void *q, const void *k_pool,
+                                  const void *v_pool, void *workspace, size_t ws_bytes,
+                                  cap_stream_t stream, float *us);
+
 #ifdef __cplusplus
 }
 #endif

@@ -266,3 +266,29 @@ def test_graph_replay_matches_eager(fused):
             assert np.array_equal(dec.output_bits(), eager)
     finally:
         dec.close()
+
+
+def test_dispatch_timed_decode_matches_plain_decode():
+    """cap_bench_decode_timed runs the same launch as cap_decode_attention:
+    the merged output has the same bits, and the time it reports is that of
+    a kernel that ran."""
+    _torch()
+    from decode_attention_prefix_amd.decoder import TreeDecoder
+    w, ref = config_case(1)
+    dec = TreeDecoder(w.tree, w.q, w.k_pool, w.v_pool)
+    try:
+        outs = []
+        for timed in (False, True):
+            dec.poison_workspace()
+            dec.out.fill_(-1)
+            if timed:
+                us = dec.decode_timed()
+                assert 1.0 < us < 1e5, us
+            else:
+                dec.decode()
+            dec.merge()
+            outs.append(dec.output_bits())
+        assert np.array_equal(outs[0], outs[1])
+        check(dec.output(), ref, "timed decode")
+    finally:
+        dec.close()
