@@ -16,10 +16,9 @@ SOURCES = [os.path.join(CSRC, "cap_tree.cpp"), os.path.join(CSRC, "cap_plan.cpp"
 HEADERS = [os.path.join(CSRC, "cap_internal.h"), os.path.join(CSRC, "cap_host_internal.h"), os.path.join(ROOT, "include", "cap.h"),
            os.path.join(ROOT, "include", "cap_bench.h"), os.path.join(ROOT, "include", "cap_rows.h")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-# -O2, not -O3: with this compiler (ROCm 7.2 clang) -O3 corrupts the o
-# accumulators of the one-wave decode path (garbage partials; the max/sum
-# statistics stay right), while -O2 matches the oracle on every case.
-FLAGS = ["--offload-arch=gfx950", "-O2", "-std=c++17", "-fPIC", "-shared", "-Wall",
+# -O3: the whole GPU parity suite passes at -O3 and -O2 alike, and the
+# two builds give bit-identical outputs on the four measured trees.
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
          # packed fp32 VALU ops are kept out of every kernel
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          # atomics stay per lane: the wave-aggregating rewrite would wait for the
