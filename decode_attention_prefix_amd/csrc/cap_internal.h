@@ -72,6 +72,8 @@ struct DecodeArgs {
     uint16_t *part_o;            // [slots][D] fp16: o / l (the normalised partial output)
     float *part_m;               // [slots]
     float *part_l;               // [slots]
+    float *part_w;               // [slots][D] fp32: o / l of each 4-dim group whose fp16 form is not
+                                 // finite (written only for those groups)
     int32_t n_items;             // the grid never exceeds it
     int32_t Hq, Hkv, G;
     int32_t log2G;               // G is a power of two: row / G = row >> log2G
@@ -92,6 +94,7 @@ struct MergeArgs {
     const uint16_t *part_o;      // fp16 o / l
     const float *part_m;
     const float *part_l;
+    const float *part_w;         // fp32 o / l of the groups whose fp16 form is not finite
     uint16_t *out;               // [R][Hq][D] bf16
     int32_t R, Hq;
 };

@@ -477,21 +477,38 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, int by
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
 }
 
-// Four dims d..d+3 of a partial's normalised output o / l, as fp16 (the
-// value is a convex combination of V rows, so |o / l| <= max |v| and fp16
-// keeps ~3 significant digits: far inside the output tolerance, at half the
-// bytes of fp32).
+// True when one of the fp16 values packed in `w` (two per dword) is not
+// finite (exponent field all ones: inf or NaN).
+__device__ __forceinline__ bool f16_pair_nonfinite(uint32_t w)
+{
+    return (w & 0x7C00u) == 0x7C00u || (w & 0x7C000000u) == 0x7C000000u;
+}
+
+// Four dims d..d+3 (a 4-dim group) of a partial's normalised output o / l,
+// as fp16: the value is a convex combination of V rows, so |o / l| <= max |v|,
+// and fp16 keeps ~3 significant digits, far inside the output tolerance, at
+// half the bytes of fp32.  bf16 V can exceed fp16's range (65504); a group
+// whose fp16 form is not finite is also written in fp32 to the side region
+// part_w, and the merge, which sees the same non-finite fp16 bits, reads it
+// from there.  So every value keeps fp32 range, and N(0,1)-scale inputs
+// write no extra byte.
 template <int D, bool FUSED>
 __device__ __forceinline__ void store_partial_o(const DecodeArgs &a, int64_t slot, int d, f32x4 v)
 {
     typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
     const f16x4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
     const u32x2 bits = __builtin_bit_cast(u32x2, h);
-    if constexpr (FUSED)
+    const bool wide = f16_pair_nonfinite(bits.x) || f16_pair_nonfinite(bits.y);
+    if constexpr (FUSED) {
         __builtin_amdgcn_raw_buffer_store_b64(bits, buf_rsrc(a.part_o, a.slots * D * 2),
                                               (int)(slot * D + d) * 2, 0, kCoherent);
-    else
+        if (wide)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v),
+                                                   buf_rsrc(a.part_w + slot * D, D * 4), d * 4, 0, kCoherent);
+    } else {
         *reinterpret_cast<u32x2 *>(a.part_o + slot * D + d) = bits;
+        if (wide) *reinterpret_cast<f32x4 *>(a.part_w + slot * D + d) = v;
+    }
 }
 
 template <bool FUSED>
@@ -907,6 +924,7 @@ struct MergeView {
     const int32_t *merge_off;    // [R+1]: request r's partial rows are merge_off[r] .. merge_off[r+1] - 1
     const uint16_t *part_o;      // fp16 o / l
     const float *part_m, *part_l;
+    const float *part_w;         // fp32 o / l of the 4-dim groups whose fp16 form is not finite
     uint16_t *out;               // [R][Hq][D] bf16
     int32_t Hq, slots;
 };
@@ -947,6 +965,18 @@ __device__ __forceinline__ void merge_load(MergeBlock<D> &b, const MergeView &v,
     }
 }
 
+// fp32 o / l of dims 8 dc + 4 g .. + 3 of one slot, from the side region
+// (read only for a group whose fp16 form is not finite; see store_partial_o).
+template <int D, bool COHERENT>
+__device__ __forceinline__ f32x4 merge_wide(const MergeView &v, int slot, int dc, int g)
+{
+    if constexpr (COHERENT)
+        return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+            buf_rsrc(v.part_w + (int64_t)slot * D, D * 4), (8 * dc + 4 * g) * 4, 0, kCoherent));
+    else
+        return *reinterpret_cast<const f32x4 *>(v.part_w + (int64_t)slot * D + 8 * dc + 4 * g);
+}
+
 // Fold a block into the running (M, L, acc): the reference M rises to the
 // block maximum (rescaling what is summed so far), then each partial adds
 // weight 2^(m_i - M) l_i.
@@ -971,6 +1001,41 @@ __device__ __forceinline__ void merge_fold(const MergeBlock<D> &b, float &M, flo
         L += w;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] += w * (float)h[e];
+    }
+    M = M_new;
+}
+
+// The same fold for partials that may hold groups past fp16's range (see
+// store_partial_o): such a group's values come from the fp32 side region, and
+// a partial of weight 0 is skipped (0 x inf would poison the sums).  Partials
+// of rows row0 .. of query head qh.
+template <int D, bool COHERENT>
+__device__ __forceinline__ void merge_fold_wide(const MergeBlock<D> &b, const MergeView &v, int row0, int qh,
+                                                int dc, float &M, float &L, float (&acc)[8])
+{
+    typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+    constexpr int NB = MergeBlock<D>::NB;
+    float mb = -INFINITY;
+    for (int i = 0; i < NB; ++i)
+        if (b.l[i] > 0.f) mb = fmaxf(mb, b.m[i]);
+    const float M_new = fmaxf(M, mb);
+    const float rescale = M_new == -INFINITY ? 0.f : fast_exp2(M - M_new);
+    L *= rescale;
+    for (int e = 0; e < 8; ++e) acc[e] *= rescale;
+    for (int i = 0; i < NB; ++i) {
+        const float w = b.l[i] > 0.f ? fast_exp2(b.m[i] - M_new) * b.l[i] : 0.f;
+        L += w;
+        if (w == 0.f) continue;
+        const f16x8 h = __builtin_bit_cast(f16x8, b.x[i]);
+        float x[8];
+        for (int e = 0; e < 8; ++e) x[e] = (float)h[e];
+        for (int g = 0; g < 2; ++g) {
+            if (f16_pair_nonfinite(b.x[i][2 * g]) || f16_pair_nonfinite(b.x[i][2 * g + 1])) {
+                const f32x4 f = merge_wide<D, COHERENT>(v, (row0 + i) * v.Hq + qh, dc, g);
+                for (int e = 0; e < 4; ++e) x[4 * g + e] = f[e];
+            }
+        }
+        for (int e = 0; e < 8; ++e) acc[e] += w * x[e];
     }
     M = M_new;
 }
@@ -1016,6 +1081,22 @@ __device__ __forceinline__ void merge_rows(const MergeView &v, int r, int beg, i
             merge_fold<D>(bb, M, L, acc);
         }
     }
+    // A non-finite sum means a partial group past fp16's range (stored as
+    // inf, its fp32 value in the side region; or 0 x inf): merge this lane's
+    // row again from the side region.  Never taken for N(0,1)-scale inputs.
+    bool bad = false;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bad |= (__builtin_bit_cast(uint32_t, acc[e]) & 0x7F800000u) == 0x7F800000u;
+    if (bad) {
+        M = -INFINITY;
+        L = 0.f;
+        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+        for (int k = 0; k < np; k += NB) {
+            MergeBlock<D> ba;
+            merge_load<D, COHERENT>(ba, v, beg + k, min(NB, np - k), qh, dc);
+            merge_fold_wide<D, COHERENT>(ba, v, beg + k, qh, dc, M, L, acc);
+        }
+    }
     if (active) {
         const float inv = 1.0f / L;
         u32x4 o;
@@ -1052,7 +1133,7 @@ __device__ __forceinline__ void finish_item(const DecodeArgs &a, const ItemRegs 
     __syncthreads();
     const int nlast = lst[0];
     if (nlast == 0) return;
-    const MergeView v{a.merge_off, a.part_o, a.part_m, a.part_l, a.out, a.Hq, a.slots};
+    const MergeView v{a.merge_off, a.part_o, a.part_m, a.part_l, a.part_w, a.out, a.Hq, a.slots};
     // row sets of up to RPW query heads of this KV head, one wave each
     constexpr int RPW = kWaveSize / (D / 8);
     const int G = a.G, sets = (G + RPW - 1) / RPW;
@@ -1154,7 +1235,7 @@ __global__ __launch_bounds__(kWaveSize) void merge_kernel(const int32_t *merge_o
     constexpr int RPW = kWaveSize / (D / 8);
     const int r = blockIdx.x;
     const int beg = merge_off[r], np = merge_off[r + 1] - beg;     // first: no argument needed
-    const MergeView v{merge_off, a.part_o, a.part_m, a.part_l, a.out, a.Hq, 0};
+    const MergeView v{merge_off, a.part_o, a.part_m, a.part_l, a.part_w, a.out, a.Hq, 0};
     const int qh0 = blockIdx.y * RPW;
     merge_rows<D, false>(v, r, beg, np, qh0, min(RPW, a.Hq - qh0), threadIdx.x & (kWaveSize - 1));
 }

@@ -48,18 +48,23 @@ cap_status cap_append_kv(const cap_tree *tree, const int32_t *dest, int32_t n, c
     return CAP_OK;
 }
 
+// Partial workspace: o / l [slots][D] fp16 | m [slots] | l [slots] | o / l
+// [slots][D] fp32 for the groups whose fp16 form is not finite; each region
+// starts on a 256-byte boundary.
 static cap_status split_workspace(const cap_plan *p, const void *ws, size_t ws_bytes, uint16_t **o,
-                                  float **m, float **l)
+                                  float **m, float **l, float **w)
 {
     if ((size_t)p->stats.workspace_bytes > ws_bytes || (reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)))
         return fail(CAP_ERR_WORKSPACE, "workspace: %zu bytes given, %lld needed (256-byte aligned)",
                     ws_bytes, (long long)p->stats.workspace_bytes);
     const size_t slots = (size_t)p->stats.partial_rows * p->tree->attn.num_q_heads;
     const size_t o_bytes = align_up(slots * p->tree->attn.head_dim * 2);
+    const size_t s_bytes = align_up(slots * 4);
     char *b = (char *)ws;
     *o = (uint16_t *)b;
     *m = (float *)(b + o_bytes);
-    *l = (float *)(b + o_bytes + align_up(slots * 4));
+    *l = (float *)(b + o_bytes + s_bytes);
+    *w = (float *)(b + o_bytes + 2 * s_bytes);
     return CAP_OK;
 }
 
@@ -71,7 +76,7 @@ static cap_status decode_args(const cap_plan *plan, const void *q, const void *k
     if (((uintptr_t)q | (uintptr_t)k_pool | (uintptr_t)v_pool) & 15)
         return fail(CAP_ERR_INVALID_ARG, "q, k_pool and v_pool must be 16-byte aligned");
     a = cap::DecodeArgs{};
-    cap_status st = split_workspace(plan, workspace, ws_bytes, &a.part_o, &a.part_m, &a.part_l);
+    cap_status st = split_workspace(plan, workspace, ws_bytes, &a.part_o, &a.part_m, &a.part_l, &a.part_w);
     if (st != CAP_OK) return st;
     const char *d = static_cast<const char *>(plan->dev);
     a.items = reinterpret_cast<const cap::DevItem *>(d + plan->off_items);
@@ -155,14 +160,15 @@ cap_status cap_merge_partials(const cap_plan *plan, const void *workspace, size_
     if ((uintptr_t)out & 15) return fail(CAP_ERR_INVALID_ARG, "out must be 16-byte aligned");
     cap::MergeArgs a{};
     uint16_t *o;
-    float *m, *l;
-    cap_status st = split_workspace(plan, workspace, ws_bytes, &o, &m, &l);
+    float *m, *l, *w;
+    cap_status st = split_workspace(plan, workspace, ws_bytes, &o, &m, &l, &w);
     if (st != CAP_OK) return st;
     const char *d = static_cast<const char *>(plan->dev);
     a.merge_off = reinterpret_cast<const int32_t *>(d + plan->off_moff);
     a.part_o = o;
     a.part_m = m;
     a.part_l = l;
+    a.part_w = w;
     a.out = static_cast<uint16_t *>(out);
     a.R = plan->tree->R;
     a.Hq = plan->tree->attn.num_q_heads;

@@ -439,7 +439,7 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
     s.num_groups = (int64_t)pl.groups.size();
     s.partial_rows = slot_rows;
     const size_t slots = (size_t)slot_rows * Hq;
-    s.workspace_bytes = (int64_t)(align_up(slots * D * 2) + 2 * align_up(slots * 4));
+    s.workspace_bytes = (int64_t)(align_up(slots * D * 2) + 2 * align_up(slots * 4) + align_up(slots * D * 4));
     s.plan_device_bytes = (int64_t)p->dev_bytes;
     s.tree_device_bytes = (int64_t)align_up(std::max<size_t>(tree->page_ids.size(), 1) * 4);
     const int64_t page_bytes = 2LL * cap::kPage * D * 2;   // K+V of one page, one head

@@ -325,10 +325,16 @@ cap_status cap_plan_refresh(cap_plan *plan, cap_stream_t stream);
  * all its query rows and writes (m, l, o/l) partials into `workspace`
  * (>= stats.workspace_bytes, 256-byte aligned): m the reference maximum of
  * the base-2-scaled logits (fp32), l the sum of 2^(logit - m) (fp32), o/l the
- * normalised weighted sum of V (fp16, |o/l| <= max |v|).  Layout: o/l
- * [slots][D] fp16, then m [slots], then l [slots], each region starting on a
- * 256-byte boundary; slot = partial row x Hq + query head.  q, k_pool, v_pool: device
- * pointers in the layouts above, 16-byte aligned.  Errors:
+ * normalised weighted sum of V (|o/l| <= max |v|), kept in fp16.  Layout:
+ * o/l [slots][D] fp16, then m [slots], then l [slots], then o/l [slots][D]
+ * fp32, each region starting on a 256-byte boundary; slot = partial row x Hq
+ * + query head.  The fp32 region is written only for 4-dim groups whose
+ * fp16 form is not finite (|o/l| past 65504), so bf16 V of any magnitude in
+ * the supported range keeps fp32 range while unit-scale V writes fp16 only.
+ * q, k_pool, v_pool: device pointers in the layouts above, 16-byte aligned.
+ * Supported values: finite bf16 Q, K, V with sm_scale x |q.k| < 2^120 (fp32
+ * logits) and |v| x 2^8 x (context tokens) < 2^127 (fp32 accumulators; e.g.
+ * |v| <= 1e30 for contexts of up to 2^20 tokens).  Errors:
  * CAP_ERR_INVALID_ARG, CAP_ERR_WORKSPACE, CAP_ERR_STATE (plan not uploaded),
  * CAP_ERR_HIP. */
 cap_status cap_decode_attention(const cap_plan *plan, const void *q, const void *k_pool,
