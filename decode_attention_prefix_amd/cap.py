@@ -29,7 +29,7 @@ EXPORTED = [
     "cap_plan_get_view", "cap_plan_upload", "cap_decode_attention", "cap_merge_partials",
     "cap_decode_step", "cap_plan_free", "cap_tree_get_desc", "cap_tree_append", "cap_append_kv",
     "cap_plan_refresh", "cap_bench_fill", "cap_bench_read", "cap_bench_read_stream", "cap_bench_copy",
-    "cap_bench_decode_timed", "cap_rows_softmax", "cap_rows_layernorm",
+    "cap_bench_decode_timed", "cap_rows_softmax", "cap_rows_layernorm", "cap_plan_rebuild",
 ]
 
 
@@ -110,6 +110,7 @@ def lib():
         L.cap_tree_free.argtypes = [vp]
         L.cap_tree_free.restype = None
         L.cap_plan_step.argtypes = [vp, ctypes.POINTER(PlanOpts), ctypes.POINTER(vp)]
+        L.cap_plan_rebuild.argtypes = [vp, vp, ctypes.POINTER(PlanOpts)]
         L.cap_plan_get_stats.argtypes = [vp, ctypes.POINTER(PlanStats)]
         L.cap_plan_get_view.argtypes = [vp, ctypes.POINTER(PlanView)]
         L.cap_plan_upload.argtypes = [vp, vp, sz, vp]
@@ -130,7 +131,7 @@ def lib():
         L.cap_bench_read_stream.argtypes = [vp, sz, vp, vp]
         L.cap_bench_copy.argtypes = [vp, vp, sz, vp]
         L.cap_bench_decode_timed.argtypes = [vp, vp, vp, vp, vp, sz, vp, ctypes.POINTER(ctypes.c_float)]
-        for name in ("cap_tree_device_bytes", "cap_tree_upload", "cap_plan_step",
+        for name in ("cap_tree_device_bytes", "cap_tree_upload", "cap_plan_step", "cap_plan_rebuild",
                      "cap_plan_get_stats", "cap_plan_get_view", "cap_plan_upload",
                      "cap_decode_attention", "cap_merge_partials", "cap_decode_step", "cap_tree_get_desc",
                      "cap_tree_append", "cap_append_kv", "cap_plan_refresh", "cap_rows_softmax",
@@ -260,6 +261,11 @@ def cap_plan_step(tree_handle: int, **opts) -> int:
     h = ctypes.c_void_p(None)
     _check(lib().cap_plan_step(ctypes.c_void_p(tree_handle), ctypes.byref(o), ctypes.byref(h)))
     return int(h.value)
+
+
+def cap_plan_rebuild(plan: int, tree_handle: int, **opts) -> None:
+    o = make_opts(**opts)
+    _check(lib().cap_plan_rebuild(ctypes.c_void_p(plan), ctypes.c_void_p(tree_handle), ctypes.byref(o)))
 
 
 def cap_plan_get_stats(plan: int) -> dict:

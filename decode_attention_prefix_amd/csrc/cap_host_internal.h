@@ -44,8 +44,45 @@ struct cap_tree {
     std::vector<uint64_t> owned;              // bitmap of pool pages held by a node (built on first append)
 };
 
+namespace cap {
+namespace host {
+
+// The planner's working memory, kept with a plan so that planning again into
+// the same handle (cap_plan_rebuild) reuses it instead of allocating.
+struct PlanGroup {
+    const int32_t *reqs;           // its requests (sorted ids, in the tree's node -> request tables)
+    int32_t nreq;
+    int32_t chain;                 // last entry of its node chain (links, root-first by following prev)
+    int32_t npages;
+    int32_t at;                    // node whose pages end the run
+};
+struct ChainLink {
+    int32_t node, prev;            // prev: the link of the folded node above (-1: none)
+};
+struct PlanTask {
+    int32_t so, np, ro, nr, sb;
+    bool shared;
+    double cost;
+    int32_t idx, grp;
+};
+struct PlanScratch {
+    std::vector<PlanGroup> groups;
+    std::vector<ChainLink> links;
+    std::vector<PlanTask> tasks, seq, heap;
+    std::vector<int32_t> grp_leaf, fill, nodes;
+    struct Frame {
+        int32_t node, chain;
+        int64_t prefix_tokens;
+    };
+    std::vector<Frame> frames;
+};
+
+}  // namespace host
+}  // namespace cap
+
 struct cap_plan {
     const cap_tree *tree = nullptr;
+    cap::host::PlanScratch scratch;
     cap_plan_stats stats{};
     std::vector<cap::WorkItem> items;          // one workgroup each
     std::vector<int32_t> stream;      // (physical page << 5) | (ntok - 1)

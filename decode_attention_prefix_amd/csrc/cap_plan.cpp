@@ -76,24 +76,22 @@ using namespace cap::host;
 
 namespace {
 
-struct Group {
-    std::vector<int32_t> reqs;     // sorted request ids
-    std::vector<int32_t> entries;  // page-stream entries
-    int32_t at = -1;               // node whose pages end the entries (the walk emitted it there)
-};
+using cap::host::ChainLink;
+using cap::host::PlanGroup;
+using cap::host::PlanScratch;
+using cap::host::PlanTask;
 
 struct Planner {
     const cap_tree &t;
     cap_plan_opts o;
+    PlanScratch &sc;
     int D, Hkv, G;
     int64_t head_tok_bytes;        // K+V bytes per token per KV head
     int64_t partial_row_bytes;     // partial bytes per query row (o, m, l)
     double unit = 0;               // target cost of one shared work item (cost units)
     double unit_private = 0;       // ... of one private work item
-    int max_pages = 0;             // largest page run of any item
-    std::vector<Group> groups;
 
-    Planner(const cap_tree &tree, const cap_plan_opts &opts) : t(tree), o(opts)
+    Planner(const cap_tree &tree, const cap_plan_opts &opts, PlanScratch &scratch) : t(tree), o(opts), sc(scratch)
     {
         D = t.attn.head_dim;
         Hkv = t.attn.num_kv_heads;
@@ -102,18 +100,21 @@ struct Planner {
         partial_row_bytes = 2LL * D + 8;
     }
 
-    void node_entries(int n, std::vector<int32_t> &out) const
+    int32_t node_pages(int n) const { return (int32_t)(t.page_off[n + 1] - t.page_off[n]); }
+
+    // Page-stream entries of node n appended at out: (physical page << 5) |
+    // (tokens in the page - 1); every page is full except the last.
+    int32_t *node_entries(int n, int32_t *out) const
     {
-        const int64_t np = t.page_off[n + 1] - t.page_off[n];
-        for (int64_t p = 0; p < np; ++p) {
-            const int64_t left = t.ntok[n] - p * cap::kPage;
-            const int nt = (int)std::min<int64_t>(cap::kPage, left);
-            out.push_back((int32_t)(((int64_t)t.page_ids[t.page_off[n] + p] << 5) | (nt - 1)));
-        }
+        const int32_t np = node_pages(n);
+        const int32_t *ids = t.page_ids.data() + t.page_off[n];
+        for (int32_t p = 0; p < np; ++p) out[p] = (ids[p] << 5) | (cap::kPage - 1);
+        if (np > 0) out[np - 1] = (ids[np - 1] << 5) | ((t.ntok[n] - 1) % cap::kPage);
+        return out + np;
     }
 
     // Groups wider than the threshold run as shared workgroup items (up to
-    // 256 rows each), the rest as private one-wave items (up to 16 rows).
+    // 128 rows each), the rest as private items (up to 16 rows).
     bool is_shared(int64_t nreq) const
     {
         return G > cap::kPrivateRows || nreq * G > o.shared_rows;
@@ -124,7 +125,7 @@ struct Planner {
     }
 
     // Cost of streaming `pages` pages for one item, in private-page units: a
-    // shared item also runs the MFMA/softmax work of up to 256 rows, which
+    // shared item also runs the MFMA/softmax work of up to 128 rows, which
     // makes its pages dearer (o.shared_cost).
     double page_cost(bool shared) const { return shared ? (double)o.shared_cost : 1.0; }
 
@@ -160,28 +161,52 @@ struct Planner {
         return (double)saved > (double)o.share_margin * (double)added;
     }
 
-    void emit(const int32_t *reqs, int nreq, const std::vector<int32_t> &entries, int at)
+    // Depth-first walk in node order (preorder, children in order): each node
+    // either is shared -- one group of every request below it streams its
+    // pages and those of the folded nodes above it -- or folds, and its pages
+    // ride along as a prefix of its children's runs (the requests that end at
+    // it form a group of their own).  A group keeps its node chain as links,
+    // not a copy of its pages.
+    void build_groups_once()
     {
-        if (entries.empty() || nreq == 0) return;
-        Group g;
-        g.reqs.assign(reqs, reqs + nreq);
-        g.entries = entries;
-        g.at = at;
-        groups.push_back(std::move(g));
+        sc.groups.clear();
+        sc.links.clear();
+        sc.frames.clear();
+        for (int n = t.N - 1; n >= 0; --n)
+            if (t.parent[n] == -1) sc.frames.push_back({n, -1, 0});
+        while (!sc.frames.empty()) {
+            const PlanScratch::Frame f = sc.frames.back();
+            sc.frames.pop_back();
+            const int n = f.node;
+            const int32_t link = (int32_t)sc.links.size();
+            sc.links.push_back({n, f.chain});
+            const int32_t prefix_pages = f.chain >= 0 ? chain_pages(f.chain) : 0;
+            const int32_t npages = prefix_pages + node_pages(n);
+            const int64_t tok = f.prefix_tokens + t.ntok[n];
+            const bool share = decide_share(n, f.prefix_tokens);
+            const int32_t *reqs = share ? &t.req_list[t.req_off[n]] : t.end_list.data() + t.end_off[n];
+            const int32_t nreq = share ? t.req_off[n + 1] - t.req_off[n] : t.end_off[n + 1] - t.end_off[n];
+            if (npages > 0 && nreq > 0) sc.groups.push_back({reqs, nreq, link, npages, n});
+            const std::vector<int32_t> &ch = t.children[n];
+            for (size_t i = ch.size(); i-- > 0;)
+                sc.frames.push_back(share ? PlanScratch::Frame{ch[i], -1, 0} : PlanScratch::Frame{ch[i], link, tok});
+        }
     }
 
-    void walk(int n, std::vector<int32_t> prefix, int64_t prefix_tokens)
+    int32_t chain_pages(int32_t link) const
     {
-        std::vector<int32_t> entries = std::move(prefix);
-        node_entries(n, entries);
-        const int64_t tok = prefix_tokens + t.ntok[n];
-        if (decide_share(n, prefix_tokens)) {
-            emit(&t.req_list[t.req_off[n]], t.req_off[n + 1] - t.req_off[n], entries, n);
-            for (int c : t.children[n]) walk(c, {}, 0);
-        } else {
-            emit(t.end_list.data() + t.end_off[n], t.end_off[n + 1] - t.end_off[n], entries, n);
-            for (int c : t.children[n]) walk(c, entries, tok);
-        }
+        int32_t np = 0;
+        for (; link >= 0; link = sc.links[link].prev) np += node_pages(sc.links[link].node);
+        return np;
+    }
+
+    // Page-stream entries of a group's run, root-first, appended at out.
+    int32_t *group_entries(const PlanGroup &g, int32_t *out)
+    {
+        sc.nodes.clear();
+        for (int32_t link = g.chain; link >= 0; link = sc.links[link].prev) sc.nodes.push_back(sc.links[link].node);
+        for (size_t i = sc.nodes.size(); i-- > 0;) out = node_entries(sc.nodes[i], out);
+        return out;
     }
 
     void build_groups()
@@ -190,14 +215,11 @@ struct Planner {
         // the total cost fills every CU about `rounds` times, and plan again
         // (the share/fold test depends on the split)
         for (int pass = 0; pass < 2; ++pass) {
-            groups.clear();
-            for (int n = 0; n < t.N; ++n)
-                if (t.parent[n] == -1) walk(n, {}, 0);
+            build_groups_once();
             double W = 0;   // total cost if nothing were split
-            for (const Group &g : groups) {
-                const int64_t nreq = (int64_t)g.reqs.size();
-                const int64_t rg = (nreq + reqs_per_item(nreq) - 1) / reqs_per_item(nreq);
-                W += (double)g.entries.size() * rg * Hkv * page_cost(is_shared(nreq));
+            for (const PlanGroup &g : sc.groups) {
+                const int64_t rg = (g.nreq + reqs_per_item(g.nreq) - 1) / reqs_per_item(g.nreq);
+                W += (double)g.npages * rg * Hkv * page_cost(is_shared(g.nreq));
             }
             unit = std::max(4.0, W / ((double)o.num_cus * o.rounds));
             unit_private = std::max(4.0, W / ((double)o.num_cus * o.private_rounds));
@@ -220,24 +242,8 @@ void fill_defaults(cap_plan_opts &o)
     if (o.append_slack == 0) o.append_slack = 8;
 }
 
-}  // namespace
-
-extern "C" {
-
-void cap_plan_opts_default(cap_plan_opts *opts)
+cap_status check_opts(const cap_plan_opts *opts_in, cap_plan_opts &o)
 {
-    if (!opts) return;
-    std::memset(opts, 0, sizeof *opts);
-    opts->share_mode = -1;
-    fill_defaults(*opts);
-}
-
-cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap_plan **out)
-{
-    if (!tree || !out) return fail(CAP_ERR_INVALID_ARG, "NULL argument");
-    *out = nullptr;
-    const auto t0 = std::chrono::steady_clock::now();
-    cap_plan_opts o;
     if (opts_in) o = *opts_in; else cap_plan_opts_default(&o);
     fill_defaults(o);
     if (o.share_mode < -1 || o.share_mode > 1)
@@ -253,30 +259,60 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
         return fail(CAP_ERR_INVALID_ARG, "append_slack %d not in [-1, 4096]", o.append_slack);
     if (o.append_slack == -1) o.append_slack = 0;
     if (o.order < 1 || o.order > 4) return fail(CAP_ERR_INVALID_ARG, "order %d not in {0, .., 4}", o.order);
+    return CAP_OK;
+}
 
-    cap_plan *p = new (std::nothrow) cap_plan();
-    if (!p) return fail(CAP_ERR_INVALID_ARG, "out of host memory");
+// Copy `bytes` bytes into the image at `off` and zero the rest of the region
+// up to `end` (the alignment gap before the next region).
+void put(std::vector<unsigned char> &img, size_t off, const void *src, size_t bytes, size_t end)
+{
+    if (bytes) std::memcpy(img.data() + off, src, bytes);
+    std::memset(img.data() + off + bytes, 0, end - off - bytes);
+}
+
+// The whole plan for `tree` into `p`, whose vectors keep their capacity from
+// earlier plans (nothing is allocated once they are large enough).
+void build_plan(cap_plan *p, const cap_tree *tree, const cap_plan_opts &o)
+{
+    const auto t0 = std::chrono::steady_clock::now();
+    PlanScratch &sc = p->scratch;
     p->tree = tree;
+    p->dev = nullptr;
+    p->stats = cap_plan_stats{};
     p->work_queue = o.item_dispatch == 1;
+    p->items.clear();
+    p->stream.clear();
+    p->rows.clear();
+    p->merge_off.clear();
+    p->slot_rows.clear();
+    p->patch.clear();
     const int Hkv = tree->attn.num_kv_heads, Hq = tree->attn.num_q_heads, D = tree->attn.head_dim;
-    Planner pl(*tree, o);
+    Planner pl(*tree, o, sc);
     pl.build_groups();
 
     // tasks: (page run, request subgroup); balanced splits of both.  Partial
     // slots are assigned once the dispatch sequence is fixed.
-    struct Task { int32_t so, np, ro, nr, sb; bool shared; double cost; int32_t idx, grp; };
-    std::vector<Task> tasks;
+    std::vector<PlanTask> &tasks = sc.tasks;
+    tasks.clear();
     p->leaf.assign(tree->R, cap_plan::Leaf{});
-    std::vector<int32_t> grp_leaf(pl.groups.size(), -1);   // request whose leaf run the group is
-    for (size_t gi = 0; gi < pl.groups.size(); ++gi) {
-        const Group &g = pl.groups[gi];
-        const int64_t npg = (int64_t)g.entries.size();
-        const int nreq = (int)g.reqs.size();
+    sc.grp_leaf.assign(sc.groups.size(), -1);   // request whose leaf run the group is
+    size_t stream_len = 0, rows_len = 0;
+    for (const PlanGroup &g : sc.groups) {
+        stream_len += g.npages + (g.nreq == 1 ? o.append_slack : 0);
+        rows_len += g.nreq;
+    }
+    p->stream.resize(stream_len);
+    p->rows.resize(rows_len);
+    int32_t so = 0, ro = 0;
+    for (size_t gi = 0; gi < sc.groups.size(); ++gi) {
+        const PlanGroup &g = sc.groups[gi];
+        const int64_t npg = g.npages;
+        const int nreq = g.nreq;
         const bool shared = pl.is_shared(nreq);
         const int64_t k = pl.chunks(npg, shared);
         const int rg = (nreq + pl.reqs_per_item(nreq) - 1) / pl.reqs_per_item(nreq);
-        const int32_t so0 = (int32_t)p->stream.size();
-        p->stream.insert(p->stream.end(), g.entries.begin(), g.entries.end());
+        const int32_t so0 = so;
+        so = (int32_t)(pl.group_entries(g, p->stream.data() + so) - p->stream.data());
         // a run serving one request, ending with the pages of the leaf where
         // that request's context ends and no other request's path passes,
         // can take the leaf's new pages in place: free entries follow it
@@ -287,39 +323,42 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
                 cap_plan::Leaf &lf = p->leaf[r];
                 lf.node = n;
                 lf.pages = (int32_t)(tree->page_off[n + 1] - tree->page_off[n]);
-                lf.end = (int32_t)p->stream.size();
+                lf.end = so;
                 lf.limit = lf.end + o.append_slack;
-                p->stream.insert(p->stream.end(), (size_t)o.append_slack, 0);
-                grp_leaf[gi] = r;
+                std::fill(p->stream.begin() + so, p->stream.begin() + so + o.append_slack, 0);
+                so += o.append_slack;
+                sc.grp_leaf[gi] = r;
             }
         }
-        const int32_t ro0 = (int32_t)p->rows.size();
-        p->rows.insert(p->rows.end(), g.reqs.begin(), g.reqs.end());
+        const int32_t ro0 = ro;
+        std::copy(g.reqs, g.reqs + nreq, p->rows.begin() + ro);
+        ro += nreq;
         for (int64_t ci = 0; ci < k; ++ci) {
             const int64_t pb = npg * ci / k, pe = npg * (ci + 1) / k;
             for (int ri = 0; ri < rg; ++ri) {
                 const int rb = (int)((int64_t)nreq * ri / rg), re = (int)((int64_t)nreq * (ri + 1) / rg);
-                tasks.push_back(Task{(int32_t)(so0 + pb), (int32_t)(pe - pb), ro0 + rb, re - rb, -1, shared,
-                                     (double)(pe - pb) * pl.page_cost(shared), (int32_t)tasks.size(),
-                                     (int32_t)gi});
+                tasks.push_back(PlanTask{(int32_t)(so0 + pb), (int32_t)(pe - pb), ro0 + rb, re - rb, -1, shared,
+                                         (double)(pe - pb) * pl.page_cost(shared), (int32_t)tasks.size(),
+                                         (int32_t)gi});
             }
         }
     }
+    p->stream.resize(so);
     // The hardware starts workgroups in item order as CUs free up, so a list
     // sorted costliest first is greedy longest-processing-time scheduling.
     // order 1 interleaves the two kinds evenly (each costliest first), 2 sorts
     // both kinds together, 3 puts every shared item first, 4 starts with one
     // shared and one private workgroup per CU.  One item per task and KV head,
     // the heads of a task back to back.
-    std::stable_sort(tasks.begin(), tasks.end(), [&](const Task &a, const Task &b) {
+    std::stable_sort(tasks.begin(), tasks.end(), [&](const PlanTask &a, const PlanTask &b) {
         if (o.order == 3 && a.shared != b.shared) return a.shared;
         return a.cost > b.cost;
     });
-    std::vector<Task> seq;
-    seq.reserve(tasks.size() * 2);
+    std::vector<PlanTask> &seq = sc.seq;
+    seq.clear();
     if (o.order == 1 || o.order == 4) {
-        std::vector<const Task *> sh, pr;
-        for (const Task &tk : tasks) (tk.shared ? sh : pr).push_back(&tk);
+        std::vector<const PlanTask *> sh, pr;
+        for (const PlanTask &tk : tasks) (tk.shared ? sh : pr).push_back(&tk);
         size_t i_sh = 0, i_pr = 0;
         if (o.order == 4) {
             // first wave: one shared and one private workgroup on every CU (the
@@ -345,25 +384,26 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
         // subgroups of one page run next to each other: with the heads of a
         // task back to back, their items for one KV head start Hkv apart, on
         // the same XCD when Hkv = 8, and the later ones read the run from its L2.
-        auto less = [](const Task &a, const Task &b) {
+        auto less = [](const PlanTask &a, const PlanTask &b) {
             return a.cost < b.cost || (a.cost == b.cost && a.idx > b.idx);
         };
-        std::vector<Task> heap(tasks.begin(), tasks.end());
+        std::vector<PlanTask> &heap = sc.heap;
+        heap.assign(tasks.begin(), tasks.end());
         std::make_heap(heap.begin(), heap.end(), less);
         double remaining = 0;
-        for (const Task &tk : tasks) remaining += tk.cost;
+        for (const PlanTask &tk : tasks) remaining += tk.cost;
         const double slots = 2.0 * o.num_cus / std::max(1, Hkv);   // task slots: Hkv items each
         // when every task already starts in the first round, a cut cannot
         // shorten the step: it only adds an item and a partial row
         const bool cut = (double)tasks.size() > slots;
         while (!heap.empty()) {
             std::pop_heap(heap.begin(), heap.end(), less);
-            Task tk = heap.back();
+            PlanTask tk = heap.back();
             heap.pop_back();
             const double cap_cost = remaining / (slots * o.tail_factor);
             const int32_t cap_pages = std::max<int32_t>(o.tail_min_pages, (int32_t)(cap_cost / pl.page_cost(false)));
             if (cut && !tk.shared && tk.np > cap_pages + o.tail_min_pages) {
-                Task rest = tk;
+                PlanTask rest = tk;
                 tk.np = cap_pages;
                 tk.cost = tk.np * pl.page_cost(false);
                 rest.so += cap_pages;
@@ -382,7 +422,7 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
     // merge finds them without a table; a task reaches the row of each of its
     // requests through slot_rows[sb + q], filled in dispatch order.
     p->merge_off.assign(tree->R + 1, 0);
-    for (const Task &tk : seq)
+    for (const PlanTask &tk : seq)
         for (int q = 0; q < tk.nr; ++q) ++p->merge_off[p->rows[tk.ro + q] + 1];
     int32_t maxp = 0;
     for (int r = 0; r < tree->R; ++r) {
@@ -390,16 +430,15 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
         p->merge_off[r + 1] += p->merge_off[r];
     }
     const int32_t slot_rows = p->merge_off[tree->R];
-    std::vector<int32_t> fill(p->merge_off.begin(), p->merge_off.end() - 1);
-    p->slot_rows.reserve(slot_rows);
-    for (Task &tk : seq) {
+    sc.fill.assign(p->merge_off.begin(), p->merge_off.end() - 1);
+    int32_t max_pages = 0;
+    for (PlanTask &tk : seq) {
         tk.sb = (int32_t)p->slot_rows.size();
-        for (int q = 0; q < tk.nr; ++q) p->slot_rows.push_back(fill[p->rows[tk.ro + q]]++);
-        pl.max_pages = std::max<int>(pl.max_pages, tk.np);
+        for (int q = 0; q < tk.nr; ++q) p->slot_rows.push_back(sc.fill[p->rows[tk.ro + q]]++);
+        max_pages = std::max<int32_t>(max_pages, tk.np);
     }
-    p->items.reserve(seq.size() * Hkv);
-    for (const Task &tk : seq) {
-        const int32_t r = grp_leaf[tk.grp];
+    for (const PlanTask &tk : seq) {
+        const int32_t r = sc.grp_leaf[tk.grp];
         if (r >= 0 && tk.so + tk.np == p->leaf[r].end) p->leaf[r].item0 = (int32_t)p->items.size();
         for (int h = 0; h < Hkv; ++h)
             p->items.push_back(WorkItem{tk.so, tk.np, h, tk.ro, tk.nr, tk.sb,
@@ -411,11 +450,9 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
     // device image: items | stream | rows | slot_rows | merge_off | counters |
     // queue | patch (the fused step's arrival counters, one per request and
     // KV head, and the work queues' counters, all zero; then the area that
-    // cap_plan_refresh stages its word patches in)
-    std::vector<cap::DevItem> dev_items(p->items.size());
-    for (size_t i = 0; i < p->items.size(); ++i) dev_items[i] = dev_item(*p, p->items[i]);
+    // cap_plan_refresh stages its word patches in, which is not uploaded)
     p->off_items = 0;
-    p->off_stream = align_up(dev_items.size() * sizeof(cap::DevItem));
+    p->off_stream = align_up(p->items.size() * sizeof(cap::DevItem));
     p->off_rows = p->off_stream + align_up(p->stream.size() * 4);
     p->off_srows = p->off_rows + align_up(p->rows.size() * 4);
     p->off_moff = p->off_srows + align_up(p->slot_rows.size() * 4);
@@ -424,19 +461,32 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
     p->off_patch = p->off_queue + align_up(cap::kQueueInts * 4);
     p->patch_cap = (size_t)4 * tree->R * (Hkv + 1) + 256;
     p->dev_bytes = p->off_patch + align_up(p->patch_cap * 8);
-    p->host_image.assign(p->dev_bytes, 0);
-    std::memcpy(p->host_image.data() + p->off_items, dev_items.data(), dev_items.size() * sizeof(cap::DevItem));
-    std::memcpy(p->host_image.data() + p->off_stream, p->stream.data(), p->stream.size() * 4);
-    std::memcpy(p->host_image.data() + p->off_rows, p->rows.data(), p->rows.size() * 4);
-    std::memcpy(p->host_image.data() + p->off_srows, p->slot_rows.data(), p->slot_rows.size() * 4);
-    std::memcpy(p->host_image.data() + p->off_moff, p->merge_off.data(), p->merge_off.size() * 4);
+    p->host_image.resize(p->dev_bytes);
+    {
+        // the Hkv items of a task differ only in their KV head
+        cap::DevItem *di = reinterpret_cast<cap::DevItem *>(p->host_image.data() + p->off_items);
+        for (size_t i = 0; i < p->items.size(); i += Hkv) {
+            cap::DevItem d = dev_item(*p, p->items[i]);
+            for (int h = 0; h < Hkv; ++h) {
+                d.head = h;
+                di[i + h] = d;
+            }
+        }
+        const size_t ib = p->items.size() * sizeof(cap::DevItem);
+        std::memset(p->host_image.data() + ib, 0, p->off_stream - ib);
+    }
+    put(p->host_image, p->off_stream, p->stream.data(), p->stream.size() * 4, p->off_rows);
+    put(p->host_image, p->off_rows, p->rows.data(), p->rows.size() * 4, p->off_srows);
+    put(p->host_image, p->off_srows, p->slot_rows.data(), p->slot_rows.size() * 4, p->off_moff);
+    put(p->host_image, p->off_moff, p->merge_off.data(), p->merge_off.size() * 4, p->off_cnt);
+    std::memset(p->host_image.data() + p->off_cnt, 0, p->off_patch - p->off_cnt);
 
     cap_plan_stats &s = p->stats;
     s.num_items = (int64_t)p->items.size();
     s.num_shared_items = 0;
     for (const WorkItem &w : p->items) s.num_shared_items += w.mode == cap::kModeShared;
     s.num_tasks = (int64_t)seq.size();
-    s.num_groups = (int64_t)pl.groups.size();
+    s.num_groups = (int64_t)sc.groups.size();
     s.partial_rows = slot_rows;
     const size_t slots = (size_t)slot_rows * Hq;
     s.workspace_bytes = (int64_t)(align_up(slots * D * 2) + 2 * align_up(slots * 4) + align_up(slots * D * 4));
@@ -444,15 +494,54 @@ cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap
     s.tree_device_bytes = (int64_t)align_up(std::max<size_t>(tree->page_ids.size(), 1) * 4);
     const int64_t page_bytes = 2LL * cap::kPage * D * 2;   // K+V of one page, one head
     int64_t streamed = 0;
-    for (const Task &tk : seq) streamed += (int64_t)tk.np * page_bytes * Hkv;
+    for (const PlanTask &tk : seq) streamed += (int64_t)tk.np * page_bytes * Hkv;
     s.kv_bytes_streamed = streamed;
     s.kv_bytes_unique = tree->unique_tokens * 4LL * D * Hkv;
     s.kv_bytes_unshared = tree->sum_ctx * 4LL * D * Hkv;
     s.partial_bytes = (int64_t)slots * (2LL * D + 8);
     s.max_partials_per_request = maxp;
-    s.max_pages_per_item = pl.max_pages;
+    s.max_pages_per_item = max_pages;
     s.plan_host_us = std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count();
+}
+
+}  // namespace
+
+extern "C" {
+
+void cap_plan_opts_default(cap_plan_opts *opts)
+{
+    if (!opts) return;
+    std::memset(opts, 0, sizeof *opts);
+    opts->share_mode = -1;
+    fill_defaults(*opts);
+}
+
+cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts_in, cap_plan **out)
+{
+    if (!tree || !out) return fail(CAP_ERR_INVALID_ARG, "NULL argument");
+    *out = nullptr;
+    const auto t0 = std::chrono::steady_clock::now();
+    cap_plan_opts o;
+    cap_status st = check_opts(opts_in, o);
+    if (st != CAP_OK) return st;
+    cap_plan *p = new (std::nothrow) cap_plan();
+    if (!p) return fail(CAP_ERR_INVALID_ARG, "out of host memory");
+    build_plan(p, tree, o);
+    p->stats.plan_host_us = std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count();
     *out = p;
+    return CAP_OK;
+}
+
+cap_status cap_plan_rebuild(cap_plan *plan, const cap_tree *tree, const cap_plan_opts *opts_in)
+{
+    if (!plan || !tree) return fail(CAP_ERR_INVALID_ARG, "NULL argument");
+    const auto t0 = std::chrono::steady_clock::now();
+    cap_plan_opts o;
+    cap_status st = check_opts(opts_in, o);
+    if (st != CAP_OK) return st;
+    build_plan(plan, tree, o);
+    plan->stats.plan_host_us =
+        std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count();
     return CAP_OK;
 }
 
@@ -485,7 +574,7 @@ cap_status cap_plan_upload(cap_plan *plan, void *dev_buf, size_t bytes, cap_stre
     if (bytes < plan->dev_bytes || (reinterpret_cast<uintptr_t>(dev_buf) & (kAlign - 1)))
         return fail(CAP_ERR_WORKSPACE, "plan buffer: %zu bytes given, %zu needed (256-byte aligned)",
                     bytes, plan->dev_bytes);
-    hipError_t e = hipMemcpyAsync(dev_buf, plan->host_image.data(), plan->dev_bytes,
+    hipError_t e = hipMemcpyAsync(dev_buf, plan->host_image.data(), plan->off_patch,
                                   hipMemcpyHostToDevice, reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(CAP_ERR_HIP, "plan upload copy failed: %s", hipGetErrorString(e));
     plan->dev = dev_buf;

@@ -50,6 +50,10 @@ class TreeDecoder:
         self.stats = None
         self.plan_opts = dict(plan_opts)
         self._grow_bufs = None
+        # second plan slot for replan(): handle, device buffer, and the event
+        # recorded after its last upload (the host image is that copy's source)
+        self._spare_h, self._spare_buf, self._spare_ev = 0, None, None
+        self._cur_ev = None
         self.plan(**plan_opts)
 
     def stream(self) -> int:
@@ -71,18 +75,58 @@ class TreeDecoder:
         if self.ws is None or self.ws.numel() * 4 < wb:
             self.ws = torch.empty(max(wb // 4, 64), dtype=torch.float32, device=self.device)
         cap.cap_plan_upload(self.plan_h, self.plan_buf.data_ptr(), self.plan_buf.numel(), self.stream())
+        self._cur_ev = self._record()
         return self.stats
+
+    def _record(self):
+        """Event after the copies just queued from the current plan's host
+        memory (an upload or a refresh patch): a rebuild of that handle waits
+        for it."""
+        ev = self.torch.cuda.Event()
+        ev.record(self.torch.cuda.current_stream(self.device))
+        return ev
+
+    def replan(self, **opts):
+        """Plan the tree as it stands for the next step without waiting for
+        the steps in flight: cap_plan_rebuild into the second plan slot (its
+        host memory reused), cap_plan_upload into that slot's own device
+        buffer on the stream, then the slots swap.  Steps already queued keep
+        their plan buffer; the only wait is for the spare slot's previous
+        upload, long done in a loop that plans every step."""
+        torch = self.torch
+        self.plan_opts = dict(opts)
+        if self._spare_h:
+            if self._spare_ev is not None:
+                self._spare_ev.synchronize()
+            cap.cap_plan_rebuild(self._spare_h, self.tree, **opts)
+        else:
+            self._spare_h = cap.cap_plan_step(self.tree, **opts)
+        st = cap.cap_plan_get_stats(self._spare_h)
+        pb, wb = int(st["plan_device_bytes"]), int(st["workspace_bytes"])
+        if self._spare_buf is None or self._spare_buf.numel() < pb:
+            self._spare_buf = torch.empty(pb, dtype=torch.uint8, device=self.device)
+        if self.ws.numel() * 4 < wb:
+            # stream-ordered: the old workspace is reused only after the steps queued on it
+            self.ws = torch.empty(max(wb // 4, 64), dtype=torch.float32, device=self.device)
+        cap.cap_plan_upload(self._spare_h, self._spare_buf.data_ptr(), self._spare_buf.numel(), self.stream())
+        ev = self._record()
+        self.plan_h, self._spare_h = self._spare_h, self.plan_h
+        self.plan_buf, self._spare_buf = self._spare_buf, self.plan_buf
+        self._cur_ev, self._spare_ev = ev, self._cur_ev
+        self.stats = st
+        return st
 
     def set_q(self, q: np.ndarray):
         """Next step's queries (uint16 bf16 bits [R][Hq][D])."""
         self.q.copy_(_dev_u16(self.torch, q, self.device))
 
-    def grow(self, k_new: np.ndarray, v_new: np.ndarray, new_pages=None, active=None):
+    def grow(self, k_new: np.ndarray, v_new: np.ndarray, new_pages=None, active=None, rebuild=False):
         """One decode step's new tokens (uint16 bf16 bits [R][Hkv][D]): extend
         the tree on the host (cap_tree_append), write their K/V into the pools
         (cap_append_kv) and bring the plan up to date (cap_plan_refresh, or a
-        new plan with the same options when it answers CAP_ERR_REPLAN).
-        Returns (dest, replanned)."""
+        new plan with the same options when it answers CAP_ERR_REPLAN; with
+        rebuild=True, always a new plan through replan(), as a loop that
+        plans every step does).  Returns (dest, replanned)."""
         torch = self.torch
         dest = cap.cap_tree_append(self.tree, self.R, active, new_pages)
         d = torch.from_numpy(dest).to(self.device)
@@ -91,8 +135,12 @@ class TreeDecoder:
         self._grow_bufs = (d, k, v)
         cap.cap_append_kv(self.tree, d.data_ptr(), self.R, k.data_ptr(), v.data_ptr(), self.k.data_ptr(),
                           self.v.data_ptr(), self.stream())
+        if rebuild:
+            self.replan(**self.plan_opts)
+            return dest, True
         try:
             cap.cap_plan_refresh(self.plan_h, self.stream())
+            self._cur_ev = self._record()
             replanned = False
         except cap.CapError as e:
             if e.status != cap.CAP_ERR_REPLAN:
@@ -155,11 +203,14 @@ class TreeDecoder:
         return b.view(np.float32)
 
     def close(self):
-        if self.plan_h or self.tree:
+        if self.plan_h or self._spare_h or self.tree:
             self.torch.cuda.synchronize(self.device)
         if self.plan_h:
             cap.cap_plan_free(self.plan_h)
             self.plan_h = 0
+        if self._spare_h:
+            cap.cap_plan_free(self._spare_h)
+            self._spare_h = 0
         if self.tree:
             cap.cap_tree_free(self.tree)
             self.tree = 0

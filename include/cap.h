@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define CAP_ABI_VERSION 6
+#define CAP_ABI_VERSION 7
 
 typedef enum cap_status {
     CAP_OK = 0,
@@ -284,6 +284,20 @@ cap_status cap_append_kv(const cap_tree *tree, const int32_t *dest, int32_t n, c
  * the per-request merge lists.  opts may be NULL (defaults).  The plan refers
  * to `tree`, which must outlive it.  Errors: CAP_ERR_INVALID_ARG. */
 cap_status cap_plan_step(const cap_tree *tree, const cap_plan_opts *opts, cap_plan **out);
+
+/* Plan again into an existing plan handle: the same plan cap_plan_step would
+ * build for `tree` and `opts` (the per-decoding-step cost model of the
+ * Capillary Kernels project page, second paragraph, run every step), in the
+ * handle's own host memory, so that a loop planning every step allocates
+ * nothing once the handle has held a plan of that size.  `tree` may be
+ * another tree than the plan's last one.  Host only: the plan afterwards
+ * counts as not uploaded (call cap_plan_upload).  Because cap_plan_upload
+ * copies from the plan's host memory asynchronously, the stream must have
+ * passed the plan's previous upload before this call (e.g. alternate two
+ * handles and wait for an event recorded after each one's upload).  Errors:
+ * CAP_ERR_INVALID_ARG (NULL plan or tree, bad option; the plan is then
+ * unchanged). */
+cap_status cap_plan_rebuild(cap_plan *plan, const cap_tree *tree, const cap_plan_opts *opts);
 cap_status cap_plan_get_stats(const cap_plan *plan, cap_plan_stats *stats);
 cap_status cap_plan_get_view(const cap_plan *plan, cap_plan_view *view);
 

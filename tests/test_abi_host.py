@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), f"libcap.so does not export {n}"
     assert set(cap.EXPORTED) == names
-    assert cap.cap_abi_version() == 6
+    assert cap.cap_abi_version() == 7
 
 
 def small_tree(**over):
@@ -257,4 +257,83 @@ def test_cuts_keep_shared_runs_whole_and_pieces_above_the_minimum(cfg, tail):
             cap.cap_plan_free(whole)
             cap.cap_plan_free(cut)
     finally:
+        cap.cap_tree_free(h)
+
+
+def _views_equal(a, b):
+    va, vb = cap.cap_plan_get_view(a), cap.cap_plan_get_view(b)
+    for k in ("items", "stream", "rows", "merge_off", "slot_rows"):
+        if not np.array_equal(np.asarray(va[k]), np.asarray(vb[k])):
+            return False
+    sa, sb = cap.cap_plan_get_stats(a), cap.cap_plan_get_stats(b)
+    skip = {"plan_host_us", "refresh_host_us"}
+    return all(sa[k] == sb[k] for k in sa if k not in skip)
+
+
+def test_rebuild_gives_the_fresh_plan_across_trees_and_options():
+    """cap_plan_rebuild into one handle, over a sequence of different trees
+    (larger and smaller than the handle's last plan) and options, gives
+    exactly the plan cap_plan_step builds, and that plan covers every
+    request's context once."""
+    handles = []
+    trees = []
+    for seed in range(8):
+        rng = np.random.default_rng([seed, 17])
+        Hq, Hkv = [(8, 2), (32, 8), (16, 1), (4, 4)][seed % 4]
+        nt, par, paths = wl.make_random_tree(rng, num_requests=int(rng.integers(1, 120)), max_depth=4,
+                                             max_len=int(rng.integers(20, 400)), num_q_heads=Hq,
+                                             num_kv_heads=Hkv, head_dim=128, internal_end_prob=0.3,
+                                             empty_root=bool(seed % 2), min_len=0)
+        t = wl.tree_from_lengths(nt, par, paths, Hq, Hkv, 128, page_perm_rng=rng)
+        trees.append(t)
+        handles.append(cap.cap_tree_upload(t))
+    reused = cap.cap_plan_step(handles[0])
+    try:
+        for i, opts in enumerate(({}, {"share_mode": 1, "split_pages": 2}, {"share_mode": 0},
+                                  {"shared_rows": 1, "order": 4}, {"tail_factor": 3.0}, {"item_dispatch": 1},
+                                  {"append_slack": -1}, {"rounds": 4.0, "shared_cost": 1.2})):
+            for k in (i, (i + 3) % 8, (i + 5) % 8):
+                cap.cap_plan_rebuild(reused, handles[k], **opts)
+                fresh = cap.cap_plan_step(handles[k], **opts)
+                try:
+                    assert _views_equal(reused, fresh), (k, opts)
+                    check_coverage(trees[k], reused)
+                finally:
+                    cap.cap_plan_free(fresh)
+    finally:
+        cap.cap_plan_free(reused)
+        for h in handles:
+            cap.cap_tree_free(h)
+
+
+def test_rebuild_follows_a_growing_tree_and_rejects_bad_options():
+    """Rebuilding after cap_tree_append plans the grown tree (as a fresh
+    plan would); a rejected option leaves the plan as it was."""
+    rng = np.random.default_rng(23)
+    nt, par, paths = wl.make_random_tree(rng, num_requests=30, max_depth=3, max_len=70, num_q_heads=8,
+                                         num_kv_heads=2, head_dim=64, internal_end_prob=0.2,
+                                         empty_root=False, min_len=1)
+    t = wl.tree_from_lengths(nt, par, paths, 8, 2, 64, page_perm_rng=rng, extra_pool_pages=200)
+    h = cap.cap_tree_upload(t)
+    p = cap.cap_plan_step(h)
+    try:
+        free = list(wl.free_pages(t))
+        for step in range(6):
+            cap.cap_tree_append(h, t.num_requests, None, np.asarray(free[:t.num_requests], np.int32))
+            d = cap.cap_tree_get_desc(h)
+            taken = set(int(x) for x in d["page_ids"])
+            free = [pg for pg in free if pg not in taken]
+            cap.cap_plan_rebuild(p, h)
+            fresh = cap.cap_plan_step(h)
+            try:
+                assert _views_equal(p, fresh), step
+            finally:
+                cap.cap_plan_free(fresh)
+        before = cap.cap_plan_get_view(p)["items"].copy()
+        with pytest.raises(cap.CapError) as e:
+            cap.cap_plan_rebuild(p, h, share_mode=5)
+        assert e.value.status == 1
+        assert np.array_equal(cap.cap_plan_get_view(p)["items"], before)
+    finally:
+        cap.cap_plan_free(p)
         cap.cap_tree_free(h)
