@@ -30,6 +30,7 @@ EXPORTED = [
     "cap_decode_step", "cap_plan_free", "cap_tree_get_desc", "cap_tree_append", "cap_append_kv",
     "cap_plan_refresh", "cap_bench_fill", "cap_bench_read", "cap_bench_read_stream", "cap_bench_copy",
     "cap_bench_decode_timed", "cap_rows_softmax", "cap_rows_layernorm", "cap_plan_rebuild",
+    "cap_decode_step_noalloc",
 ]
 
 
@@ -117,6 +118,7 @@ def lib():
         L.cap_decode_attention.argtypes = [vp, vp, vp, vp, vp, sz, vp]
         L.cap_merge_partials.argtypes = [vp, vp, sz, vp, vp]
         L.cap_decode_step.argtypes = [vp, vp, vp, vp, vp, sz, vp, vp]
+        L.cap_decode_step_noalloc.argtypes = [vp, vp, vp, vp, vp, vp]
         L.cap_plan_free.argtypes = [vp]
         L.cap_plan_free.restype = None
         L.cap_tree_get_desc.argtypes = [vp, ctypes.POINTER(TreeDesc)]
@@ -133,7 +135,8 @@ def lib():
         L.cap_bench_decode_timed.argtypes = [vp, vp, vp, vp, vp, sz, vp, ctypes.POINTER(ctypes.c_float)]
         for name in ("cap_tree_device_bytes", "cap_tree_upload", "cap_plan_step", "cap_plan_rebuild",
                      "cap_plan_get_stats", "cap_plan_get_view", "cap_plan_upload",
-                     "cap_decode_attention", "cap_merge_partials", "cap_decode_step", "cap_tree_get_desc",
+                     "cap_decode_attention", "cap_merge_partials", "cap_decode_step", "cap_decode_step_noalloc",
+                     "cap_tree_get_desc",
                      "cap_tree_append", "cap_append_kv", "cap_plan_refresh", "cap_rows_softmax",
                      "cap_rows_layernorm", "cap_bench_fill",
                      "cap_bench_read", "cap_bench_read_stream", "cap_bench_copy", "cap_bench_decode_timed"):
@@ -327,6 +330,11 @@ def cap_decode_step(plan: int, q: int, k_pool: int, v_pool: int, workspace: int,
     _check(lib().cap_decode_step(ctypes.c_void_p(plan), ctypes.c_void_p(q), ctypes.c_void_p(k_pool),
                                  ctypes.c_void_p(v_pool), ctypes.c_void_p(workspace), ws_bytes,
                                  ctypes.c_void_p(out), ctypes.c_void_p(stream or None)))
+
+
+def cap_decode_step_noalloc(plan: int, q: int, k_pool: int, v_pool: int, out: int, stream: int = 0) -> None:
+    _check(lib().cap_decode_step_noalloc(ctypes.c_void_p(plan), ctypes.c_void_p(q), ctypes.c_void_p(k_pool),
+                                         ctypes.c_void_p(v_pool), ctypes.c_void_p(out), ctypes.c_void_p(stream)))
 
 
 def cap_plan_free(plan: int) -> None:

@@ -130,6 +130,11 @@ struct RowArgs {
 int launch_decode(const DecodeArgs &a, int head_dim, void *stream, void *ev_start = nullptr,
                   void *ev_stop = nullptr);
 int launch_merge(const MergeArgs &a, int head_dim, void *stream);
+// The static partial workspace of cap_decode_step_noalloc (cap_kernels.hip):
+// its device address on the current device (looked up on the first call per
+// device).
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+int scratch_address(void **ptr);
 int launch_fill(void *buf, size_t words, uint32_t value, void *stream);
 int launch_patch(void *base, const uint32_t *patch, int n, void *stream);
 int launch_append(const AppendArgs &a, void *stream);

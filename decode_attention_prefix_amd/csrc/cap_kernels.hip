@@ -37,6 +37,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "cap_internal.h"
 
@@ -1258,6 +1259,34 @@ static int device_cus(int *cus)
     if (e != hipSuccess) return (int)e;
     *cus = n > 0 ? n : 1;
     if (dev >= 0 && dev < 64) cache[dev] = *cus;
+    return 0;
+}
+
+// Partial workspace of cap_decode_step_noalloc: a fixed array in the code
+// object, so that callers that cannot allocate (graph capture, allocation-
+// free serving loops) get one.  Each GPU the library runs on holds its own
+// copy until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current,
+// and only that address is ever passed to a kernel.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+int scratch_address(void **ptr)
+{
+    static std::mutex mu;
+    static void *addr[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    if (dev < 0 || dev >= 64) return (int)hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return (int)e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
     return 0;
 }
 

@@ -152,6 +152,22 @@ cap_status cap_decode_step(const cap_plan *plan, const void *q, const void *k_po
     return CAP_OK;
 }
 
+static_assert(CAP_NOALLOC_WORKSPACE_BYTES == cap::kScratchBytes, "static workspace size");
+
+cap_status cap_decode_step_noalloc(const cap_plan *plan, const void *q, const void *k_pool, const void *v_pool,
+                                   void *out, cap_stream_t stream)
+{
+    if (!plan) return fail(CAP_ERR_INVALID_ARG, "NULL argument");
+    if ((uint64_t)plan->stats.workspace_bytes > cap::kScratchBytes)
+        return fail(CAP_ERR_UNSUPPORTED, "the plan needs a %lld-byte partial workspace; the static one holds %zu "
+                    "(use cap_decode_step with a caller workspace)", (long long)plan->stats.workspace_bytes,
+                    cap::kScratchBytes);
+    void *ws = nullptr;
+    const int e = cap::scratch_address(&ws);
+    if (e != 0) return fail(CAP_ERR_HIP, "static workspace lookup failed: %s", cap::hip_error_string(e));
+    return cap_decode_step(plan, q, k_pool, v_pool, ws, cap::kScratchBytes, out, stream);
+}
+
 cap_status cap_merge_partials(const cap_plan *plan, const void *workspace, size_t ws_bytes, void *out,
                               cap_stream_t stream)
 {

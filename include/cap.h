@@ -378,6 +378,23 @@ cap_status cap_merge_partials(const cap_plan *plan, const void *workspace, size_
 cap_status cap_decode_step(const cap_plan *plan, const void *q, const void *k_pool,
                            const void *v_pool, void *workspace, size_t ws_bytes, void *out,
                            cap_stream_t stream);
+
+/* cap_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, allocation-free
+ * serving loops, harnesses that forbid hipMalloc).  The partial workspace is
+ * a static device array inside the library, CAP_NOALLOC_WORKSPACE_BYTES
+ * (64 MiB) per GPU, held from the library's first use on that GPU until the
+ * process ends; this call allocates nothing.  Same kernels, arguments and
+ * result as cap_decode_step.  Every call on one GPU shares that GPU's array
+ * (whose contents persist between calls; nothing in it needs to start at
+ * zero): calls that overlap on one GPU race, so serialise them (one stream,
+ * or events).  Errors: as cap_decode_step, and CAP_ERR_UNSUPPORTED when the
+ * plan's stats.workspace_bytes exceeds CAP_NOALLOC_WORKSPACE_BYTES (nothing
+ * launched). */
+#define CAP_NOALLOC_WORKSPACE_BYTES (64u << 20)
+cap_status cap_decode_step_noalloc(const cap_plan *plan, const void *q, const void *k_pool,
+                                   const void *v_pool, void *out, cap_stream_t stream);
+
 void cap_plan_free(cap_plan *plan);
 
 #ifdef __cplusplus

@@ -337,3 +337,23 @@ def test_rebuild_follows_a_growing_tree_and_rejects_bad_options():
     finally:
         cap.cap_plan_free(p)
         cap.cap_tree_free(h)
+
+
+def test_noalloc_step_rejects_a_plan_past_the_static_workspace():
+    """cap_decode_step_noalloc checks the plan's workspace against its static
+    64 MiB before touching a device: a plan that needs more is refused with
+    CAP_ERR_UNSUPPORTED (here a host-only plan, never uploaded)."""
+    rng = np.random.default_rng([0, 1])
+    nt, par, paths, Hq, Hkv, D = wl._config_shape(1, rng)
+    t = wl.tree_from_lengths(nt, par, paths, Hq, Hkv, D)
+    h = cap.cap_tree_upload(t)
+    p = cap.cap_plan_step(h, split_pages=1)
+    try:
+        assert cap.cap_plan_get_stats(p)["workspace_bytes"] > 64 << 20
+        with pytest.raises(cap.CapError) as e:
+            cap.cap_decode_step_noalloc(p, 16, 16, 16, 16, 0)
+        assert e.value.status == cap.CAP_ERR_UNSUPPORTED
+        assert "static" in str(e.value)
+    finally:
+        cap.cap_plan_free(p)
+        cap.cap_tree_free(h)
