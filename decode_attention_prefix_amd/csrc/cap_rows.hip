@@ -247,7 +247,9 @@ __global__ __launch_bounds__(THREADS) void rows_reread_kernel(RowArgs a)
                 if (t > m) {
                     s = s * fexp2((m - t) * kLog2e) + 1.f;
                     m = t;
-                } else {
+                } else if (t != -INFINITY) {
+                    // a masked logit adds nothing; while m is still -inf,
+                    // its exponent would be -inf - -inf = NaN
                     s += fexp2((t - m) * kLog2e);
                 }
             }

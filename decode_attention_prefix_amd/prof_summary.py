@@ -1,7 +1,7 @@
 """Turn rocprofv3 output of bench.py runs into the short text summaries kept
 under profiles/ (kernel-trace statistics and HBM traffic per decode launch).
 
-Usage (after the three rocprofv3 runs named in each summary's header):
+Usage (after the rocprofv3 runs named in each summary's header):
 
     python -m decode_attention_prefix_amd.prof_summary --config 1 \
         --kt <dir with kt_kernel_stats.csv> --fetch <dir> --write <dir> [--out profiles]
@@ -69,11 +69,84 @@ def counter_means(pmc_dir: str, counter: str) -> dict[str, float]:
     return {k: statistics.fmean(v) for k, v in vals.items()}
 
 
+# Derived metrics as rocprofv3 defines them for this GPU (its counter list
+# on the box): 256 CUs, 4 SIMDs each.  GRBM_GUI_ACTIVE arrives summed over the
+# 8 XCDs (each has its own GRBM), while the formulas take its maximum over
+# them; a decode launch keeps every XCD busy for the whole dispatch, so the
+# per-XCD value is the sum / 8 (check: MFMA busy cycles / this value / 1024
+# SIMDs matches the MFMA instruction count x 16 cycles over the kernel's
+# duration).
+CU_NUM, SIMD_NUM, XCD_NUM = 256, 1024, 8
+
+
+def counter_summary(pmc_dirs: list[str], target: str) -> tuple[dict, int]:
+    """Mean per dispatch of every counter collected for the target kernel
+    over several --pmc runs, and the number of dispatches averaged."""
+    vals: dict[str, list[float]] = defaultdict(list)
+    for d in pmc_dirs:
+        with open(os.path.join(d, "pmc_counter_collection.csv")) as f:
+            for r in csv.DictReader(f):
+                if _short(r["Kernel_Name"]).startswith(target):
+                    vals[r["Counter_Name"]].append(float(r["Counter_Value"]))
+    n = min((len(v) for v in vals.values()), default=0)
+    return {k: statistics.fmean(v) for k, v in vals.items()}, n
+
+
+def derived(c: dict) -> list[tuple[str, float]]:
+    """The percentages rocprofv3 derives from these counters (same formulas),
+    each normalised by GRBM_GUI_ACTIVE of the run that collected it."""
+    out = []
+    g = c.get("GRBM_GUI_ACTIVE")
+    if not g:
+        return out
+    g /= XCD_NUM
+    out.append(("GRBM_GUI_ACTIVE_per_XCD", g))
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+        out.append(("MfmaUtil_pct", 100 * c["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * SIMD_NUM)))
+    if "SQ_ACTIVE_INST_VALU" in c:
+        out.append(("VALUBusy_pct", 100 * c["SQ_ACTIVE_INST_VALU"] / CU_NUM / g))
+    if "SQ_LDS_IDX_ACTIVE" in c:
+        out.append(("LdsUtil_pct", 100 * c["SQ_LDS_IDX_ACTIVE"] / (g * CU_NUM)))
+    if "SQ_LDS_BANK_CONFLICT" in c:
+        out.append(("LDSBankConflict_pct", 100 * c["SQ_LDS_BANK_CONFLICT"] / g / CU_NUM))
+    if "SQ_INST_CYCLES_SALU" in c:
+        out.append(("SALUBusy_pct", 100 * c["SQ_INST_CYCLES_SALU"] / CU_NUM / g))
+    if "SQ_BUSY_CYCLES" in c:
+        out.append(("SQ_BUSY_CYCLES_over_GRBM_GUI_ACTIVE", c["SQ_BUSY_CYCLES"] / g))
+    if "SQ_WAIT_INST_ANY" in c and "SQ_WAVE_CYCLES" in c:
+        out.append(("wave_cycles_waiting_for_any_instruction_pct", 100 * c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"]))
+    return out
+
+
+def write_counters(a, h: str, bench: str) -> None:
+    c, n = counter_summary(a.pmc, a.target)
+    groups = [g.replace(",", " ") for g in a.pmc_groups] if a.pmc_groups else ["?"] * len(a.pmc)
+    lines = [f"rocprofv3 counters of {a.kernel}, bench.py {bench} ({a.workload})",
+             "commands (one run per counter group, each with GRBM_GUI_ACTIVE):"]
+    lines += [f"  cd /tmp && rocprofv3 --pmc {g} --output-format csv -d <out> -o pmc -- python3 <repo>/bench.py "
+              f"{bench} --steps 3 --warmup 1" for g in groups]
+    lines += [f"kernel_code_sha256_16: {h}", f"kernel: {a.kernel}", f"dispatches_averaged: {n}", "",
+              "mean per dispatch (values summed over the GPU):"]
+    lines += [f"  {k}: {v:.1f}" for k, v in sorted(c.items())]
+    lines += ["", "derived (rocprofv3's formulas; CU_NUM 256, SIMD_NUM 1024):"]
+    lines += [f"  {k}: {v:.2f}" for k, v in derived(c)]
+    if a.per_unit and a.per_unit_name:
+        lines += ["", f"per {a.per_unit_name} ({a.per_unit:g} of them per dispatch):"]
+        for k in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VMEM",
+                  "SQ_INSTS_VALU_MFMA_MOPS_BF16"):
+            if k in c:
+                lines.append(f"  {k}: {c[k] / a.per_unit:.1f}")
+    name = a.counters_name or f"decode_kernel_cfg{a.config}_counters.txt"
+    with open(os.path.join(a.out, name), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--config", type=int, default=None, help="bench.py --config (omit for --rows runs)")
     ap.add_argument("--workload", default="", help="one-line workload description")
-    ap.add_argument("--kt", required=True)
+    ap.add_argument("--kt", default=None)
     ap.add_argument("--fetch", default=None, help="omit to write the kernel-trace summary only")
     ap.add_argument("--write", default=None)
     ap.add_argument("--copy-mb", type=int, default=512)
@@ -87,7 +160,17 @@ def main(argv=None):
     ap.add_argument("--target", default="decode_kernel", help="kernel name prefix the traffic is taken for")
     ap.add_argument("--src", choices=["attention", "rows"], default="attention",
                     help="kernel source the code hash covers")
+    ap.add_argument("--pmc", nargs="*", default=[], help="rocprofv3 --pmc output dirs: write a counter summary")
+    ap.add_argument("--pmc-groups", nargs="*", default=[], help="the counters of each --pmc run, comma-separated")
+    ap.add_argument("--counters-name", default="", help="counter summary file name")
+    ap.add_argument("--per-unit", type=float, default=0.0, help="divide instruction counts by this many units")
+    ap.add_argument("--per-unit-name", default="", help="what the unit is (e.g. 'wave-step of the shared path')")
     a = ap.parse_args(argv)
+    if a.pmc:
+        h = kernel_hash(ROWS_SRC if a.src == "rows" else KERNEL_SRC)
+        bench = (f"--config {a.config} " if a.config is not None else "") + a.bench_args
+        write_counters(a, h, bench)
+        return
     if a.fetch and a.write and a.alg_bytes <= 0:
         ap.error("--alg-bytes is needed with --fetch/--write")
     h = kernel_hash(ROWS_SRC if a.src == "rows" else KERNEL_SRC)

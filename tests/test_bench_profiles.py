@@ -54,7 +54,7 @@ def test_figures_only_for_the_current_kernel_source(tmp_path, monkeypatch):
     assert b.load_trace_us(3, KERNEL) is None and b.load_traffic(3, KERNEL) is None
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, "4c"])
 def test_committed_summaries_match_the_kernel_source(cfg):
     """The committed decode profiles were taken on the kernel source in the
     tree: bench.py reports their trace average and traffic."""

@@ -137,3 +137,27 @@ def test_full_size_sampled_rows(kind):
     if kind == "softmax":
         sums = yd.double().sum(dim=1).cpu().numpy()
         assert np.max(np.abs(sums - 1.0)) <= 1e-4
+
+
+@pytest.mark.parametrize("W", [64, 1000, 4096, 70000])
+def test_masked_logits(W):
+    """Softmax rows with -inf (masked) logits at the left end, the right end
+    and scattered, as attention masks leave them: a lane whose first values
+    are -inf must not turn its running sum into NaN.  Both schedules (the
+    retained row where it fits, and the two-pass one), against the oracle;
+    masked positions come out exactly 0."""
+    x, _, _ = inputs("softmax", W, rows=6, seed=W + 1)
+    x[0, : W // 2] = -np.inf                    # left half masked
+    x[1, W // 3:] = -np.inf                     # right part masked
+    x[2, :-1] = -np.inf                         # one logit left (at the end)
+    x[3, 1:] = -np.inf                          # one logit left (at the start)
+    rng = np.random.default_rng(W)
+    x[4, rng.random(W) < 0.7] = -np.inf         # scattered
+    x[4, 0] = 0.5
+    ref = oracle_of("softmax", x, None, None)
+    assert np.all(ref[x == -np.inf] == 0)
+    for mode in ([1, 2] if W <= 65536 else [2]):
+        for offset in ((0, 1) if W % 4 == 0 else (0,)):
+            out = run("softmax", x, mode=mode, offset=offset)
+            check("softmax", out, ref, f"masked W={W} mode={mode} off={offset}")
+            assert np.all(out[x == -np.inf] == 0)
