@@ -61,7 +61,8 @@ class PlanOpts(ctypes.Structure):
                 ("share_margin", ctypes.c_float), ("order", ctypes.c_int32),
                 ("private_rounds", ctypes.c_float), ("tail_factor", ctypes.c_float),
                 ("tail_min_pages", ctypes.c_int32), ("item_dispatch", ctypes.c_int32),
-                ("append_slack", ctypes.c_int32)]
+                ("append_slack", ctypes.c_int32), ("item_us", ctypes.c_float),
+                ("reread_factor", ctypes.c_float)]
 
 
 class PlanStats(ctypes.Structure):

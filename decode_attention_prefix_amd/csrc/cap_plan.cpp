@@ -12,9 +12,11 @@
 //   * folded: its pages ride along as a prefix of each child's run, read
 //     again by every child group but adding no partials of its own.
 // A node is shared when the bytes it saves, (groups below - 1) x its bytes,
-// exceed `share_margin` x the partial bytes sharing adds (cf. the CREDIT
-// summary, section III.B "Traffic Model": the saving is the removed reread
-// bytes, while fixed traffic stays).  Runs are sized so that the work items
+// discounted for the rereads that hit the L2, exceed `share_margin` x the
+// partial bytes sharing adds plus the start cost of the items it adds (cf.
+// the CREDIT summary, section III.B "Traffic Model": the saving is the
+// removed reread bytes, while fixed traffic stays; section III.D: each
+// candidate's overhead enters its profitability).  Runs are sized so that the work items
 // fill the GPU's resident wave slots about `rounds` times (cf. CREDIT
 // section III.D "Occupancy": the wave count enters the execution time).
 #include <hip/hip_runtime.h>
@@ -90,6 +92,7 @@ struct Planner {
     int64_t partial_row_bytes;     // partial bytes per query row (o, m, l)
     double unit = 0;               // target cost of one shared work item (cost units)
     double unit_private = 0;       // ... of one private work item
+    double item_bytes = 0;         // start cost of one item, as bytes streamed meanwhile (per KV head)
 
     Planner(const cap_tree &tree, const cap_plan_opts &opts, PlanScratch &scratch) : t(tree), o(opts), sc(scratch)
     {
@@ -98,7 +101,13 @@ struct Planner {
         G = t.G;
         head_tok_bytes = 4LL * D;
         partial_row_bytes = 2LL * D + 8;
+        // a round of items (every workgroup slot starting one) costs item_us;
+        // one item's share of it, over 2 x num_cus slots, while the GPU
+        // streams at the HBM rate (7.2 TB/s measured on MI355X = 7.2e6 B/us)
+        item_bytes = o.item_us > 0.f ? (double)o.item_us * kHbmBytesPerUs / (2.0 * o.num_cus) : 0.0;
     }
+
+    static constexpr double kHbmBytesPerUs = 7.2e6;
 
     int32_t node_pages(int n) const { return (int32_t)(t.page_off[n + 1] - t.page_off[n]); }
 
@@ -146,6 +155,21 @@ struct Planner {
 
     int64_t estimate_chunks(int64_t pages) const { return chunks(pages, true); }
 
+    // Share node n (with the folded nodes above it, prefix_tokens) or fold
+    // it into its children's runs.  Per KV head, in bytes of streaming:
+    //   saved = (groups below - 1) x its K+V bytes / reread_factor -- what
+    //           folding would reread (mostly from the XCD's L2: the sibling
+    //           groups' items run side by side);
+    //   added = share_margin x the partial bytes sharing adds (written and
+    //           merged) + its new items x one item's start cost, i.e. the
+    //           measured start cost of a round of items spread over the
+    //           workgroup slots, as bytes streamed at the HBM rate meanwhile.
+    // Share when saved > added.  A node's shared items are small when the
+    // node is, and the scheduler starts the smallest items last, so their
+    // start latency lands in the step's tail; this is the occupancy side of
+    // the trade (cf. the CREDIT summary, section III.D, "Profitability and
+    // Candidate Selection": the wave count enters the execution time), next
+    // to its traffic side (section III.B, "Traffic Model").
     bool decide_share(int n, int64_t prefix_tokens) const
     {
         if (o.share_mode == 1) return t.ntok[n] > 0 || prefix_tokens > 0;
@@ -155,10 +179,13 @@ struct Planner {
         const int64_t tok = t.ntok[n] + prefix_tokens;
         if (tok == 0) return false;
         const int64_t nreq = t.req_off[n + 1] - t.req_off[n];
-        const int64_t saved = (below - 1) * tok * head_tok_bytes;
+        const double saved = (double)((below - 1) * tok * head_tok_bytes) / o.reread_factor;
         const int64_t pages = (tok + cap::kPage - 1) / cap::kPage;
-        const int64_t added = 2 * nreq * G * partial_row_bytes * estimate_chunks(pages);
-        return (double)saved > (double)o.share_margin * (double)added;
+        const int64_t chunks = estimate_chunks(pages);
+        const double added_partial = (double)(2 * nreq * G * partial_row_bytes * chunks);
+        const int64_t row_groups = (nreq + reqs_per_item(nreq) - 1) / reqs_per_item(nreq);
+        const double added_items = (double)(chunks * row_groups) * item_bytes;
+        return saved > (double)o.share_margin * added_partial + added_items;
     }
 
     // Depth-first walk in node order (preorder, children in order): each node
@@ -240,6 +267,8 @@ void fill_defaults(cap_plan_opts &o)
     if (o.tail_factor == 0.f) o.tail_factor = 1.0f;
     if (o.tail_min_pages == 0) o.tail_min_pages = 16;
     if (o.append_slack == 0) o.append_slack = 8;
+    if (o.item_us == 0.f) o.item_us = 4.7f;
+    if (o.reread_factor == 0.f) o.reread_factor = 3.0f;
 }
 
 cap_status check_opts(const cap_plan_opts *opts_in, cap_plan_opts &o)
@@ -259,6 +288,8 @@ cap_status check_opts(const cap_plan_opts *opts_in, cap_plan_opts &o)
         return fail(CAP_ERR_INVALID_ARG, "append_slack %d not in [-1, 4096]", o.append_slack);
     if (o.append_slack == -1) o.append_slack = 0;
     if (o.order < 1 || o.order > 4) return fail(CAP_ERR_INVALID_ARG, "order %d not in {0, .., 4}", o.order);
+    if (!std::isfinite(o.item_us) || !(o.reread_factor >= 1.f) || !std::isfinite(o.reread_factor))
+        return fail(CAP_ERR_INVALID_ARG, "item_us must be finite and reread_factor finite and >= 1");
     return CAP_OK;
 }
 

@@ -154,6 +154,15 @@ typedef struct cap_plan_opts {
                                  reserved after each request's own leaf run, so that
                                  cap_plan_refresh can add that many new leaf pages per
                                  request before a new plan is needed */
+    float item_us;            /* 0 = 4.7; < 0 = no item term.  Start cost of one round of
+                                 work items (every workgroup slot starting one), in us:
+                                 sharing a node adds items, and each is charged this
+                                 cost / (2 x num_cus) slots, as bytes of streaming at
+                                 7.2 TB/s, against the bytes sharing saves */
+    float reread_factor;      /* 0 = 3.0; >= 1.  A folded node's rereads by its sibling
+                                 groups cost 1 / reread_factor of fresh HBM bytes: the
+                                 siblings run side by side on one XCD and read the node
+                                 mostly from its L2 */
 } cap_plan_opts;
 
 /* Plan summary (host-side numbers; bytes are per decode step). */
