@@ -143,6 +143,11 @@ def bench_rows(args, dev):
     nb = M * W * 4
     cdst = torch.empty(nb, dtype=torch.uint8, device=dev)
     copy_us = timed(lambda: cap.cap_bench_copy(cdst.data_ptr(), xd.data_ptr(), nb, sp), args.steps)
+    # the streaming floor: non-temporal loads and stores, in 256 KB runs per
+    # workgroup and in one-row runs (the retained kernel's own shape)
+    stream_us = {run: timed(lambda run=run: cap.cap_bench_copy_stream(cdst.data_ptr(), xd.data_ptr(), nb, run, sp),
+                            args.steps)
+                 for run in (0, W * 4 if (W * 4) % 16 == 0 else 0)}
     del cdst
     mode = args.row_mode
     us = timed(lambda: launch(mode), args.steps)
@@ -152,8 +157,12 @@ def bench_rows(args, dev):
     alg = 2 * M * W * 4 + (2 * W * 4 if kind == "layernorm" else 0)
     value = alg / (mean_us * 1e-6) / 1e9
     src_hash = kernel_hash(ROWS_SRC)
-    retained = mode == 1 or (mode == 0 and W <= 65536 and W % 4 == 0) or (mode == 0 and W <= 16384)
-    kname = "rows_retained_kernel" if retained else "rows_reread_kernel"
+    # the kernel the library runs (the rule of cap_rows.h's mode argument)
+    retained = mode in (1, 3) or (mode == 0 and W <= 65536 and W % 4 == 0) or (mode == 0 and W <= 16384)
+    pipelined = ((mode == 3 or (mode == 0 and kind == "layernorm" and W % 4 == 0 and 8192 <= W <= 16384
+                                and M >= 1024))
+                 and W <= (16384 if kind == "layernorm" or W % 4 else 32768))
+    kname = ("rows_pipelined_kernel" if pipelined else "rows_retained_kernel") if retained else "rows_reread_kernel"
     traffic = None
     tpath = os.path.join(ROOT, "profiles", f"rows_{kind}_{W}_traffic.txt")
     if os.path.exists(tpath):
@@ -170,7 +179,7 @@ def bench_rows(args, dev):
         "ms_per_step": round(mean_us / 1e3, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{kind} over {M} rows x {W} FP32 (N(0,1) inputs)", "rows": M, "width": W,
-                   "mode": {0: "auto", 1: "retained row", 2: "two passes"}[mode]},
+                   "mode": {0: "auto", 1: "retained row", 2: "two passes", 3: "retained rows, pipelined"}[mode]},
         "roofline": {"bound": "hbm", "achieved": round(value, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(value / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel": kname,
                      "algorithmic_bytes_per_launch": alg, "kernel_us_mean": round(mean_us, 3)},
@@ -180,9 +189,18 @@ def bench_rows(args, dev):
         "speedup_vs_two_pass": round(statistics.fmean(reread_us) / mean_us, 3),
         "speedup_vs_torch": round(statistics.fmean(torch_us) / mean_us, 3),
         "kernel_code_sha256_16": src_hash,
-        "copy_same_bytes_gbs": round(2 * nb / (min(copy_us) * 1e-6) / 1e9, 1),
-        "pct_of_copy_rate": round(100 * value / (2 * nb / (min(copy_us) * 1e-6) / 1e9), 2),
     }
+    # read + write floor: copies of x's bytes, timed like the kernel (mean
+    # over the timed launches; min for reference); the rows kernel's rate on
+    # the same x + y bytes against the fastest copy's mean
+    copies = {"cached_grid_stride": copy_us}
+    copies.update({("stream_256KB_runs" if run == 0 else "stream_row_runs"): t for run, t in stream_us.items()})
+    rates = {k: {"mean_gbs": round(2 * nb / (statistics.fmean(t) * 1e-6) / 1e9, 1),
+                 "best_gbs": round(2 * nb / (min(t) * 1e-6) / 1e9, 1)} for k, t in copies.items()}
+    best = max(rates, key=lambda k: rates[k]["mean_gbs"])
+    result["copy_floor"] = {"rates": rates, "fastest": best,
+                            "kernel_pct_of_fastest_mean": round(100 * (2 * nb / (mean_us * 1e-6) / 1e9)
+                                                                / rates[best]["mean_gbs"], 2)}
     if not args.no_cpu_baseline:
         from oracle import rows_np
         # the whole workload, run again until about 10 s of CPU time has
@@ -589,8 +607,8 @@ def main():
     ap.add_argument("--rows", choices=["softmax", "layernorm"], default=None,
                     help="time a wide-row reduction-reuse workload instead of decode attention")
     ap.add_argument("--width", type=int, default=65536, help="row width for --rows")
-    ap.add_argument("--row-mode", type=int, default=0, choices=[0, 1, 2],
-                    help="0 auto, 1 retained row, 2 two passes (for --rows)")
+    ap.add_argument("--row-mode", type=int, default=0, choices=[0, 1, 2, 3],
+                    help="0 auto, 1 retained row, 2 two passes, 3 retained rows pipelined (for --rows)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run one plain copy of this size (calibrates HBM byte counters)")
     args = ap.parse_args()

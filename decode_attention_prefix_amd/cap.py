@@ -29,6 +29,7 @@ EXPORTED = [
     "cap_plan_get_view", "cap_plan_upload", "cap_decode_attention", "cap_merge_partials",
     "cap_decode_step", "cap_plan_free", "cap_tree_get_desc", "cap_tree_append", "cap_append_kv",
     "cap_plan_refresh", "cap_bench_fill", "cap_bench_read", "cap_bench_read_stream", "cap_bench_copy",
+    "cap_bench_copy_stream",
     "cap_bench_decode_timed", "cap_rows_softmax", "cap_rows_layernorm", "cap_plan_rebuild",
     "cap_decode_step_noalloc",
 ]
@@ -133,6 +134,7 @@ def lib():
         L.cap_bench_read.argtypes = [vp, sz, vp, vp]
         L.cap_bench_read_stream.argtypes = [vp, sz, vp, vp]
         L.cap_bench_copy.argtypes = [vp, vp, sz, vp]
+        L.cap_bench_copy_stream.argtypes = [vp, vp, sz, sz, vp]
         L.cap_bench_decode_timed.argtypes = [vp, vp, vp, vp, vp, sz, vp, ctypes.POINTER(ctypes.c_float)]
         for name in ("cap_tree_device_bytes", "cap_tree_upload", "cap_plan_step", "cap_plan_rebuild",
                      "cap_plan_get_stats", "cap_plan_get_view", "cap_plan_upload",
@@ -140,7 +142,8 @@ def lib():
                      "cap_tree_get_desc",
                      "cap_tree_append", "cap_append_kv", "cap_plan_refresh", "cap_rows_softmax",
                      "cap_rows_layernorm", "cap_bench_fill",
-                     "cap_bench_read", "cap_bench_read_stream", "cap_bench_copy", "cap_bench_decode_timed"):
+                     "cap_bench_read", "cap_bench_read_stream", "cap_bench_copy", "cap_bench_copy_stream",
+                     "cap_bench_decode_timed"):
             getattr(L, name).restype = st
         _lib = L
     return _lib
@@ -371,3 +374,8 @@ def cap_bench_read_stream(buf: int, nbytes: int, sink: int, stream: int = 0) -> 
 def cap_bench_copy(dst: int, src: int, nbytes: int, stream: int = 0) -> None:
     _check(lib().cap_bench_copy(ctypes.c_void_p(dst), ctypes.c_void_p(src), nbytes,
                                 ctypes.c_void_p(stream or None)))
+
+
+def cap_bench_copy_stream(dst: int, src: int, nbytes: int, run_bytes: int = 0, stream: int = 0) -> None:
+    _check(lib().cap_bench_copy_stream(ctypes.c_void_p(dst), ctypes.c_void_p(src), nbytes, run_bytes,
+                                       ctypes.c_void_p(stream or None)))

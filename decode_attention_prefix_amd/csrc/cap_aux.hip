@@ -1,7 +1,7 @@
 // cap_aux.hip -- gfx950 kernels of libcap off the attention hot path: the
 // per-step growth of the KV pools and of an uploaded plan (append_kernel,
 // patch_kernel), and the measurement kernels of cap_bench.h (fill, cached
-// read, streaming read probe, copy).
+// read, streaming read probe, copy, streaming copy probe).
 #include <hip/hip_runtime.h>
 
 #include "cap_internal.h"
@@ -117,6 +117,27 @@ __global__ __launch_bounds__(256) void copy_kernel(u32x4 *dst, const u32x4 *src,
         dst[i] = src[i];
 }
 
+// The achievable read-plus-write probe: workgroup b copies runs b, b + grid,
+// ... of `run` 16-byte vectors each, eight non-temporal 16-byte loads in
+// flight per lane, written back with non-temporal stores (the access shape
+// of a kernel that streams rows through registers).
+__global__ __launch_bounds__(256) void copy_stream_kernel(u32x4 *dst, const u32x4 *src, size_t n, size_t run)
+{
+    constexpr int K = 8;
+    for (size_t base = (size_t)blockIdx.x * run; base < n; base += (size_t)gridDim.x * run) {
+        const size_t end = base + run < n ? base + run : n;
+        size_t i = base + threadIdx.x;
+        for (; i + (K - 1) * 256 < end; i += K * 256) {
+            u32x4 v[K];
+#pragma unroll
+            for (int k = 0; k < K; ++k) v[k] = __builtin_nontemporal_load(&src[i + k * 256]);
+#pragma unroll
+            for (int k = 0; k < K; ++k) __builtin_nontemporal_store(v[k], &dst[i + k * 256]);
+        }
+        for (; i < end; i += 256) __builtin_nontemporal_store(__builtin_nontemporal_load(&src[i]), &dst[i]);
+    }
+}
+
 }  // namespace
 
 static unsigned grid_for(size_t n)
@@ -173,6 +194,17 @@ int launch_copy(void *dst, const void *src, size_t vec16, void *stream)
     hipLaunchKernelGGL(copy_kernel, dim3(grid_for(vec16)), dim3(256), 0,
                        reinterpret_cast<hipStream_t>(stream), (u32x4 *)dst, (const u32x4 *)src,
                        vec16);
+    return (int)hipGetLastError();
+}
+
+int launch_copy_stream(void *dst, const void *src, size_t vec16, size_t run16, void *stream)
+{
+    // one workgroup per run, up to 8192 workgroups (32 per CU); longer inputs
+    // loop over their runs
+    size_t g = (vec16 + run16 - 1) / run16;
+    g = g > 8192 ? 8192 : (g < 1 ? 1 : g);
+    hipLaunchKernelGGL(copy_stream_kernel, dim3((unsigned)g), dim3(256), 0,
+                       reinterpret_cast<hipStream_t>(stream), (u32x4 *)dst, (const u32x4 *)src, vec16, run16);
     return (int)hipGetLastError();
 }
 

@@ -121,6 +121,7 @@ struct RowArgs {
     int64_t rows, width;
     float eps;
     int32_t kind;
+    int32_t rows_per_wg;         // retained schedule: > 1 = that many rows per workgroup, pipelined
 };
 
 // Kernel launchers (cap_kernels.hip, cap_aux.hip, cap_rows.hip); return the
@@ -142,6 +143,7 @@ int launch_rows(const RowArgs &a, bool vec4, bool retained, void *stream);
 int launch_read_stream(const void *buf, size_t vec16, void *sink, void *stream);
 int launch_read(const void *buf, size_t vec16, void *sink, void *stream);
 int launch_copy(void *dst, const void *src, size_t vec16, void *stream);
+int launch_copy_stream(void *dst, const void *src, size_t vec16, size_t run16, void *stream);
 const char *hip_error_string(int err);
 
 }  // namespace cap

@@ -196,17 +196,37 @@ cap_status cap_merge_partials(const cap_plan *plan, const void *workspace, size_
 
 // ------------------------------------------------------- wide-row workloads
 
+// Rows per workgroup of the pipelined retained schedule: of 2, 4 and 8, 4
+// is within 4% of the best for LayerNorm at 8K-16K values and keeps a full
+// grid (256 workgroups) from 1024 rows up.
+static int pipelined_rows_per_workgroup(const cap::RowArgs &a)
+{
+    (void)a;
+    return 4;
+}
+
+// Auto mode takes the pipelined schedule where it measured faster than one
+// row per workgroup: LayerNorm rows of 8K-16K values with 16-byte accesses
+// (3-15% faster; gamma and beta stay in registers across a workgroup's
+// rows), with rows enough for a full grid of 4-row workgroups.  Softmax
+// keeps one row per workgroup (as fast or faster from 8K to 32K), and so do
+// rows of 4K values and less (where a row's latency, not bandwidth, decides).
+static bool auto_pipelined(const cap::RowArgs &a, bool vec4)
+{
+    return vec4 && a.kind == cap::kRowLayerNorm && a.width >= 8192 && a.width <= 16384 && a.rows >= 1024;
+}
+
 static cap_status rows_launch(cap::RowArgs &a, int32_t mode, cap_stream_t stream)
 {
     if (!a.x || !a.y) return fail(CAP_ERR_INVALID_ARG, "NULL argument");
     if (a.rows < 0 || a.width < 1) return fail(CAP_ERR_INVALID_ARG, "rows %lld / width %lld out of range",
                                              (long long)a.rows, (long long)a.width);
-    if (mode < 0 || mode > 2) return fail(CAP_ERR_INVALID_ARG, "mode %d not in {0, 1, 2}", mode);
+    if (mode < 0 || mode > 3) return fail(CAP_ERR_INVALID_ARG, "mode %d not in {0, 1, 2, 3}", mode);
     if (a.rows > std::numeric_limits<int32_t>::max())
         return fail(CAP_ERR_UNSUPPORTED, "%lld rows: at most 2^31 - 1", (long long)a.rows);
     if (a.width > ((int64_t)1 << 24))
         return fail(CAP_ERR_UNSUPPORTED, "width %lld above 2^24", (long long)a.width);
-    if (mode == 1 && a.width > cap::kMaxRetainedWidth)
+    if ((mode == 1 || mode == 3) && a.width > cap::kMaxRetainedWidth)
         return fail(CAP_ERR_UNSUPPORTED, "width %lld: a retained row holds at most %lld values",
                     (long long)a.width, (long long)cap::kMaxRetainedWidth);
     const size_t bytes = (size_t)a.rows * a.width * 4;
@@ -219,7 +239,8 @@ static cap_status rows_launch(cap::RowArgs &a, int32_t mode, cap_stream_t stream
     const bool vec4 = (a.width % 4 == 0) && (align & 15) == 0;
     // auto: retained up to 64K values with 16-byte accesses; with 4-byte
     // accesses only up to 16K (a wider retained row spills registers)
-    const bool retained = mode == 1 || (mode == 0 && a.width <= (vec4 ? cap::kMaxRetainedWidth : 16384));
+    const bool retained = mode == 1 || mode == 3 || (mode == 0 && a.width <= (vec4 ? cap::kMaxRetainedWidth : 16384));
+    a.rows_per_wg = (mode == 3 || (mode == 0 && auto_pipelined(a, vec4))) ? pipelined_rows_per_workgroup(a) : 1;
     const int e = cap::launch_rows(a, vec4, retained, stream);
     if (e != 0) return fail(CAP_ERR_HIP, "row kernel launch failed: %s", cap::hip_error_string(e));
     return CAP_OK;
@@ -285,6 +306,16 @@ cap_status cap_bench_copy(void *dst, const void *src, size_t bytes, cap_stream_t
     if (!dst || !src || bytes == 0 || (bytes & 15) || (((uintptr_t)dst | (uintptr_t)src) & 15))
         return fail(CAP_ERR_INVALID_ARG, "copy: bad buffer or size");
     const int e = cap::launch_copy(dst, src, bytes / 16, stream);
+    return e ? fail(CAP_ERR_HIP, "copy launch failed: %s", cap::hip_error_string(e)) : CAP_OK;
+}
+
+cap_status cap_bench_copy_stream(void *dst, const void *src, size_t bytes, size_t run_bytes, cap_stream_t stream)
+{
+    if (!dst || !src || bytes == 0 || (bytes & 15) || (((uintptr_t)dst | (uintptr_t)src) & 15))
+        return fail(CAP_ERR_INVALID_ARG, "copy: bad buffer or size");
+    if (run_bytes == 0) run_bytes = (size_t)256 << 10;
+    if (run_bytes & 15) return fail(CAP_ERR_INVALID_ARG, "copy: run_bytes must be a multiple of 16");
+    const int e = cap::launch_copy_stream(dst, src, bytes / 16, run_bytes / 16, stream);
     return e ? fail(CAP_ERR_HIP, "copy launch failed: %s", cap::hip_error_string(e)) : CAP_OK;
 }
 

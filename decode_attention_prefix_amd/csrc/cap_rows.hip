@@ -15,10 +15,13 @@
 // across the workgroup (wave shuffles, then one LDS slot per wave), and the
 // output is computed from the registers and written once.
 //
-// rows_retained_kernel: that schedule, for rows of at most 64K values.
-// rows_reread_kernel:   the non-retaining schedule (and the only one for
-//                       wider rows): a statistics pass over the row, then a
-//                       second read for the output pass.
+// rows_retained_kernel:  that schedule, for rows of at most 64K values.
+// rows_pipelined_kernel: the same, several rows per workgroup, the next
+//                        row's loads in flight while the current row is
+//                        reduced and written.
+// rows_reread_kernel:    the non-retaining schedule (and the only one for
+//                        wider rows): a statistics pass over the row, then a
+//                        second read for the output pass.
 #include <hip/hip_runtime.h>
 
 #include "cap_internal.h"
@@ -109,6 +112,12 @@ __device__ __forceinline__ Vec<VEC> load_cached(const float *p)
     return r;
 }
 
+// The retained schedules write their output with plain stores (write-back
+// through L2): on this GPU they measured 4-17% faster than non-temporal
+// stores for softmax rows of 8K-64K values, also where the output far
+// exceeds the 256 MB Infinity Cache, and about as fast for LayerNorm.  The two-pass
+// schedule keeps non-temporal stores: its second read finds the row in the
+// Infinity Cache, and plain stores would evict it (5-6% slower measured).
 template <int VEC>
 __device__ __forceinline__ void store_nt(float *p, const Vec<VEC> &r)
 {
@@ -122,20 +131,29 @@ __device__ __forceinline__ void store_nt(float *p, const Vec<VEC> &r)
     }
 }
 
-// One row per workgroup, kept in registers: EPT loads of VEC values per lane.
-template <int KIND, int VEC, int EPT, int THREADS>
-__global__ __launch_bounds__(THREADS) void rows_retained_kernel(RowArgs a)
+template <int VEC>
+__device__ __forceinline__ void store_row(float *p, const Vec<VEC> &r)
 {
-    __shared__ float red0[kMaxRowWaves], red1[kMaxRowWaves];
-    const int64_t row = blockIdx.x;
+    if constexpr (VEC == 4) {
+        typedef float f4 __attribute__((ext_vector_type(4)));
+        f4 x;
+        x.x = r.v[0], x.y = r.v[1], x.z = r.v[2], x.w = r.v[3];
+        *reinterpret_cast<f4 *>(p) = x;
+    } else {
+        *p = r.v[0];
+    }
+}
+
+// One row kept in registers: EPT loads of VEC values per lane (padding
+// beyond the row: -inf for softmax, 0 for LayerNorm, neutral in the sums).
+template <int KIND, int VEC, int EPT, int THREADS>
+__device__ __forceinline__ void load_row(Vec<VEC> (&v)[EPT], const RowArgs &a, int64_t row)
+{
     const int64_t nvec = a.width / VEC;
     const float *x = a.x + row * a.width;
-    float *y = a.y + row * a.width;
-    const int tid = threadIdx.x;
-    Vec<VEC> v[EPT];
 #pragma unroll
     for (int k = 0; k < EPT; ++k) {
-        const int64_t i = (int64_t)k * THREADS + tid;
+        const int64_t i = (int64_t)k * THREADS + threadIdx.x;
         if (i < nvec) {
             v[k] = load_nt<VEC>(x + i * VEC);
         } else {
@@ -143,6 +161,18 @@ __global__ __launch_bounds__(THREADS) void rows_retained_kernel(RowArgs a)
             for (int j = 0; j < VEC; ++j) v[k].v[j] = KIND == kRowSoftmax ? -INFINITY : 0.f;
         }
     }
+}
+
+// The row's statistics from the registers, then its output, written once.
+// red0 / red1: one LDS slot per wave for each of the two reductions.
+template <int KIND, int VEC, int EPT, int THREADS, bool GB_REGS = false>
+__device__ __forceinline__ void finish_row(Vec<VEC> (&v)[EPT], const RowArgs &a, int64_t row, float *red0,
+                                           float *red1, const Vec<VEC> *gam = nullptr,
+                                           const Vec<VEC> *bet = nullptr)
+{
+    const int64_t nvec = a.width / VEC;
+    float *y = a.y + row * a.width;
+    const int tid = threadIdx.x;
     if constexpr (KIND == kRowSoftmax) {
         float m = -INFINITY;
 #pragma unroll
@@ -170,7 +200,7 @@ __global__ __launch_bounds__(THREADS) void rows_retained_kernel(RowArgs a)
             if (i < nvec) {
 #pragma unroll
                 for (int j = 0; j < VEC; ++j) v[k].v[j] *= inv;
-                store_nt<VEC>(y + i * VEC, v[k]);
+                store_row<VEC>(y + i * VEC, v[k]);
             }
         }
     } else {
@@ -199,14 +229,74 @@ __global__ __launch_bounds__(THREADS) void rows_retained_kernel(RowArgs a)
         for (int k = 0; k < EPT; ++k) {
             const int64_t i = (int64_t)k * THREADS + tid;
             if (i < nvec) {
-                const Vec<VEC> g = load_cached<VEC>(a.gamma + i * VEC);
-                const Vec<VEC> b = load_cached<VEC>(a.beta + i * VEC);
+                Vec<VEC> g, b;
+                if constexpr (GB_REGS) {
+                    g = gam[k];
+                    b = bet[k];
+                } else {
+                    g = load_cached<VEC>(a.gamma + i * VEC);
+                    b = load_cached<VEC>(a.beta + i * VEC);
+                }
 #pragma unroll
                 for (int j = 0; j < VEC; ++j)
                     v[k].v[j] = __builtin_fmaf((v[k].v[j] - mean) * rstd, g.v[j], b.v[j]);
-                store_nt<VEC>(y + i * VEC, v[k]);
+                store_row<VEC>(y + i * VEC, v[k]);
             }
         }
+    }
+}
+
+// One row per workgroup, kept in registers.
+template <int KIND, int VEC, int EPT, int THREADS>
+__global__ __launch_bounds__(THREADS) void rows_retained_kernel(RowArgs a)
+{
+    __shared__ float red0[kMaxRowWaves], red1[kMaxRowWaves];
+    Vec<VEC> v[EPT];
+    load_row<KIND, VEC, EPT, THREADS>(v, a, blockIdx.x);
+    finish_row<KIND, VEC, EPT, THREADS>(v, a, blockIdx.x, red0, red1);
+}
+
+// Rows blockIdx.x, + gridDim.x, ... per workgroup, each kept in registers,
+// with the next row's loads in flight while the current row is reduced and
+// written: the workgroup's reads and writes overlap, where one-row
+// workgroups that all start together read the whole input first and write
+// it all afterwards.  LayerNorm's gamma and beta are loaded once per
+// workgroup and kept in registers (when a lane holds at most 16 values of a
+// row), not read again from L2 for every row.  Same arithmetic per row as
+// rows_retained_kernel, so the same bits.  The reductions' LDS slots are
+// reused row after row: a wave writes a slot again only after every wave
+// has passed the barrier of the other reduction, i.e. after every read of
+// the slot's previous value.
+template <int KIND, int VEC, int EPT, int THREADS>
+__global__ __launch_bounds__(THREADS) void rows_pipelined_kernel(RowArgs a)
+{
+    constexpr bool GB = KIND == kRowLayerNorm && EPT * VEC <= 16;
+    __shared__ float red0[kMaxRowWaves], red1[kMaxRowWaves];
+    const int64_t g = gridDim.x;
+    int64_t row = blockIdx.x;
+    Vec<VEC> v[EPT], w[EPT];
+    Vec<VEC> gam[GB ? EPT : 1], bet[GB ? EPT : 1];
+    load_row<KIND, VEC, EPT, THREADS>(v, a, row);
+    if constexpr (GB) {
+        const int64_t nvec = a.width / VEC;
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) {
+            const int64_t i = (int64_t)k * THREADS + threadIdx.x;
+            if (i < nvec) {
+                gam[k] = load_cached<VEC>(a.gamma + i * VEC);
+                bet[k] = load_cached<VEC>(a.beta + i * VEC);
+            }
+        }
+    }
+    for (;;) {
+        if (row + g < a.rows) load_row<KIND, VEC, EPT, THREADS>(w, a, row + g);
+        finish_row<KIND, VEC, EPT, THREADS, GB>(v, a, row, red0, red1, gam, bet);
+        row += g;
+        if (row >= a.rows) break;
+        if (row + g < a.rows) load_row<KIND, VEC, EPT, THREADS>(v, a, row + g);
+        finish_row<KIND, VEC, EPT, THREADS, GB>(w, a, row, red0, red1, gam, bet);
+        row += g;
+        if (row >= a.rows) break;
     }
 }
 
@@ -309,6 +399,15 @@ int launch_retained(const RowArgs &a, hipStream_t s)
     return (int)hipGetLastError();
 }
 
+template <int KIND, int VEC, int EPT, int THREADS>
+int launch_pipelined(const RowArgs &a, hipStream_t s)
+{
+    const int64_t grid = (a.rows + a.rows_per_wg - 1) / a.rows_per_wg;
+    hipLaunchKernelGGL((rows_pipelined_kernel<KIND, VEC, EPT, THREADS>), dim3((unsigned)grid), dim3(THREADS),
+                       0, s, a);
+    return (int)hipGetLastError();
+}
+
 template <int KIND, int VEC>
 int dispatch_retained(const RowArgs &a, hipStream_t s)
 {
@@ -329,9 +428,37 @@ int dispatch_retained(const RowArgs &a, hipStream_t s)
     }
 }
 
+// The pipelined schedule holds two rows per lane, so it spreads a row over
+// more lanes than the one-row kernel does (at most 4 float4 per lane and
+// row up to 16K values).  Wider rows (softmax: above 32K; LayerNorm, which
+// also holds gamma and beta: above 16K; either with 4-byte accesses: above
+// 16K) would not fit twice in a lane's registers: they take the one-row
+// kernel.
+template <int KIND, int VEC>
+int dispatch_pipelined(const RowArgs &a, hipStream_t s)
+{
+    const int64_t nvec = a.width / VEC;
+    if constexpr (VEC == 4) {
+        if (nvec <= 256) return launch_pipelined<KIND, 4, 1, 256>(a, s);
+        if (nvec <= 512) return launch_pipelined<KIND, 4, 2, 256>(a, s);
+        if (nvec <= 1024) return launch_pipelined<KIND, 4, 4, 256>(a, s);
+        if (nvec <= 2048) return launch_pipelined<KIND, 4, 4, 512>(a, s);
+        if (nvec <= 4096) return launch_pipelined<KIND, 4, 4, 1024>(a, s);
+        if constexpr (KIND == kRowSoftmax)
+            if (nvec <= 8192) return launch_pipelined<KIND, 4, 8, 1024>(a, s);
+    } else {
+        if (nvec <= 1024) return launch_pipelined<KIND, 1, 4, 256>(a, s);
+        if (nvec <= 4096) return launch_pipelined<KIND, 1, 16, 256>(a, s);
+        if (nvec <= 16384) return launch_pipelined<KIND, 1, 16, 1024>(a, s);
+    }
+    return dispatch_retained<KIND, VEC>(a, s);
+}
+
 template <int KIND>
 int dispatch(const RowArgs &a, bool vec4, bool retained, hipStream_t s)
 {
+    if (retained && a.rows_per_wg > 1)
+        return vec4 ? dispatch_pipelined<KIND, 4>(a, s) : dispatch_pipelined<KIND, 1>(a, s);
     if (retained) return vec4 ? dispatch_retained<KIND, 4>(a, s) : dispatch_retained<KIND, 1>(a, s);
     const int threads = a.width >= 16384 ? 1024 : 256;
     if (vec4) {

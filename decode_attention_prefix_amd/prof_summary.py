@@ -42,9 +42,9 @@ def kernel_hash(src: str = KERNEL_SRC) -> str:
 
 
 def _short(name: str) -> str:
-    for key in ("decode_kernel", "merge_kernel", "rows_retained_kernel", "rows_reread_kernel",
-                "read_stream_kernel", "read_kernel", "fill_kernel", "copy_kernel", "patch_kernel",
-                "append_kernel"):
+    for key in ("decode_kernel", "merge_kernel", "rows_retained_kernel", "rows_pipelined_kernel",
+                "rows_reread_kernel", "read_stream_kernel", "read_kernel", "fill_kernel", "copy_stream_kernel",
+                "copy_kernel", "patch_kernel", "append_kernel"):
         if key in name:
             tail = name[name.index(key):]
             return tail.split("(")[0]
@@ -187,8 +187,8 @@ def main(argv=None):
         lines.append(f"{name:40s} {calls:6d} {avg:9.3f} {mn:9.3f} {mx:9.3f}")
     lines += ["", "(read_kernel and fill_kernel: the bench's cache-eviction read and buffer setup; "
               "read_stream_kernel: its plain-read probes (2 GiB, and the decode launch's own bytes); append_kernel and patch_kernel: "
-              "cap_append_kv and cap_plan_refresh in its growth steps; rows_reread_kernel, copy_kernel "
-              "and at::native kernels: the two-pass, copy and torch references of a --rows run)"]
+              "cap_append_kv and cap_plan_refresh in its growth steps; rows_reread_kernel, copy_kernel, "
+              "copy_stream_kernel and at::native kernels: the two-pass, copy and torch references of a --rows run)"]
     name = a.name or f"decode_kernel_cfg{cfg}_kernel_trace.txt"
     with open(os.path.join(a.out, name), "w") as f:
         f.write("\n".join(lines) + "\n")

@@ -40,6 +40,15 @@ cap_status cap_bench_read_stream(const void *buf, size_t bytes, void *sink, cap_
  * for scaling FETCH_SIZE / WRITE_SIZE counters. */
 cap_status cap_bench_copy(void *dst, const void *src, size_t bytes, cap_stream_t stream);
 
+/* The achievable read-plus-write probe: copy `bytes` from src to dst, each
+ * workgroup copying contiguous runs of `run_bytes` (0 = 256 KB; else a
+ * multiple of 16: e.g. one row, for the shape of a one-row-per-workgroup
+ * kernel) with non-temporal 128-bit loads and stores, eight loads in flight
+ * per lane; up to 8192 workgroups, each looping over its runs.  src and dst
+ * must not overlap. */
+cap_status cap_bench_copy_stream(void *dst, const void *src, size_t bytes, size_t run_bytes,
+                                 cap_stream_t stream);
+
 /* cap_decode_attention (same arguments, same checks and errors), launched
  * with two HIP events bound to the kernel's own dispatch (hipExtLaunchKernel)
  * that the call creates and destroys; it waits for the kernel and writes its

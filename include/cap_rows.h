@@ -22,12 +22,20 @@
  * [width] FP32.  Rows whose width is a multiple of 4 with 16-byte aligned
  * buffers use 16-byte accesses; other shapes use 4-byte accesses.
  *
- * mode: 0 = auto (1 for width <= 65536 with 16-byte accesses or <= 16384
- * with 4-byte accesses, else 2); 1 = retained: one
- * workgroup keeps its whole row in registers, so the row is read from HBM
- * once (width <= 65536, CAP_ERR_UNSUPPORTED above); 2 = two passes: a
- * statistics pass, then a second read of the row for the output (any width;
- * the non-retaining baseline).
+ * mode: 0 = auto (3 for LayerNorm with 8192 <= width <= 16384, 16-byte
+ * accesses and rows >= 1024; else 1 for width <= 65536 with 16-byte accesses
+ * or <= 16384 with 4-byte accesses; else 2); 1 = retained: one workgroup
+ * keeps its whole row in registers, so the row is read from HBM once
+ * (width <= 65536, CAP_ERR_UNSUPPORTED above); 2 = two passes: a statistics
+ * pass, then a second read of the row for the output (any width; the
+ * non-retaining baseline); 3 = retained, pipelined: each workgroup takes 4
+ * rows in turn, keeping each in registers and loading the next while it
+ * reduces and writes the current one (LayerNorm: gamma and beta stay in
+ * registers across its rows); HBM traffic as for 1 (width <= 65536,
+ * CAP_ERR_UNSUPPORTED above; rows too wide to be held twice run as 1).
+ * Results are deterministic for a given (mode, width); modes 1 and 3 may
+ * differ in the last bits, since they may split a row over a different
+ * number of lanes.
  *
  * Errors: CAP_ERR_INVALID_ARG (NULL pointer, rows < 0, width < 1, bad mode,
  * partial overlap of x and y, eps negative or not finite), CAP_ERR_UNSUPPORTED

@@ -70,7 +70,7 @@ def oracle_of(kind, x, g, b):
 def test_parity_all_paths(kind, W):
     x, g, b = inputs(kind, W, rows=5, seed=W)
     ref = oracle_of(kind, x, g, b)
-    modes = [0, 2] + ([1] if W <= 65536 else [])
+    modes = [0, 2] + ([1, 3] if W <= 65536 else [])
     for mode in modes:
         for offset in ((0, 1) if W % 4 == 0 else (0,)):
             check(kind, run(kind, x, g, b, mode=mode, offset=offset), ref, f"{kind} W={W} mode={mode} off={offset}")
@@ -80,13 +80,46 @@ def test_parity_all_paths(kind, W):
 def test_in_place_and_deterministic(kind):
     x, g, b = inputs(kind, 20000, rows=9, seed=5)
     ref = oracle_of(kind, x, g, b)
-    for mode in (1, 2):
+    for mode in (1, 2, 3):
         y1 = run(kind, x, g, b, mode=mode)
         y2 = run(kind, x, g, b, mode=mode)
         assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32)), "repeat run changed the bits"
         y3 = run(kind, x, g, b, mode=mode, inplace=True)
         assert np.array_equal(y1.view(np.uint32), y3.view(np.uint32)), "in-place run differs"
         check(kind, y1, ref, f"{kind} mode={mode}")
+
+
+@pytest.mark.parametrize("kind", ["softmax", "layernorm"])
+@pytest.mark.parametrize("W", [100, 4096, 8192, 16384, 32768, 65536])
+def test_pipelined_rows(kind, W):
+    """The pipelined schedule (4 rows per workgroup, the next row's loads in
+    flight) against the oracle for row counts that leave the last workgroup
+    one row, several, or all of its rows; repeat runs give the same bits, and
+    so does an in-place run; where it holds a row over the same lanes as the
+    one-row kernel (rows of up to 4K values, and the widths it hands to that
+    kernel), it gives the one-row kernel's bits."""
+    same_shape = W <= 4096 or W > (16384 if kind == "layernorm" else 32768)
+    for rows in ((1, 3, 5, 9) if W > 16384 else (1, 3, 5, 9, 130)):
+        x, g, b = inputs(kind, W, rows=rows, seed=rows)
+        y3 = run(kind, x, g, b, mode=3)
+        check(kind, y3, oracle_of(kind, x, g, b), f"{kind} W={W} rows={rows} mode=3")
+        assert np.array_equal(y3.view(np.uint32), run(kind, x, g, b, mode=3).view(np.uint32))
+        assert np.array_equal(y3.view(np.uint32), run(kind, x, g, b, mode=3, inplace=True).view(np.uint32))
+        if same_shape:
+            y1 = run(kind, x, g, b, mode=1)
+            assert np.array_equal(y1.view(np.uint32), y3.view(np.uint32)), f"{kind} W={W} rows={rows}"
+
+
+@pytest.mark.parametrize("W", [8192, 16384])
+def test_auto_mode_pipelined_layernorm(W):
+    """Auto mode runs the pipelined schedule on LayerNorm rows of 8K-16K
+    values when there are 1024 rows or more: the evaluation's 2048 rows
+    (and a ragged 1027) against the oracle, every row."""
+    for rows in (1027, 2048):
+        x, g, b = inputs("layernorm", W, rows=rows, seed=rows)
+        y0 = run("layernorm", x, g, b, mode=0)
+        check("layernorm", y0, oracle_of("layernorm", x, g, b), f"auto W={W} rows={rows}")
+        assert np.array_equal(y0.view(np.uint32), run("layernorm", x, g, b, mode=3).view(np.uint32))
 
 
 def test_large_logits_and_constant_rows():

@@ -12,8 +12,9 @@ BASE = 1 << 20   # fake device addresses: never dereferenced on these paths
     ((BASE, BASE + 64, 4, 16, 0), cap.CAP_ERR_INVALID_ARG),           # partial overlap
     ((BASE, BASE * 4, -1, 16, 0), cap.CAP_ERR_INVALID_ARG),           # negative rows
     ((BASE, BASE * 4, 4, 0, 0), cap.CAP_ERR_INVALID_ARG),             # empty rows
-    ((BASE, BASE * 4, 4, 16, 3), cap.CAP_ERR_INVALID_ARG),            # bad mode
+    ((BASE, BASE * 4, 4, 16, 4), cap.CAP_ERR_INVALID_ARG),            # bad mode
     ((BASE, BASE * 4, 4, 65537, 1), cap.CAP_ERR_UNSUPPORTED),         # retained above 64K
+    ((BASE, BASE * 4, 4, 65537, 3), cap.CAP_ERR_UNSUPPORTED),         # pipelined retained above 64K
     ((BASE, BASE * 4, 1 << 31, 16, 0), cap.CAP_ERR_UNSUPPORTED),      # too many rows
     ((BASE, BASE * 4, 1, (1 << 24) + 4, 0), cap.CAP_ERR_UNSUPPORTED),
 ])
