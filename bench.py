@@ -60,6 +60,37 @@ def load_traffic(cfg: int, kernel: str):
         return None
 
 
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_kernel_cfg{cfg}_counters.txt")
+
+
+def load_counters(cfg, kernel: str):
+    """The derived figures (MfmaUtil_pct, VALUBusy_pct, ...) of a committed
+    rocprofv3 counter summary of the decode kernel, if it was taken on the
+    current kernel source and the same kernel; else None."""
+    path = COUNTERS_FILE.format(cfg=cfg)
+    if not os.path.exists(path):
+        return None
+    kv, derived, section = {}, {}, None
+    for line in open(path):
+        if line.startswith("derived"):
+            section = "derived"
+            continue
+        if ":" in line:
+            k, v = line.split(":", 1)
+            if section == "derived":
+                try:
+                    derived[k.strip()] = float(v)
+                except ValueError:
+                    pass
+            else:
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_code_sha256_16") != kernel_hash() or kv.get("kernel") != kernel or not derived:
+        return None
+    keep = ("MfmaUtil_pct", "VALUBusy_pct", "LdsUtil_pct", "LDSBankConflict_pct",
+            "wave_cycles_waiting_for_any_instruction_pct")
+    return {k: derived[k] for k in keep if k in derived}
+
+
 def load_trace_us(cfg: int, kernel: str):
     """Average duration (us) of the decode kernel in a committed rocprofv3
     --kernel-trace --stats summary, if it was taken on the current kernel
@@ -457,6 +488,7 @@ def measure(w, cfg: int, control: bool, args, dev, evict, stream, profiled: bool
     pkey = "4c" if control and cfg == 4 else cfg
     traffic = load_traffic(pkey, kernel_name) if profiled else None
     trace_us = load_trace_us(pkey, kernel_name) if profiled else None
+    counters = load_counters(pkey, kernel_name) if profiled else None
     r = {
         "value": round(value, 2),
         "ms_per_step": round(mean_ms, 5),
@@ -491,7 +523,12 @@ def measure(w, cfg: int, control: bool, args, dev, evict, stream, profiled: bool
         },
         "pct_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
         "req_heads_per_s": round(st_tree["request_heads"] / (mean_ms * 1e-3), 1),
+        # useful FLOP of the step / its time / the bf16 dense peak
         "mfma_util": round(st_tree["useful_flop"] / (mean_ms * 1e-3) / 2.5e15, 5),
+        # the decode kernel's matrix-core busy share and its other SQ figures,
+        # from the committed rocprofv3 counter summary (rocprofv3's formulas)
+        "counters": ({**counters, "source": os.path.relpath(COUNTERS_FILE.format(cfg=pkey), ROOT)}
+                     if counters else None),
         "t_decode_us": {"mean": round(dec_mean * 1e3, 3),
                         "median": round(statistics.median(disp_ms or dec_ms) * 1e3, 3),
                         "events_around_launch_mean": round(dec_ev_mean * 1e3, 3)},
@@ -530,6 +567,7 @@ def summary(r: dict) -> dict:
         "decode_over_size_matched_read": r["size_matched_read"]["decode_over_read"],
         "bytes_unique_kv": r["bytes"]["unique_kv"], "bytes_partial": r["bytes"]["partial"],
         "plan_host_us": r["plan_host_us"],
+        "counters": r["counters"],
     }
 
 

@@ -63,3 +63,13 @@ def test_committed_summaries_match_the_kernel_source(cfg):
     hbm = b.load_traffic(cfg, KERNEL)
     assert us is not None and us > 0, "kernel-trace summary missing or taken on other kernel code"
     assert hbm is not None and hbm > 0, "traffic summary missing or taken on other kernel code"
+
+
+@pytest.mark.parametrize("cfg", [1, 3, 4])
+def test_committed_counter_summaries_match_the_kernel_source(cfg):
+    """The counter summaries (three rocprofv3 --pmc passes) were taken on the
+    kernel source in the tree: bench.py reports their MFMA-busy share."""
+    b = load_bench()
+    c = b.load_counters(cfg, KERNEL)
+    assert c is not None, "counter summary missing or taken on other kernel code"
+    assert 0.0 < c["MfmaUtil_pct"] < 100.0 and 0.0 < c["VALUBusy_pct"] < 100.0
