@@ -65,7 +65,7 @@ def test_committed_summaries_match_the_kernel_source(cfg):
     assert hbm is not None and hbm > 0, "traffic summary missing or taken on other kernel code"
 
 
-@pytest.mark.parametrize("cfg", [1, 3, 4])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, "4c"])
 def test_committed_counter_summaries_match_the_kernel_source(cfg):
     """The counter summaries (three rocprofv3 --pmc passes) were taken on the
     kernel source in the tree: bench.py reports their MFMA-busy share."""
