@@ -121,7 +121,7 @@ struct RowArgs {
     int64_t rows, width;
     float eps;
     int32_t kind;
-    int32_t rows_per_wg;         // retained schedule: > 1 = that many rows per workgroup, pipelined
+    int32_t pipelined;           // retained schedule: 1 = several rows per workgroup, the next one in flight
 };
 
 // Kernel launchers (cap_kernels.hip, cap_aux.hip, cap_rows.hip); return the

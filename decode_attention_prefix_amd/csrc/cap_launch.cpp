@@ -196,19 +196,10 @@ cap_status cap_merge_partials(const cap_plan *plan, const void *workspace, size_
 
 // ------------------------------------------------------- wide-row workloads
 
-// Rows per workgroup of the pipelined retained schedule: of 2, 4 and 8, 4
-// is within 4% of the best for LayerNorm at 8K-16K values and keeps a full
-// grid (256 workgroups) from 1024 rows up.
-static int pipelined_rows_per_workgroup(const cap::RowArgs &a)
-{
-    (void)a;
-    return 4;
-}
-
 // Auto mode takes the pipelined schedule where it measured faster than one
 // row per workgroup: LayerNorm rows of 8K-16K values with 16-byte accesses
 // (3-15% faster; gamma and beta stay in registers across a workgroup's
-// rows), with rows enough for a full grid of 4-row workgroups.  Softmax
+// rows), with rows enough to give every resident workgroup two.  Softmax
 // keeps one row per workgroup (as fast or faster from 8K to 32K), and so do
 // rows of 4K values and less (where a row's latency, not bandwidth, decides).
 static bool auto_pipelined(const cap::RowArgs &a, bool vec4)
@@ -240,7 +231,7 @@ static cap_status rows_launch(cap::RowArgs &a, int32_t mode, cap_stream_t stream
     // auto: retained up to 64K values with 16-byte accesses; with 4-byte
     // accesses only up to 16K (a wider retained row spills registers)
     const bool retained = mode == 1 || mode == 3 || (mode == 0 && a.width <= (vec4 ? cap::kMaxRetainedWidth : 16384));
-    a.rows_per_wg = (mode == 3 || (mode == 0 && auto_pipelined(a, vec4))) ? pipelined_rows_per_workgroup(a) : 1;
+    a.pipelined = (mode == 3 || (mode == 0 && auto_pipelined(a, vec4))) ? 1 : 0;
     const int e = cap::launch_rows(a, vec4, retained, stream);
     if (e != 0) return fail(CAP_ERR_HIP, "row kernel launch failed: %s", cap::hip_error_string(e));
     return CAP_OK;

@@ -24,6 +24,9 @@
 //                        second read for the output pass.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
+
 #include "cap_internal.h"
 
 namespace cap {
@@ -258,7 +261,8 @@ __global__ __launch_bounds__(THREADS) void rows_retained_kernel(RowArgs a)
 
 // Rows blockIdx.x, + gridDim.x, ... per workgroup, each kept in registers,
 // with the next row's loads in flight while the current row is reduced and
-// written: the workgroup's reads and writes overlap, where one-row
+// written (the launch picks the grid, so rows per workgroup; see
+// launch_pipelined): the workgroup's reads and writes overlap, where one-row
 // workgroups that all start together read the whole input first and write
 // it all afterwards.  LayerNorm's gamma and beta are loaded once per
 // workgroup and kept in registers (when a lane holds at most 16 values of a
@@ -399,12 +403,41 @@ int launch_retained(const RowArgs &a, hipStream_t s)
     return (int)hipGetLastError();
 }
 
+// Workgroups of `kernel` the current device holds at once (its occupancy per
+// CU times the CU count), looked up once per kernel and device; 0 if the
+// runtime cannot say.
+template <typename K>
+int resident_workgroups(K kernel, int threads)
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (dev >= 0 && dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    const int r = std::max(1, per_cu) * std::max(1, cus);
+    if (dev >= 0 && dev < 64) cache[dev].store(r, std::memory_order_relaxed);
+    return r;
+}
+
+// The pipelined schedule runs one round of resident workgroups: each takes
+// ceil(rows / resident) rows (at least 2), so no workgroup waits for a slot
+// and every one has a next row to load while it finishes the current one.
+// (Measured on LayerNorm at 16K values, 2048 rows, one 1024-lane workgroup
+// per CU: 8 rows per workgroup 49.3 us against 51.1 with 4; at 8K, two
+// 512-lane workgroups per CU: 4 rows 26.3 us against 31.3 with 8.)
 template <int KIND, int VEC, int EPT, int THREADS>
 int launch_pipelined(const RowArgs &a, hipStream_t s)
 {
-    const int64_t grid = (a.rows + a.rows_per_wg - 1) / a.rows_per_wg;
-    hipLaunchKernelGGL((rows_pipelined_kernel<KIND, VEC, EPT, THREADS>), dim3((unsigned)grid), dim3(THREADS),
-                       0, s, a);
+    auto kernel = rows_pipelined_kernel<KIND, VEC, EPT, THREADS>;
+    const int64_t resident = resident_workgroups(kernel, THREADS);
+    const int64_t rpw = resident > 0 ? std::max<int64_t>(2, (a.rows + resident - 1) / resident) : 4;
+    const int64_t grid = (a.rows + rpw - 1) / rpw;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(THREADS), 0, s, a);
     return (int)hipGetLastError();
 }
 
@@ -457,7 +490,7 @@ int dispatch_pipelined(const RowArgs &a, hipStream_t s)
 template <int KIND>
 int dispatch(const RowArgs &a, bool vec4, bool retained, hipStream_t s)
 {
-    if (retained && a.rows_per_wg > 1)
+    if (retained && a.pipelined)
         return vec4 ? dispatch_pipelined<KIND, 4>(a, s) : dispatch_pipelined<KIND, 1>(a, s);
     if (retained) return vec4 ? dispatch_retained<KIND, 4>(a, s) : dispatch_retained<KIND, 1>(a, s);
     const int threads = a.width >= 16384 ? 1024 : 256;

@@ -28,8 +28,9 @@
  * keeps its whole row in registers, so the row is read from HBM once
  * (width <= 65536, CAP_ERR_UNSUPPORTED above); 2 = two passes: a statistics
  * pass, then a second read of the row for the output (any width; the
- * non-retaining baseline); 3 = retained, pipelined: each workgroup takes 4
- * rows in turn, keeping each in registers and loading the next while it
+ * non-retaining baseline); 3 = retained, pipelined: one round of resident
+ * workgroups, each taking rows / (workgroups the GPU holds at once) rows (at
+ * least 2) in turn, keeping each in registers and loading the next while it
  * reduces and writes the current one (LayerNorm: gamma and beta stay in
  * registers across its rows); HBM traffic as for 1 (width <= 65536,
  * CAP_ERR_UNSUPPORTED above; rows too wide to be held twice run as 1).

@@ -92,14 +92,16 @@ def test_in_place_and_deterministic(kind):
 @pytest.mark.parametrize("kind", ["softmax", "layernorm"])
 @pytest.mark.parametrize("W", [100, 4096, 8192, 16384, 32768, 65536])
 def test_pipelined_rows(kind, W):
-    """The pipelined schedule (4 rows per workgroup, the next row's loads in
-    flight) against the oracle for row counts that leave the last workgroup
-    one row, several, or all of its rows; repeat runs give the same bits, and
-    so does an in-place run; where it holds a row over the same lanes as the
-    one-row kernel (rows of up to 4K values, and the widths it hands to that
-    kernel), it gives the one-row kernel's bits."""
+    """The pipelined schedule (one round of resident workgroups, several rows
+    each, the next row's loads in flight) against the oracle for row counts
+    that give workgroups 1 or 2 rows, or many (5000 rows of up to 4K values:
+    several per workgroup, the last one ragged); repeat runs give the same
+    bits, and so does an in-place run; where it holds a row over the same
+    lanes as the one-row kernel (rows of up to 4K values, and the widths it
+    hands to that kernel), it gives the one-row kernel's bits."""
     same_shape = W <= 4096 or W > (16384 if kind == "layernorm" else 32768)
-    for rows in ((1, 3, 5, 9) if W > 16384 else (1, 3, 5, 9, 130)):
+    counts = (1, 3, 5, 9) if W > 16384 else (1, 3, 5, 9, 130) if W > 4096 else (1, 3, 5, 9, 130, 5000)
+    for rows in counts:
         x, g, b = inputs(kind, W, rows=rows, seed=rows)
         y3 = run(kind, x, g, b, mode=3)
         check(kind, y3, oracle_of(kind, x, g, b), f"{kind} W={W} rows={rows} mode=3")
