@@ -292,3 +292,22 @@ def test_dispatch_timed_decode_matches_plain_decode():
         check(dec.output(), ref, "timed decode")
     finally:
         dec.close()
+
+
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 32, 8), (64, 16, 2)])
+def test_many_requests(D, Hq, Hkv):
+    """A wide batch: 2000 requests over a random forest of short nodes
+    (some requests ending at internal nodes, zero-token nodes allowed), so
+    the plan holds thousands of items, partial rows in the tens of
+    thousands and request lists far past one item's rows; every output
+    element against the oracle, both step forms, the default plan and a
+    split-everything one."""
+    rng = np.random.default_rng([2000, D, Hq, Hkv])
+    nt, par, paths = wl.make_random_tree(rng, num_requests=2000, max_depth=4, max_len=70, num_q_heads=Hq,
+                                         num_kv_heads=Hkv, head_dim=D, internal_end_prob=0.2,
+                                         empty_root=True, min_len=0)
+    w = wl.make_workload(nt, par, paths, Hq, Hkv, D, rng, extra_pool_pages=3)
+    ref = oracle.decode(w.tree, w.q, w.k_pool, w.v_pool)
+    for opts in ({}, {"split_pages": 1, "share_mode": 1}):
+        st = run_both(w, ref, f"R=2000 D={D} Hq={Hq} Hkv={Hkv} {opts}", **opts)
+        assert st["num_items"] > 1000
