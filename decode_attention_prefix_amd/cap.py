@@ -91,6 +91,7 @@ class PlanView(ctypes.Structure):
 
 
 _lib = None
+ABI_VERSION = 8          # CAP_ABI_VERSION of include/cap.h that these bindings follow
 
 
 def lib():
@@ -103,6 +104,10 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         vp, sz, st = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
         L.cap_abi_version.restype = ctypes.c_int32
+        if L.cap_abi_version() != ABI_VERSION:
+            # the structures below would not match the library's
+            raise RuntimeError(f"{LIB_PATH} has ABI version {L.cap_abi_version()}, this binding "
+                               f"expects {ABI_VERSION}: rebuild it with `python -m decode_attention_prefix_amd.build`")
         L.cap_last_error.restype = ctypes.c_char_p
         L.cap_plan_opts_default.argtypes = [ctypes.POINTER(PlanOpts)]
         L.cap_plan_opts_default.restype = None

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define CAP_ABI_VERSION 7
+#define CAP_ABI_VERSION 8
 
 typedef enum cap_status {
     CAP_OK = 0,

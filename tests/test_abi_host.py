@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), f"libcap.so does not export {n}"
     assert set(cap.EXPORTED) == names
-    assert cap.cap_abi_version() == 7
+    assert cap.cap_abi_version() == 8 == cap.ABI_VERSION
 
 
 def small_tree(**over):
